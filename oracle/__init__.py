@@ -1,0 +1,194 @@
+"""CPU oracle for the AFD dispatch/combine path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The library never does, and shares no code with it.
+
+The arithmetic lives in ``afd_oracle.c`` (plain single-threaded C, built with
+``-ffp-contract=off``); this module only builds it and marshals numpy arrays.
+Each C function names the passage of the afdEP-comm pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "afd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+_lib = None
+
+ROUTE_RANGE, ROUTE_NEG, ROUTE_DUP = 1, 2, 3
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99, no contraction of a*b+c)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _ptr_array(arrs: Sequence[np.ndarray]):
+    t = ctypes.c_void_p * max(len(arrs), 1)
+    return t(*[a.ctypes.data for a in arrs])
+
+
+class Layout:
+    """Result of :func:`layout` (all numpy)."""
+
+    def __init__(self, ends, host_counts, rows_exact, slot_part, slot_row, err):
+        self.ends = ends                # int32 [E]
+        self.host_counts = host_counts  # int32 [E]
+        self.rows_exact = rows_exact    # int64 [F]
+        self.slot_part = slot_part      # int32 [ntok, K]
+        self.slot_row = slot_row        # int32 [ntok, K]
+        self.err = err                  # (code, s, t, k)
+
+
+def check_config(N, E, F, K, H, alpha) -> bool:
+    return lib().orc_check_config(N, E, F, K, H, alpha) == 0
+
+
+def layout(T: Sequence[int], ids: np.ndarray, E: int, F: int, K: int, alpha: int) -> Layout:
+    """ids: int32 [sum(T), K] (sources concatenated in order)."""
+    T_arr = np.ascontiguousarray(T, dtype=np.int32)
+    ntok = int(T_arr.sum())
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(ntok, K)
+    ends = np.zeros(E, np.int32)
+    hc = np.zeros(E, np.int32)
+    rows = np.zeros(F, np.int64)
+    sp = np.zeros((max(ntok, 1), K), np.int32)
+    sr = np.zeros((max(ntok, 1), K), np.int32)
+    err = np.zeros(4, np.int32)
+    rc = lib().orc_layout(len(T_arr), _p(T_arr), _p(ids), E, F, K, alpha, _p(ends), _p(hc),
+                          _p(rows), _p(sp), _p(sr), _p(err))
+    if rc != 0:
+        raise ValueError("invalid configuration")
+    return Layout(ends, hc, rows, sp[:ntok], sr[:ntok], tuple(int(v) for v in err))
+
+
+def dispatch(x_all: np.ndarray, w_all: np.ndarray, lay: Layout, F: int, rows_cap: Sequence[int],
+             fill_rows: Optional[int] = None):
+    """Expert-major rows and per-row weights for every partition.
+
+    x_all: [ntok, H] uint16 (bf16 bits) or uint8 (e4m3 bits).  Rows that are
+    not targets keep ``fill_rows`` bytes (0 if None) and weight NaN."""
+    ntok, K = lay.slot_part.shape
+    x_all = np.ascontiguousarray(x_all)
+    row_bytes = x_all.shape[1] * x_all.itemsize if ntok else 0
+    rows = [np.full((rows_cap[f], x_all.shape[1]), fill_rows or 0, dtype=x_all.dtype) for f in range(F)]
+    roww = [np.full(rows_cap[f], np.nan, np.float32) for f in range(F)]
+    if ntok:
+        lib().orc_dispatch(ctypes.c_int64(ntok), K, _p(x_all), ctypes.c_int64(row_bytes),
+                           _p(np.ascontiguousarray(w_all, np.float32)), _p(lay.slot_part),
+                           _p(lay.slot_row), _ptr_array(rows), _ptr_array(roww))
+    return rows, roww
+
+
+def dispatch_scales(T: Sequence[int], scale_src: List[np.ndarray], strides: List[tuple], G: int,
+                    lay: Layout, F: int, rows_cap: Sequence[int]):
+    """scale_src[s]: float32 buffer of source s; strides[s] = (stride_t, stride_g) in elements."""
+    T_arr = np.ascontiguousarray(T, dtype=np.int32)
+    ntok, K = lay.slot_part.shape
+    scales = [np.full((rows_cap[f], G), np.nan, np.float32) for f in range(F)]
+    st = np.ascontiguousarray([s[0] for s in strides], np.int64)
+    sg = np.ascontiguousarray([s[1] for s in strides], np.int64)
+    srcs = [np.ascontiguousarray(a, np.float32) if a is not None else np.zeros(1, np.float32) for a in scale_src]
+    if ntok:
+        lib().orc_dispatch_scales(len(T_arr), _p(T_arr), K, G, _ptr_array(srcs), _p(st), _p(sg),
+                                  _p(lay.slot_part), _p(lay.slot_row), _ptr_array(scales))
+    return scales
+
+
+def identity_experts(fp8: bool, E: int, F: int, f: int, alpha: int, H: int, ends: np.ndarray,
+                     rows: np.ndarray, scales: Optional[np.ndarray], y: np.ndarray) -> np.ndarray:
+    """Fill y (uint16 [rows, H]) in place for partition f's live rows."""
+    ends = np.ascontiguousarray(ends, np.int32)
+    sc = np.ascontiguousarray(scales, np.float32) if scales is not None else np.zeros(1, np.float32)
+    lib().orc_identity_experts(1 if fp8 else 0, E, F, f, alpha, H, _p(ends),
+                               _p(np.ascontiguousarray(rows)), _p(sc), _p(y))
+    return y
+
+
+def combine(w_all: np.ndarray, lay: Layout, H: int, ys: List[np.ndarray]) -> np.ndarray:
+    ntok, K = lay.slot_part.shape
+    out = np.zeros((ntok, H), np.uint16)
+    if ntok:
+        ys = [np.ascontiguousarray(y, np.uint16) for y in ys]
+        lib().orc_combine(ctypes.c_int64(ntok), K, H, _p(np.ascontiguousarray(w_all, np.float32)),
+                          _p(lay.slot_part), _p(lay.slot_row), _ptr_array(ys), _p(out))
+    return out
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.zeros(v.shape, np.uint16)
+    lib().orc_bf16_round(_p(v), _p(out), ctypes.c_int64(v.size))
+    return out
+
+
+def e4m3_decode(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, np.uint8)
+    out = np.zeros(q.shape, np.float32)
+    lib().orc_e4m3_decode(_p(q), _p(out), ctypes.c_int64(q.size))
+    return out
+
+
+class RoundResult:
+    def __init__(self, lay, rows, roww, scales, ys, out, rows_cap):
+        self.layout = lay
+        self.rows = rows
+        self.row_weights = roww
+        self.scales = scales
+        self.replies = ys
+        self.out = out          # uint16 [ntok, H]
+        self.rows_cap = rows_cap
+
+
+def run_round(inst, rows_cap: Optional[Sequence[int]] = None) -> RoundResult:
+    """The whole round for a generated instance (synthetic.gen.Instance):
+    layout -> dispatch (+scales) -> identity experts -> combine."""
+    cfg = inst.cfg
+    fp8 = cfg.dtype == "fp8"
+    T = [len(s.ids) for s in inst.sources]
+    K, H, E, F = cfg.K, cfg.H, cfg.E, cfg.F
+    ids = np.concatenate([s.ids for s in inst.sources]) if sum(T) else np.zeros((0, K), np.int32)
+    w = np.concatenate([s.weights for s in inst.sources]) if sum(T) else np.zeros((0, K), np.float32)
+    dt = np.uint8 if fp8 else np.uint16
+    x = np.concatenate([s.x for s in inst.sources]) if sum(T) else np.zeros((0, H), dt)
+    lay = layout(T, ids, E, F, K, cfg.alpha)
+    if rows_cap is None:
+        rows_cap = [int(max(lay.rows_exact[f], 1)) for f in range(F)]
+    rows, roww = dispatch(x, w, lay, F, rows_cap)
+    scales = None
+    if fp8:
+        scales = dispatch_scales(T, [s.scale for s in inst.sources], [(H // 128, 1)] * len(T), H // 128,
+                                 lay, F, rows_cap)
+    ys = []
+    for f in range(F):
+        y = np.zeros((rows_cap[f], H), np.uint16)
+        identity_experts(fp8, E, F, f, cfg.alpha, H, lay.ends, rows[f], scales[f] if fp8 else None, y)
+        ys.append(y)
+    out = combine(w, lay, H, ys)
+    return RoundResult(lay, rows, roww, scales, ys, out, rows_cap)

@@ -1,0 +1,360 @@
+/*
+ * afd_oracle.c -- plain CPU reference of the AFD expert-parallel dispatch and
+ * combine (the "hot path" of the afdEP-comm exchange), written from the
+ * afdEP-comm design and API-contract pages.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library links, includes or calls
+ * this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it.  It shares no source, header, table or helper
+ * with the GPU path.
+ *
+ * Everything here is single-threaded, plain loops, in the order the method
+ * defines it.  Build: gcc -std=c99 -O2 -ffp-contract=off -fPIC -shared.
+ *
+ * Pins (tests/): layout against an independent brute-force sort and
+ * invariants; combine against the float64 closed form with identity experts,
+ * a scipy.sparse routing-matrix product and exact special cases; number
+ * formats against torch's casts.  The pages' own per-stage rounding of the
+ * multi-GPU combine is not modelled here ("parity unpinned" for that
+ * variant; this oracle rounds once).
+ *
+ * Notation: N sources (s), T[s] tokens each, K choices per token, E experts,
+ * F partitions owning E_loc = E/F consecutive experts each, alignment alpha,
+ * hidden size H.  Tokens are numbered globally g = sum_{s'<s} T[s'] + t, so
+ * increasing g is the (source, token) order.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+#define ORC_OK 0
+#define ORC_BAD_CONFIG (-1)
+
+/* Route classification codes (shared meaning with the library's error word,
+ * but defined here independently). */
+#define ORC_ROUTE_RANGE 1
+#define ORC_ROUTE_NEG 2
+#define ORC_ROUTE_DUP 3
+
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+/* ---- number formats ---------------------------------------------------- */
+
+/* bfloat16 is the upper half of an IEEE binary32 pattern. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round binary32 to bfloat16, nearest with ties to even; NaN -> 0x7FC0. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return 0x7FC0;
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* float8_e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0
+ * is subnormal (step 2^-9); 0x7F / 0xFF are NaN; no infinities. */
+static float e4m3_to_f32(uint8_t q)
+{
+    int sign = q >> 7;
+    int e = (q >> 3) & 0xF;
+    int m = q & 7;
+    float v;
+    if (e == 0xF && m == 7) {
+        uint32_t nan = 0x7FC00000u;
+        memcpy(&v, &nan, 4);
+        return v;
+    }
+    if (e == 0) {
+        v = (float)m / 512.0f;                 /* m * 2^-9, exact */
+    } else {
+        float p = 1.0f;
+        int k;
+        if (e >= 7) for (k = 7; k < e; ++k) p *= 2.0f;
+        else for (k = e; k < 7; ++k) p *= 0.5f;
+        v = (1.0f + (float)m / 8.0f) * p;       /* exact in binary32 */
+    }
+    return sign ? -v : v;
+}
+
+/* ---- configuration (API contract page, "Roles and tensors") ------------- */
+
+/* H a multiple of 256, 1 <= K <= min(32, E), experts divide evenly over the
+ * FFN partitions, alignment >= 1. */
+int orc_check_config(int N, int E, int F, int K, int H, int alpha)
+{
+    if (N < 1 || E < 1 || F < 1 || K < 1 || alpha < 1 || H < 256) return ORC_BAD_CONFIG;
+    if (H % 256 != 0) return ORC_BAD_CONFIG;
+    if (K > 32 || K > E) return ORC_BAD_CONFIG;
+    if (E % F != 0) return ORC_BAD_CONFIG;
+    return ORC_OK;
+}
+
+/* ---- layout ------------------------------------------------------------ */
+
+/*
+ * orc_layout: the receive layout of one round.
+ *
+ * Route rule (API contract page, "Roles and tensors"; design page section 8
+ * on invalid routes): each id must be -1 (skip) or an expert in [0, E) that
+ * is not already live at an earlier k of the same token.  Visiting (s,t,k)
+ * in lexicographic order, a choice is
+ *   -1             -> skipped
+ *   < -1           -> NEG error, skipped
+ *   >= E           -> RANGE error, skipped
+ *   equal to a live id at an earlier k of the token -> DUP error, skipped
+ *   otherwise      -> live.
+ * The first error in that order is reported in err[0..3] = {code, s, t, k}
+ * (code 0 when every route is valid).
+ *
+ * Ownership (same section): partition f owns experts [f*E_loc, (f+1)*E_loc).
+ *
+ * Prefix sums (API contract page, "receive prefix sum ends[e]"): expert j of
+ * a partition occupies rows [align_up(ends[j-1], alpha), ends[j]) with
+ * ends[-1] = 0, i.e. start_j = align_up(ends_{j-1}, alpha) and
+ * ends_j = start_j + C_j with C_j its number of live choices.  Host counts
+ * are the aligned counts align_up(C_j, alpha); the partition's exact row
+ * count is align_up(ends_last, alpha).
+ *
+ * Row order inside an expert: ascending source, then ascending token (the
+ * deterministic order this implementation fixes where the pages' atomics
+ * leave any order valid).  A cursor per expert walks the live choices in
+ * (s, t, k) order.
+ *
+ * Outputs: ends[E] (partition f's entry j at f*E_loc+j), host_counts[E],
+ * rows_exact[F], slot_part/slot_row[ntok*K] (-1 where skipped), err[4].
+ */
+int orc_layout(int N, const int32_t *T, const int32_t *ids, int E, int F, int K, int alpha,
+               int32_t *ends, int32_t *host_counts, int64_t *rows_exact,
+               int32_t *slot_part, int32_t *slot_row, int32_t *err)
+{
+    int E_loc, s, t, k, kk, e, f, j;
+    int64_t g, ntok = 0;
+    int64_t *C, *start, *cursor;
+    unsigned char *live;
+
+    if (N < 1 || E < 1 || F < 1 || K < 1 || alpha < 1 || E % F != 0) return ORC_BAD_CONFIG;
+    E_loc = E / F;
+    for (s = 0; s < N; ++s) {
+        if (T[s] < 0) return ORC_BAD_CONFIG;
+        ntok += T[s];
+    }
+    C = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    start = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    cursor = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    live = (unsigned char *)calloc((size_t)(ntok * K + 1), 1);
+    err[0] = err[1] = err[2] = err[3] = 0;
+
+    /* 1. classify every choice */
+    g = 0;
+    for (s = 0; s < N; ++s) {
+        for (t = 0; t < T[s]; ++t, ++g) {
+            const int32_t *row = ids + g * K;
+            for (k = 0; k < K; ++k) {
+                int code = 0;
+                e = row[k];
+                if (e == -1) {
+                    code = 0;                       /* skipped, no error */
+                } else if (e < -1) {
+                    code = ORC_ROUTE_NEG;
+                } else if (e >= E) {
+                    code = ORC_ROUTE_RANGE;
+                } else {
+                    int dup = 0;
+                    for (kk = 0; kk < k; ++kk)
+                        if (live[g * K + kk] && row[kk] == e) dup = 1;
+                    if (dup) code = ORC_ROUTE_DUP;
+                    else live[g * K + k] = 1;
+                }
+                if (code != 0 && err[0] == 0) {
+                    err[0] = code; err[1] = s; err[2] = t; err[3] = k;
+                }
+            }
+        }
+    }
+
+    /* 2. live count per expert */
+    for (g = 0; g < ntok; ++g)
+        for (k = 0; k < K; ++k)
+            if (live[g * K + k]) C[ids[g * K + k]] += 1;
+
+    /* 3. aligned prefix per partition */
+    for (f = 0; f < F; ++f) {
+        int64_t prev_end = 0;
+        for (j = 0; j < E_loc; ++j) {
+            e = f * E_loc + j;
+            start[e] = align_up(prev_end, alpha);
+            ends[e] = (int32_t)(start[e] + C[e]);
+            host_counts[e] = (int32_t)align_up(C[e], alpha);
+            prev_end = ends[e];
+        }
+        rows_exact[f] = align_up(prev_end, alpha);
+    }
+
+    /* 4. slots: (source, token) order inside each expert */
+    for (g = 0; g < ntok; ++g) {
+        for (k = 0; k < K; ++k) {
+            if (live[g * K + k]) {
+                e = ids[g * K + k];
+                slot_part[g * K + k] = e / E_loc;
+                slot_row[g * K + k] = (int32_t)(start[e] + cursor[e]);
+                cursor[e] += 1;
+            } else {
+                slot_part[g * K + k] = -1;
+                slot_row[g * K + k] = -1;
+            }
+        }
+    }
+    free(C); free(start); free(cursor); free(live);
+    return ORC_OK;
+}
+
+/* ---- dispatch ---------------------------------------------------------- */
+
+/*
+ * orc_dispatch: expert-major receive rows (API contract page, worker_receive
+ * returns expert-major rows and their weights; DeepEP's copy epilogue writes
+ * each received token into its expert slots).  For every live choice
+ * (g, k) -> (f, row): rows_f[row] = x[g] byte for byte and
+ * row_w_f[row] = w[g][k].  Padding rows are left untouched.
+ * x is the concatenation of every source's [T, H] rows (row_bytes each).
+ */
+void orc_dispatch(int64_t ntok, int K, const uint8_t *x, int64_t row_bytes, const float *w,
+                  const int32_t *slot_part, const int32_t *slot_row,
+                  uint8_t *const *rows, float *const *row_w)
+{
+    int64_t g;
+    int k;
+    for (g = 0; g < ntok; ++g) {
+        for (k = 0; k < K; ++k) {
+            int32_t f = slot_part[g * K + k];
+            int32_t r = slot_row[g * K + k];
+            if (f < 0) continue;
+            memcpy(rows[f] + (int64_t)r * row_bytes, x + g * row_bytes, (size_t)row_bytes);
+            row_w[f][r] = w[g * K + k];
+        }
+    }
+}
+
+/*
+ * orc_dispatch_scales: FP8 block scales travel with their rows (API contract
+ * page: FP32 block-128 scales [T, H/128], strided views allowed).  Source
+ * s's scale of token t, block b, is at scale_src[s][t*stride_t[s] +
+ * b*stride_g[s]]; the receive side stores them densely, [rows, G].
+ */
+void orc_dispatch_scales(int N, const int32_t *T, int K, int G, const float *const *scale_src,
+                         const int64_t *stride_t, const int64_t *stride_g,
+                         const int32_t *slot_part, const int32_t *slot_row, float *const *scales)
+{
+    int s, t, k, b;
+    int64_t g = 0;
+    for (s = 0; s < N; ++s) {
+        for (t = 0; t < T[s]; ++t, ++g) {
+            for (k = 0; k < K; ++k) {
+                int32_t f = slot_part[g * K + k];
+                int32_t r = slot_row[g * K + k];
+                if (f < 0) continue;
+                for (b = 0; b < G; ++b)
+                    scales[f][(int64_t)r * G + b] =
+                        scale_src[s][(int64_t)t * stride_t[s] + (int64_t)b * stride_g[s]];
+            }
+        }
+    }
+}
+
+/* ---- identity experts (the synthetic FFN stand-in) ---------------------- */
+
+/*
+ * Expert e's reply scales its row by s_e = 1 + e/E and rounds to bfloat16:
+ * y = bf16(x * s_e) for BF16 rows, y = bf16((q * scale_b) * s_e) for FP8
+ * rows (two float32 products, each rounded).  Rows of partition f's local
+ * expert j are [align_up(ends[j-1], alpha), ends[j]); other rows of y are
+ * not written.
+ */
+static float expert_scale(int e, int E) { return 1.0f + (float)e / (float)E; }
+
+void orc_identity_experts(int fp8, int E, int F, int f, int alpha, int H, const int32_t *ends,
+                          const uint8_t *rows, const float *scales, uint16_t *y)
+{
+    int E_loc = E / F, j, h;
+    int64_t prev_end = 0, r;
+    int G = H / 128;
+    for (j = 0; j < E_loc; ++j) {
+        int e = f * E_loc + j;
+        int64_t st = align_up(prev_end, alpha);
+        int64_t en = ends[e];
+        float se = expert_scale(e, E);
+        for (r = st; r < en; ++r) {
+            for (h = 0; h < H; ++h) {
+                float v;
+                if (fp8) {
+                    float xv = e4m3_to_f32(rows[r * H + h]) * scales[r * G + h / 128];
+                    v = xv * se;
+                } else {
+                    uint16_t b;
+                    memcpy(&b, rows + (r * H + h) * 2, 2);
+                    v = bf16_to_f32(b) * se;
+                }
+                y[r * H + h] = f32_to_bf16_rne(v);
+            }
+        }
+        prev_end = en;
+    }
+}
+
+/* ---- combine ----------------------------------------------------------- */
+
+/*
+ * orc_combine: the source-side result (API contract page, source_collect:
+ * BF16 [T, H] summed over the selected experts in original token order; the
+ * routing weight is applied exactly once).  Replies are unweighted expert
+ * outputs, so per element
+ *     out[g][h] = bf16( sum over live k, ascending, of w[g][k] * y[slot][h] )
+ * accumulated in float32 from +0 (each product rounded, then added).  A token
+ * with no live choice gives +0 (design page section 13: rows of tokens with
+ * no valid route are zero).
+ */
+void orc_combine(int64_t ntok, int K, int H, const float *w, const int32_t *slot_part,
+                 const int32_t *slot_row, const uint16_t *const *y, uint16_t *out)
+{
+    int64_t g;
+    int k, h;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (g = 0; g < ntok; ++g) {
+        for (h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (k = 0; k < K; ++k) {
+            int32_t f = slot_part[g * K + k];
+            int32_t r = slot_row[g * K + k];
+            float wk = w[g * K + k];
+            if (f < 0) continue;
+            for (h = 0; h < H; ++h) {
+                float p = wk * bf16_to_f32(y[f][(int64_t)r * H + h]);
+                acc[h] = acc[h] + p;
+            }
+        }
+        for (h = 0; h < H; ++h) out[g * H + h] = f32_to_bf16_rne(acc[h]);
+    }
+    free(acc);
+}
+
+/* Exposed for the number-format pins. */
+void orc_bf16_round(const float *in, uint16_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
+}
+
+void orc_e4m3_decode(const uint8_t *in, float *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = e4m3_to_f32(in[i]);
+}
