@@ -1,0 +1,118 @@
+// afd_backend_fake.cpp -- a recording backend for CPU-only tests of the host
+// core.  Linked with afd_core.cpp into a separate host library: every device
+// action is appended to a text log instead of running, so the state machine,
+// the argument checks and the launch plan can be exercised without a GPU.
+// Never linked into the HIP library.
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "afd_plan.h"
+
+namespace {
+std::vector<std::string> g_log;
+std::vector<int32_t> g_ends;
+uint64_t g_err = afd::kNoError;
+int g_capturing = 0;
+int g_fail = 0;
+
+void logf(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+void logf(const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_log.emplace_back(buf);
+}
+}  // namespace
+
+namespace afd {
+
+int be_init_workspace(void *, const WorkspacePlan &wp)
+{
+    logf("init total=%zu nblk_max=%d", wp.total, wp.nblk_max);
+    return g_fail;
+}
+
+int be_is_capturing(void *, int *capturing)
+{
+    *capturing = g_capturing;
+    return 0;
+}
+
+int be_launch_dispatch(const RoundPlan &p, void *)
+{
+    std::string srcs;
+    for (int s = 0; s < p.N; ++s) {
+        char b[64];
+        snprintf(b, sizeof(b), "%s%d", s ? "," : "", p.tok_off[s + 1] - p.tok_off[s]);
+        srcs += b;
+    }
+    logf("dispatch fused=%d ntok=%d nblk=%d T=%s", p.fused ? 1 : 0, p.ntok, p.nblk, srcs.c_str());
+    return g_fail;
+}
+
+int be_read_ends(const RoundPlan &p, void *, int32_t *host_ends, uint64_t *err_word)
+{
+    logf("read_ends E=%d", p.E);
+    for (int e = 0; e < p.E; ++e) host_ends[e] = e < int(g_ends.size()) ? g_ends[e] : 0;
+    *err_word = g_err;
+    return g_fail;
+}
+
+int be_launch_combine(const RoundPlan &p, void *)
+{
+    std::string outs;
+    for (int s = 0; s < p.N; ++s) {
+        char b[64];
+        snprintf(b, sizeof(b), "%s%p", s ? "," : "", p.out[s]);
+        outs += b;
+    }
+    logf("combine ntok=%d out=%s", p.ntok, outs.c_str());
+    return g_fail;
+}
+
+int be_launch_copy(const void *src, void *dst, int64_t bytes, void *)
+{
+    logf("copy %p->%p bytes=%lld", src, dst, static_cast<long long>(bytes));
+    return g_fail;
+}
+
+int be_read_error(uint64_t *, void *, int clear, uint64_t *word)
+{
+    logf("read_error clear=%d", clear);
+    *word = g_err;
+    if (clear) g_err = kNoError;
+    return g_fail;
+}
+
+int be_device_sync()
+{
+    logf("sync");
+    return 0;
+}
+
+}  // namespace afd
+
+extern "C" {
+int afd_fake_log_size() { return int(g_log.size()); }
+int afd_fake_log_get(int i, char *buf, int n)
+{
+    if (i < 0 || i >= int(g_log.size()) || n <= 0) return -1;
+    std::snprintf(buf, size_t(n), "%s", g_log[size_t(i)].c_str());
+    return 0;
+}
+void afd_fake_log_clear() { g_log.clear(); }
+void afd_fake_set_ends(const int32_t *ends, int n, uint64_t err)
+{
+    g_ends.assign(ends, ends + n);
+    g_err = err;
+}
+void afd_fake_set_capturing(int c) { g_capturing = c; }
+void afd_fake_set_fail(int f) { g_fail = f; }
+}

@@ -1,0 +1,90 @@
+// afd_plan.h -- host-side plan of one round, shared by the host core and the
+// backends (the HIP executor, or the recording backend used by CPU tests).
+// Plain C++17; no HIP types.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/afd.h"
+
+namespace afd {
+
+constexpr int kMaxSources = AFD_MAX_SOURCES;
+constexpr int kMaxParts = AFD_MAX_PARTITIONS;
+constexpr int kMaxExperts = AFD_MAX_EXPERTS;
+constexpr int kMaxTopk = AFD_MAX_TOPK;
+
+// Tokens handled by one workgroup of the layout kernel (8 wavefronts of
+// 64 lanes, one token per lane; a wavefront's 64 tokens form one chunk).
+constexpr int kLayoutTile = 512;
+// Up to this many tokens per round the layout is rebuilt inside every
+// scatter workgroup (one kernel for the whole dispatch).
+constexpr int kFusedMaxTokens = 512;
+
+// Sticky route-error word: (s << 56) | (t << 24) | (k << 16) | code, so the
+// numeric minimum is the first offender in (source, token, k) order.
+constexpr uint64_t kNoError = ~0ull;
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Byte offsets of the workspace regions (each 256-byte aligned).
+struct WorkspacePlan {
+    size_t err = 0;        // uint64 sticky route-error word
+    size_t counter = 0;    // uint32 arrival counter of the layout kernel
+    size_t ends = 0;       // int32 [E]
+    size_t blkcnt = 0;     // int32 [nblk_max][E] live choices per layout tile
+    size_t blkbase = 0;    // int32 [nblk_max][E] first row of each tile's run
+    size_t packed = 0;     // int32 [N*capacity*K] (expert << 16 | rank in tile), -1 skipped
+    size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}
+    size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
+    size_t total = 0;
+    int nblk_max = 0;
+};
+
+// Everything a backend needs to run one round; pointers are device
+// addresses recorded from the caller.
+struct RoundPlan {
+    // configuration
+    int N = 0, F = 0, E = 0, E_loc = 0, K = 0, H = 0, alpha = 1, fp8 = 0, capacity = 0;
+    int64_t row_bytes = 0;   // H * bytes per activation
+    int G = 0;               // H / 128 scale blocks per row
+    // tokens, concatenated over sources in order
+    int ntok = 0;
+    int tok_off[kMaxSources + 1] = {};
+    bool fused = false;      // one-kernel dispatch
+    int nblk = 0;            // layout tiles (split path)
+    // per source
+    const void *x[kMaxSources] = {};
+    const int32_t *ids[kMaxSources] = {};
+    const float *w[kMaxSources] = {};
+    const float *scale[kMaxSources] = {};
+    int64_t sst[kMaxSources] = {}, ssg[kMaxSources] = {};
+    void *out[kMaxSources] = {};       // combine destination (out_bf16 or inbox)
+    // per partition
+    void *rows[kMaxParts] = {};
+    float *scales[kMaxParts] = {};
+    float *roww[kMaxParts] = {};
+    const void *reply[kMaxParts] = {};
+    // workspace
+    uint64_t *err = nullptr;
+    uint32_t *counter = nullptr;
+    int32_t *ends = nullptr;
+    int32_t *blkcnt = nullptr;
+    int32_t *blkbase = nullptr;
+    int32_t *packed = nullptr;
+    int32_t *slot = nullptr;
+};
+
+// ---- backend: implemented by the HIP executor or the recording fake ----
+// Each returns 0 on success, nonzero on a runtime failure.
+int be_init_workspace(void *workspace, const WorkspacePlan &wp);
+int be_is_capturing(void *stream, int *capturing);
+int be_launch_dispatch(const RoundPlan &p, void *stream);
+int be_read_ends(const RoundPlan &p, void *stream, int32_t *host_ends, uint64_t *err_word);
+int be_launch_combine(const RoundPlan &p, void *stream);
+int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream);
+int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word);
+int be_device_sync();
+
+}  // namespace afd
