@@ -1,0 +1,371 @@
+"""Benchmark of one AFD dispatch+combine round on one MI355X.
+
+A step is one round of the whole hot path for every role: N source
+dispatches, F worker receives (layout + scatter), F worker replies (the last
+one runs the combine) and N source collects, over one seeded synthetic batch
+resident in HBM.  Replies come from identity experts computed once before
+timing (expert compute is outside the library and outside the round, as in
+the afdEP-comm measurements, which time communication only).
+
+Rounds are captured in HIP graphs and replayed.  "cold" rounds rotate over
+enough independent input/arena/reply sets to push every round's bytes through
+HBM past the on-package cache; "hot" rounds reuse one set.  `value` is the
+cold whole-round algorithmic throughput:
+
+  per token       : H*b_x (+4*H/128 FP8 scales) read x, 2*H write the output,
+                    8*K read ids+weights, 8*K write + 8*K read the slot map
+  per live choice : H*b_x (+ scales) write its row, 2*H read its reply,
+                    4 write its row weight
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synthetic import gen  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "dispatch+combine µs/round and achieved HBM GB/s (% peak), E128/K8/H2048"
+
+
+# ----------------------------------------------------------------- bytes ----
+
+def live_choices(inst) -> int:
+    ids = np.concatenate([s.ids for s in inst.sources])
+    # generated routes are valid, so every id other than -1 is live
+    return int((ids >= 0).sum())
+
+
+def round_bytes(cfg, L: int) -> dict:
+    """Algorithmic HBM bytes of one round, split by kernel role."""
+    ntok = sum(cfg.T)
+    bx = 1 if cfg.dtype == "fp8" else 2
+    row = cfg.H * bx
+    sc = 4 * (cfg.H // 128) if cfg.dtype == "fp8" else 0
+    dispatch = ntok * (row + sc) + ntok * 8 * cfg.K + ntok * 8 * cfg.K + L * (row + sc) + L * 4
+    combine = L * 2 * cfg.H + ntok * 2 * cfg.H + ntok * 8 * cfg.K
+    return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine}
+
+
+# ----------------------------------------------------------- GPU harness ----
+
+class RoundSet:
+    """One independent set of inputs, outputs, arenas and replies."""
+
+    def __init__(self, inst, view):
+        import torch
+        from tests import gpu_harness as h
+        self.inst = inst
+        self.cfg = inst.cfg
+        self.view = view
+        self.dev = h.upload(inst)
+        self.buf = h.make_buffer(inst)
+        self.outs = [torch.empty((T, self.cfg.H), dtype=torch.bfloat16, device="cuda") for T in self.cfg.T]
+        # one eager round to obtain the receive layout, then the replies
+        for s, (x, ids, w, scl) in enumerate(self.dev):
+            self.buf.source_dispatch(s, x, ids, w, scl, bucket=self.cfg.bucket, out=self.outs[s])
+        recs = [self.buf.worker_receive(f, bucket=self.cfg.bucket) for f in range(self.cfg.F)]
+        self.replies = [h.identity_replies(self.cfg, r, f) for f, r in enumerate(recs)]
+        for f, r in enumerate(recs):
+            self.buf.worker_reply(f, self.replies[f], r.receipt)
+        for s in range(self.cfg.N):
+            self.buf.source_collect(s, view=view)
+        torch.cuda.synchronize()
+
+    def round(self, mark=None):
+        """Enqueue one full round on the current stream.  `mark(kind)` is
+        called right before and after the calls that launch kernels."""
+        c = self.cfg
+        b = self.buf
+        for s, (x, ids, w, scl) in enumerate(self.dev):
+            b.source_dispatch(s, x, ids, w, scl, bucket=c.bucket, out=self.outs[s])
+        if mark:
+            mark("dispatch", 0)
+        recs = [b.worker_receive(f, bucket=c.bucket) for f in range(c.F)]
+        if mark:
+            mark("dispatch", 1)
+        for f in range(c.F - 1):
+            b.worker_reply(f, self.replies[f], recs[f].receipt)
+        if mark:
+            mark("combine", 0)
+        b.worker_reply(c.F - 1, self.replies[c.F - 1], recs[c.F - 1].receipt)
+        if mark:
+            mark("combine", 1)
+        for s in range(c.N):
+            b.source_collect(s, view=self.view)
+
+
+def capture(sets, order):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for i in order[:2]:
+            sets[i].round()  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in order:
+            sets[i].round()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph_rounds(sets, order, steps, warmup):
+    """Replay graphs so that exactly `steps` rounds are timed."""
+    import torch
+    G = len(order)
+    g_full = capture(sets, order)
+    rem = steps % G
+    g_rem = capture(sets, order[:rem]) if rem else None
+    reps = steps // G
+    for _ in range(max(1, math.ceil(warmup / G))):
+        g_full.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / steps  # us per round
+
+
+def time_kernels_live(rs, rounds=64):
+    """Average duration of the dispatch and combine launches of a round,
+    from HIP events recorded around the calls that enqueue them, on the
+    stream they run on.  A sleep kernel first holds the stream so that the
+    host enqueues every round ahead of the GPU and the events bracket only
+    device work."""
+    import torch
+    st = torch.cuda.current_stream()
+    evs = []
+
+    def mark(kind, edge):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(st)
+        evs.append((kind, edge, e))
+
+    rs.round()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for _ in range(rounds):
+        rs.round(mark)
+    torch.cuda.synchronize()
+    acc = {"dispatch": [], "combine": []}
+    for i in range(0, len(evs), 2):
+        (k0, _, e0), (k1, _, e1) = evs[i], evs[i + 1]
+        assert k0 == k1
+        acc[k0].append(e0.elapsed_time(e1) * 1e3)
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def launch_floor(G=32, steps=3200):
+    """Graph of G rounds of two tiny dependent kernels: the floor a round of
+    two launches cannot go below."""
+    import torch
+    a = torch.zeros(1, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        a.add_(1.0)
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        for _ in range(G):
+            a.add_(1.0)
+            a.mul_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps // G):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (steps // G * G)
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=20):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+
+
+# ---------------------------------------------------------- CPU baseline ----
+
+def cpu_baseline(inst, budget_s=10.0):
+    """The oracle as it stands (single-threaded C), timed on this host:
+    layout + row/scale/weight dispatch + combine per round, identity-expert
+    replies computed once outside the timing (as on the GPU)."""
+    import oracle
+    cfg = inst.cfg
+    T = cfg.T
+    ids = np.concatenate([s.ids for s in inst.sources])
+    w = np.concatenate([s.weights for s in inst.sources])
+    x = np.concatenate([s.x for s in inst.sources])
+    G = cfg.H // 128
+    ref = oracle.run_round(inst)
+    caps = ref.rows_cap
+    rounds = 0
+    t_total = 0.0
+    while True:
+        t0 = time.perf_counter()
+        lay = oracle.layout(T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
+        oracle.dispatch(x, w, lay, cfg.F, caps)
+        if cfg.dtype == "fp8":
+            oracle.dispatch_scales(T, [s.scale for s in inst.sources], [(G, 1)] * cfg.N, G, lay, cfg.F, caps)
+        oracle.combine(w, lay, cfg.H, ref.replies)
+        t_total += time.perf_counter() - t0
+        rounds += 1
+        if t_total >= budget_s:
+            break
+    return t_total / rounds, rounds
+
+
+# ------------------------------------------------------------------ main ----
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE) for this kernel and workload, if a summary with the current
+    kernel source digest is committed under profiles/."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    src = os.path.join(ROOT, "combine_layout_amd", "csrc", "afd_kernels.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3200)
+    ap.add_argument("--warmup", type=int, default=320)
+    ap.add_argument("--workload", default="2a2f_decode", choices=gen.WORKLOADS)
+    ap.add_argument("--graph-rounds", type=int, default=0, help="rounds per captured graph (default by size)")
+    ap.add_argument("--cold-bytes", type=float, default=512e6, help="bytes the cold rotation spans")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip launch-floor and copy probes")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the dispatch/combine path runs every role on a single "
+              "device, so there is no multi-GPU configuration to launch (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    inst = gen.instance_by_name(args.workload)
+    cfg = inst.cfg
+    L = live_choices(inst)
+    nb = round_bytes(cfg, L)
+    view = cfg.F == 1
+    print(f"[bench] {args.workload}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} "
+          f"alpha={cfg.alpha} dtype={cfg.dtype} L={L} bytes/round={nb['total']}", file=sys.stderr, flush=True)
+
+    S = max(1, math.ceil(args.cold_bytes / nb["total"]))
+    G = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
+    G = max(G, S) if S > 1 else G
+    G = int(math.ceil(G / S) * S)
+    sets = [RoundSet(inst, view)]
+    hot_us = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
+    print(f"[bench] hot: {hot_us:.3f} us/round", file=sys.stderr, flush=True)
+    for _ in range(S - 1):
+        sets.append(RoundSet(inst, view))
+    cold_us = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
+    print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round", file=sys.stderr, flush=True)
+
+    kern = time_kernels_live(sets[-1])
+    dom = max(kern, key=kern.get)
+    dom_name = {"dispatch": "k_fused" if sum(cfg.T) <= 512 else "k_layout+k_scatter", "combine": "k_combine"}[dom]
+    dom_bytes = nb[dom]
+    dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
+    traffic = load_traffic(dom_name, args.workload)
+
+    extras = {}
+    if not args.no_extras:
+        extras["launch_floor_us_per_round"] = round(launch_floor(), 3)
+        extras["copy_gbps"] = round(copy_bandwidth(), 1)
+
+    value = nb["total"] / (cold_us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold_us / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
+                   "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
+                   "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
+                   "rounds_per_graph": G},
+        "us_per_round": round(cold_us, 3),
+        "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "us_per_round_hot": round(hot_us, 3),
+        "gbps_hot": round(nb["total"] / (hot_us * 1e-6) / 1e9, 2),
+        "bytes_per_round": nb["total"],
+        "kernels_us": {k: round(v, 3) for k, v in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern[dom], 3)},
+    }
+    res.update(extras)
+    if not args.no_cpu:
+        t_cpu, n = cpu_baseline(inst, args.cpu_budget)
+        res["cpu_baseline"] = {"value": round(nb["total"] / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{n} full rounds of {args.workload} (layout+dispatch+combine, "
+                                         f"{t_cpu * 1e3:.2f} ms/round, single-threaded C oracle, "
+                                         f"{platform.processor() or platform.machine()})"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

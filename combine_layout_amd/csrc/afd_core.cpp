@@ -156,7 +156,8 @@ void build_plan(afd_ctx *c)
     p.tok_off[0] = 0;
     for (int s = 0; s < p.N; ++s) p.tok_off[s + 1] = p.tok_off[s] + c->T[s];
     p.ntok = p.tok_off[p.N];
-    p.fused = p.ntok <= kFusedMaxTokens;
+    p.fused = p.ntok <= kFusedMaxTokens && int64_t(p.ntok) * p.K <= kFusedMaxIds && p.E <= kFusedMaxExperts &&
+              p.row_bytes / 16 <= kFusedMaxCols;
     p.nblk = (p.ntok + kLayoutTile - 1) / kLayoutTile;
     if (p.nblk < 1) p.nblk = 1;
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];

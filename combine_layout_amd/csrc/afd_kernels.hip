@@ -58,7 +58,7 @@ struct DispatchArgs {
     float *scales[kMaxParts];
     float *roww[kMaxParts];
     int tok_off[kMaxSources + 1];
-    int N, ntok, K, E, E_loc, alpha, nblk, nvec, G;
+    int N, ntok, K, E, E_loc, alpha, nblk, nvec, G, fp8;
     int64_t row_bytes;
     uint64_t *err;
     uint32_t *counter;
@@ -78,11 +78,36 @@ struct CombineArgs {
 };
 
 // ------------------------------------------------------------- helpers ----
+//
+// Kernel arguments live in the constant kernarg segment.  Indexing one of
+// its arrays with a value that differs between lanes becomes a dependent
+// vector load per lane, so kernels index them only with wave-uniform values
+// (scalar loads); lanes that need per-lane lookups read small LDS copies.
 
-__device__ __forceinline__ int src_of(const int *tok_off, int N, int g)
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+template <typename T>
+using lptr = __attribute__((address_space(3))) T *;
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int wave_id() { return uni(threadIdx.x / kWave); }
+
+// Source of global token g (g uniform): the number of sources q >= 1 whose
+// first token is at or before g (empty sources share their successor's
+// offset).  Only constant indices into the kernarg array.
+__device__ __forceinline__ int src_of_uniform(const int (&tok_off)[kMaxSources + 1], int N, int g)
 {
     int s = 0;
-    while (s + 1 < N && g >= tok_off[s + 1]) ++s;
+#pragma unroll
+    for (int q = 1; q < kMaxSources; ++q) s += (q < N && g >= tok_off[q]) ? 1 : 0;
+    return uni(s);
+}
+
+// The same from an LDS copy of the offsets, for per-lane tokens.
+__device__ __forceinline__ int src_of_lds(const int *tok_off, int N, int g)
+{
+    int s = 0;
+    for (int q = 1; q < N; ++q) s += g >= tok_off[q] ? 1 : 0;
     return s;
 }
 
@@ -92,11 +117,6 @@ __device__ __forceinline__ uint64_t make_err(int s, int t, int k, unsigned code)
 }
 
 __device__ __forceinline__ int align_up_i(int v, int a) { return (v + a - 1) / a * a; }
-
-__device__ __forceinline__ int load_agent(const int32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Exclusive prefix sum of vals[0..n) (LDS), in place, by a block of BLOCK
 // threads; each thread owns ceil(n / BLOCK) consecutive entries.
@@ -137,12 +157,13 @@ __device__ void block_exclusive_scan(int *vals, int n, int *wave_tot)
     __syncthreads();
 }
 
-// Classify the K choices of one token (route rule of the contract page) and
-// mark the live ones in the chunk's per-expert lane masks.  A duplicate is
-// detected by the token's own bit already being set in the expert's mask.
+// Route rule of the contract page for one token's K ids: -1 skips; other
+// negatives, ids >= E and repeats of an earlier valid id are errors and are
+// skipped too.  Returns the bit set of live choices and records the first
+// error (lowest k) of the token in `err`.  A repeat is caught by comparing
+// with the token's earlier ids in registers.
 template <int KMAX>
-__device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int K, int E, unsigned long long *mask_row,
-                                                   unsigned long long bit, int s, int t, uint64_t &err)
+__device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int K, int E, int s, int t, uint64_t &err)
 {
     uint32_t live = 0;
 #pragma unroll
@@ -156,8 +177,10 @@ __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int K,
         } else if (e >= E) {
             code = AFD_ROUTE_RANGE;
         } else {
-            const unsigned long long old = atomicOr(&mask_row[e], bit);
-            if (old & bit) code = AFD_ROUTE_DUP;
+            bool dup = false;
+#pragma unroll
+            for (int j = 0; j < k; ++j) dup |= ev[j] == e;
+            if (dup) code = AFD_ROUTE_DUP;
             else live |= 1u << k;
         }
         if (code != 0 && err == kNoError) err = make_err(s, t, k, code);
@@ -165,172 +188,190 @@ __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int K,
     return live;
 }
 
-// Store one token's row to each of its live slots, plus the slot map, the
-// per-row weights and (FP8) the block scales.  `part`/`row` of choice k are
-// held by lane k.  The first chunk of the row is already in v[].
-template <int VMAX>
-__device__ __forceinline__ void scatter_token(const DispatchArgs &a, int g, int s, int t, int lane, int part,
-                                              int row, const u32x4 *xs, u32x4 (&v)[VMAX])
+// Set the token's lane bit in the per-expert masks of its chunk.
+template <int KMAX>
+__device__ __forceinline__ void mark_token(const int (&ev)[KMAX], int K, uint32_t live, unsigned long long *mask_row,
+                                           unsigned long long bit)
 {
-    const int K = a.K;
-    if (lane < K) {
-        const float wk = a.w[s][int64_t(t) * K + lane];
-        int2 sl;
-        sl.x = part < 0 ? -1 : ((part << 24) | row);
-        sl.y = __float_as_int(wk);
-        reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
-        if (part >= 0) a.roww[part][row] = wk;
-    }
-    const int nvec = a.nvec;
-    for (int base = 0; base < nvec; base += kWave * VMAX) {
-        if (base > 0) {
 #pragma unroll
-            for (int i = 0; i < VMAX; ++i) {
-                const int c = base + i * kWave + lane;
-                if (c < nvec) v[i] = xs[c];
-            }
-        }
-        for (int k = 0; k < K; ++k) {
-            const int pr = __builtin_amdgcn_readlane(part, k);
-            if (pr < 0) continue;
-            const int rw = __builtin_amdgcn_readlane(row, k);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(a.rows[pr] + int64_t(rw) * a.row_bytes);
-#pragma unroll
-            for (int i = 0; i < VMAX; ++i) {
-                const int c = base + i * kWave + lane;
-                if (c < nvec) dst[c] = v[i];
-            }
-        }
-    }
-    if (a.scale[s] != nullptr) {
-        const float *sc = a.scale[s] + int64_t(t) * a.sst[s];
-        const int G = a.G;
-        for (int k = 0; k < K; ++k) {
-            const int pr = __builtin_amdgcn_readlane(part, k);
-            if (pr < 0) continue;
-            const int rw = __builtin_amdgcn_readlane(row, k);
-            float *dst = a.scales[pr] + int64_t(rw) * G;
-            for (int b = lane; b < G; b += kWave) dst[b] = sc[int64_t(b) * a.ssg[s]];
-        }
+    for (int k = 0; k < KMAX; ++k) {
+        if (k >= K) break;
+        if ((live >> k) & 1u) atomicOr(&mask_row[ev[k]], bit);
     }
 }
 
 // ------------------------------------------------------------- kernels ----
 
-// Dispatch in one kernel (rounds of at most kFusedMaxTokens tokens).
-// Block = 4 wavefronts; block b scatters tokens 4b..4b+3 (one per wavefront)
-// after building the full layout in LDS.
+// Dispatch in one kernel for small rounds (at most kFusedMaxTokens tokens,
+// kFusedMaxIds ids, kFusedMaxExperts experts).  Block g scatters token g,
+// each thread holding up to VMAX 16-byte columns of the row.  The row, the
+// token's weights and scales and every id of the round (copied straight
+// into LDS) are requested at entry, so a block waits on memory once before
+// its stores.  The block then needs only two histograms of the round's live
+// choices: over all tokens (for the aligned starts of every expert) and over
+// the tokens before g (the rank of g's row inside each of its experts, since
+// a token holds an expert at most once):
+//   row(g, e) = start_e + #{live choices of e in tokens before g}.
 template <int VMAX, int KMAX>
 __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_tot[4];
-    const int E = a.E, K = a.K, ntok = a.ntok;
-    const int nchunk = (ntok + kWave - 1) / kWave;
-    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [nchunk][E]
-    int *pre = reinterpret_cast<int *>(mask + size_t(nchunk) * E);            // [nchunk][E]
-    int *pfx = pre + size_t(nchunk) * E;                                      // [E]
-    uint32_t *livebits = reinterpret_cast<uint32_t *>(pfx + E);               // [ntok]
+    __shared__ int s_off[kMaxSources + 1];
+    __shared__ int s_row[kMaxTopk];
+    __shared__ float s_w[kMaxTopk];
+    __shared__ uint32_t s_live;
+    const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
+    int *hall = reinterpret_cast<int *>(lds);   // [E] live choices per expert
+    int *hbef = hall + E;                       // [E] ... in tokens before g
+    int *pfx = hbef + E;                        // [E] aligned counts, then their exclusive prefix
+    int *sids = pfx + E;                        // [ntok * K]
+    float *sscale = reinterpret_cast<float *>(sids + size_t(ntok) * K);  // [G] (FP8)
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int g = blockIdx.x * 4 + tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    const int g = blockIdx.x;
     const bool mine = g < ntok;
+    const int s = mine ? src_of_uniform(a.tok_off, N, g) : 0;
+    const int t = g - a.tok_off[s];
 
-    // 1. start this wavefront's row load; its latency overlaps the layout
-    int s = 0, t = 0;
-    const u32x4 *xs = nullptr;
+    // 1. request every load: row, weights, scales, all ids
     u32x4 v[VMAX];
     if (mine) {
-        s = src_of(a.tok_off, a.N, g);
-        t = g - a.tok_off[s];
-        xs = reinterpret_cast<const u32x4 *>(a.x[s] + int64_t(t) * a.row_bytes);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
-            const int c = i * kWave + lane;
+            const int c = tid + i * 256;
             if (c < a.nvec) v[i] = xs[c];
         }
     }
-
-    // 2. route check and per-chunk lane masks of every token
-    for (int i = tid; i < nchunk * E; i += 256) mask[i] = 0ull;
+    float wk = 0.0f;
+    if (mine && tid < K) wk = a.w[s][int64_t(t) * K + tid];
+    float scv = 0.0f;
+    const bool myscale = mine && a.fp8 && tid < G;
+    if (myscale) scv = a.scale[s][int64_t(t) * a.sst[s] + int64_t(tid) * a.ssg[s]];
+    for (int q = 0; q < N; ++q) {
+        const int lo = a.tok_off[q] * K;
+        const int n = a.tok_off[q + 1] * K - lo;
+        const gptr<const int32_t> src = (gptr<const int32_t>)a.ids[q];
+        for (int base = wave * kWave; base < n; base += 256)
+            if (base + lane < n)
+                __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4, 0,
+                                                 0);
+    }
+    if (tid == 0 && blockIdx.x == 0)
+        for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
+    for (int i = tid; i < 2 * E; i += 256) hall[i] = 0;
+    if (myscale) sscale[tid] = scv;
     __syncthreads();
+
+    // 2. route check and the two histograms
     uint64_t err = kNoError;
     for (int gg = tid; gg < ntok; gg += 256) {
-        const int ss = src_of(a.tok_off, a.N, gg);
-        const int tt = gg - a.tok_off[ss];
-        const int32_t *idp = a.ids[ss] + int64_t(tt) * K;
         int ev[KMAX];
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) ev[k] = k < K ? idp[k] : -1;
-        livebits[gg] = classify_token<KMAX>(ev, K, E, mask + size_t(gg / kWave) * E, 1ull << (gg % kWave), ss, tt, err);
+        for (int k = 0; k < KMAX; ++k) ev[k] = k < K ? sids[gg * K + k] : -1;
+        int ss = 0, tt = 0;
+        if (blockIdx.x == 0) {
+            ss = src_of_lds(s_off, N, gg);
+            tt = gg - s_off[ss];
+        }
+        const uint32_t live = classify_token<KMAX>(ev, K, E, ss, tt, err);
+        const bool before = gg < g;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k >= K) break;
+            if ((live >> k) & 1u) {
+                atomicAdd(&hall[ev[k]], 1);
+                if (before) atomicAdd(&hbef[ev[k]], 1);
+            }
+        }
+        if (gg == g) s_live = live;
     }
     if (blockIdx.x == 0 && err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
     __syncthreads();
 
-    // 3. per expert: exclusive prefix over chunks; aligned total
-    for (int e = tid; e < E; e += 256) {
-        int run = 0;
-        for (int c = 0; c < nchunk; ++c) {
-            pre[c * E + e] = run;
-            run += __popcll(mask[c * E + e]);
-        }
-        pfx[e] = align_up_i(run, a.alpha);
-    }
+    // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
+    // partitions); expert e starts at pfx[e] - pfx[first expert of its part]
+    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hall[e], a.alpha);
     __syncthreads();
-    // pfx[e] = sum of aligned counts of experts < e (all partitions); the
-    // start of expert e inside its partition is pfx[e] - pfx[first of part]
     block_exclusive_scan<256>(pfx, E, s_tot);
-
-    if (blockIdx.x == 0) {
-        for (int e = tid; e < E; e += 256) {
-            const int C = nchunk ? pre[(nchunk - 1) * E + e] + __popcll(mask[(nchunk - 1) * E + e]) : 0;
-            a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + C;
-        }
-    }
+    if (blockIdx.x == 0)
+        for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + hall[e];
     if (!mine) return;
 
-    // 4. rows of this wavefront's token: lane k holds choice k
-    int part = -1, row = -1;
-    if (lane < K && ((livebits[g] >> lane) & 1u)) {
-        const int e = a.ids[s][int64_t(t) * K + lane];
-        const int c = g / kWave;
-        const unsigned long long below = (1ull << (g % kWave)) - 1ull;
-        row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + pre[c * E + e] + __popcll(mask[c * E + e] & below);
-        part = e / a.E_loc;
+    // 4. slot of choice k (thread k)
+    if (tid < K) {
+        int part = -1, row = -1;
+        if ((s_live >> tid) & 1u) {
+            const int e = sids[g * K + tid];
+            row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + hbef[e];
+            part = e / a.E_loc;
+        }
+        const int packed = part < 0 ? -1 : ((part << 24) | row);
+        s_row[tid] = packed;
+        s_w[tid] = wk;
+        int2 sl;
+        sl.x = packed;
+        sl.y = __float_as_int(wk);
+        reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + tid] = sl;
     }
-    scatter_token<VMAX>(a, g, s, t, lane, part, row, xs, v);
+    __syncthreads();
+
+    // 5. stores: the row to every live slot, its weight and scales
+    for (int k = 0; k < K; ++k) {
+        const int pr = uni(s_row[k]);
+        if (pr < 0) continue;
+        const int f = pr >> 24, row = pr & 0xFFFFFF;
+        const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[f] + int64_t(row) * a.row_bytes);
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i) {
+            const int c = tid + i * 256;
+            if (c < a.nvec) dst[c] = v[i];
+        }
+        if (tid == 0) a.roww[f][row] = s_w[k];
+        if (myscale) a.scales[f][int64_t(row) * G + tid] = sscale[tid];
+    }
 }
 
-// Layout of larger rounds.  Block = 8 wavefronts = one 512-token tile; lane
-// = token.  packed[g][k] = (expert << 16) | rank of the choice among the
-// tile's choices of that expert, or -1.  The last tile to arrive scans the
-// tile counts into ends[] and blkbase[tile][e] (first row of the tile's run).
+// Tile histogram of larger rounds.  Block = 8 wavefronts = one 512-token
+// tile, lane = token.  blkcnt[tile][e] = live choices of expert e in the
+// tile; packed[g][k] = (expert << 16) | rank of the choice among the tile's
+// choices of that expert (source, token order), or -1.
 template <int KMAX>
 __global__ __launch_bounds__(512) void k_layout(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int s_tot[8];
-    __shared__ int s_last;
-    const int E = a.E, K = a.K;
+    __shared__ int s_off[kMaxSources + 1];
+    __shared__ const int32_t *s_ids[kMaxSources];
+    const int E = a.E, K = a.K, N = a.N;
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [8][E]
     int *pre = reinterpret_cast<int *>(mask + size_t(8) * E);                 // [8][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int g = blockIdx.x * kLayoutTile + tid;
+    const bool have = g < a.ntok;
 
+    if (tid == 0) {
+        for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
+        for (int q = 0; q < N; ++q) s_ids[q] = a.ids[q];
+    }
     for (int i = tid; i < 8 * E; i += 512) mask[i] = 0ull;
     __syncthreads();
+
     int ev[KMAX];
-    uint32_t live = 0;
-    const bool have = g < a.ntok;
+    int s = 0, t = 0;
     if (have) {
-        const int s = src_of(a.tok_off, a.N, g);
-        const int t = g - a.tok_off[s];
-        const int32_t *idp = a.ids[s] + int64_t(t) * K;
+        s = src_of_lds(s_off, N, g);
+        t = g - s_off[s];
+        const gptr<const int32_t> idp = (gptr<const int32_t>)s_ids[s] + int64_t(t) * K;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) ev[k] = k < K ? idp[k] : -1;
+    }
+    uint32_t live = 0;
+    if (have) {
         uint64_t err = kNoError;
-        live = classify_token<KMAX>(ev, K, E, mask + size_t(wave) * E, 1ull << lane, s, t, err);
+        live = classify_token<KMAX>(ev, K, E, s, t, err);
         if (err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
+        mark_token<KMAX>(ev, K, live, mask + size_t(wave) * E, 1ull << lane);
     }
     __syncthreads();
     for (int e = tid; e < E; e += 512) {
@@ -357,60 +398,148 @@ __global__ __launch_bounds__(512) void k_layout(DispatchArgs a)
             pk[k] = val;
         }
     }
-
-    // last tile to finish: scan the tile counts
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(a.counter, 1u) == unsigned(a.nblk - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    int *A = pre;  // reuse LDS: [E]
-    int C = 0;
-    if (tid < E) {
-        for (int b = 0; b < a.nblk; ++b) C += load_agent(a.blkcnt + b * E + tid);
-        A[tid] = align_up_i(C, a.alpha);
-    }
-    __syncthreads();
-    block_exclusive_scan<512>(A, E, s_tot);
-    if (tid < E) {
-        const int start = A[tid] - A[(tid / a.E_loc) * a.E_loc];
-        a.ends[tid] = start + C;
-        int run = start;
-        for (int b = 0; b < a.nblk; ++b) {
-            a.blkbase[b * E + tid] = run;
-            run += load_agent(a.blkcnt + b * E + tid);
-        }
-    }
-    if (tid == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Scatter of larger rounds: one wavefront per token.
+// Scatter of larger rounds.  Block = 4 wavefronts; wavefront w handles the
+// W = 8 / VMAX consecutive tokens starting at block_first + w * W (a block's
+// tokens lie in one layout tile).  Every block first turns the tile counts
+// into this tile's first row per expert:
+//   base[e] = start_e + sum of counts of e in earlier tiles,
+//   start_e = aligned prefix of the partition's experts before e,
+// which needs no communication between blocks.  The rows, ids' ranks and
+// weights are requested before that scan; the stores follow it.
 template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int g = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (g >= a.ntok) return;
-    const int s = src_of(a.tok_off, a.N, g);
-    const int t = g - a.tok_off[s];
-    const u32x4 *xs = reinterpret_cast<const u32x4 *>(a.x[s] + int64_t(t) * a.row_bytes);
-    u32x4 v[VMAX];
+    constexpr int W = VMAX >= 8 ? 1 : 8 / VMAX;
+    constexpr int TB = 4 * W;
+    extern __shared__ __align__(16) unsigned char lds[];
+    __shared__ int s_tot[4];
+    int *base = reinterpret_cast<int *>(lds);   // [E]
+    int *A = base + a.E;                        // [E]
+    int *Cs = A + a.E;                          // [E]
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok;
+    const int g_first = blockIdx.x * TB;
+    const int tile = g_first / kLayoutTile;
+
+    // 1. request the rows and the ranks of this wavefront's tokens
+    u32x4 v[W][VMAX];
+    int pk[W];
+    float wk[W];
 #pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-        const int c = i * kWave + lane;
-        if (c < a.nvec) v[i] = xs[c];
-    }
-    int part = -1, row = -1;
-    if (lane < a.K) {
-        const int pk = a.packed[int64_t(g) * a.K + lane];
-        if (pk >= 0) {
-            const int e = pk >> 16;
-            row = a.blkbase[(g / kLayoutTile) * a.E + e] + (pk & 0xFFFF);
-            part = e / a.E_loc;
+    for (int j = 0; j < W; ++j) {
+        const int g = g_first + wave * W + j;
+        pk[j] = -1;
+        wk[j] = 0.0f;
+        if (g < ntok) {
+            const int s = src_of_uniform(a.tok_off, a.N, g);
+            const int t = g - a.tok_off[s];
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = i * kWave + lane;
+                if (c < nvec) v[j][i] = xs[c];
+            }
+            if (lane < K) {
+                pk[j] = a.packed[int64_t(g) * K + lane];
+                wk[j] = a.w[s][int64_t(t) * K + lane];
+            }
         }
     }
-    scatter_token<VMAX>(a, g, s, t, lane, part, row, xs, v);
+
+    // 2. this tile's first row of every expert
+    for (int e = tid; e < E; e += 256) {
+        int C = 0, before = 0;
+        for (int b = 0; b < a.nblk; ++b) {
+            const int c = a.blkcnt[b * E + e];
+            C += c;
+            before += b < tile ? c : 0;
+        }
+        A[e] = align_up_i(C, a.alpha);
+        Cs[e] = C;
+        base[e] = before;
+    }
+    __syncthreads();
+    block_exclusive_scan<256>(A, E, s_tot);
+    for (int e = tid; e < E; e += 256) {
+        const int start = A[e] - A[(e / a.E_loc) * a.E_loc];
+        base[e] += start;
+        if (blockIdx.x == 0) a.ends[e] = start + Cs[e];
+    }
+    __syncthreads();
+
+    // 3. slots and stores, token by token
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const int g = g_first + wave * W + j;
+        if (g >= ntok) break;
+        int part = -1, row = -1;
+        if (pk[j] >= 0) {
+            const int e = pk[j] >> 16;
+            row = base[e] + (pk[j] & 0xFFFF);
+            part = e / a.E_loc;
+        }
+        if (lane < K) {
+            int2 sl;
+            sl.x = part < 0 ? -1 : ((part << 24) | row);
+            sl.y = __float_as_int(wk[j]);
+            reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
+        }
+        for (int k = 0; k < K; ++k) {
+            const int pr = __builtin_amdgcn_readlane(part, k);
+            if (pr < 0) continue;
+            const int rw = __builtin_amdgcn_readlane(row, k);
+            const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[pr] + int64_t(rw) * a.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = i * kWave + lane;
+                if (c < nvec) dst[c] = v[j][i];
+            }
+            if (lane == 0) a.roww[pr][rw] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk[j]), k));
+        }
+        // rows longer than 64 * VMAX columns: the remaining columns, chunk by chunk
+        if (nvec > kWave * VMAX) {
+            const int s = src_of_uniform(a.tok_off, a.N, g);
+            const gptr<const u32x4> xs =
+                (gptr<const u32x4>)(a.x[s] + int64_t(g - a.tok_off[s]) * a.row_bytes);
+            for (int cb = kWave * VMAX; cb < nvec; cb += kWave * VMAX) {
+                u32x4 r[VMAX];
+#pragma unroll
+                for (int i = 0; i < VMAX; ++i) {
+                    const int c = cb + i * kWave + lane;
+                    if (c < nvec) r[i] = xs[c];
+                }
+                for (int k = 0; k < K; ++k) {
+                    const int pr = __builtin_amdgcn_readlane(part, k);
+                    if (pr < 0) continue;
+                    const int rw = __builtin_amdgcn_readlane(row, k);
+                    const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[pr] + int64_t(rw) * a.row_bytes);
+#pragma unroll
+                    for (int i = 0; i < VMAX; ++i) {
+                        const int c = cb + i * kWave + lane;
+                        if (c < nvec) dst[c] = r[i];
+                    }
+                }
+            }
+        }
+        if (a.fp8) {
+            const int s = src_of_uniform(a.tok_off, a.N, g);
+            const int t = g - a.tok_off[s];
+            const gptr<const float> sc = (gptr<const float>)a.scale[s] + int64_t(t) * a.sst[s];
+            const int64_t ssg = a.ssg[s];
+            const int G = a.G;
+            for (int b = lane; b < G; b += kWave) {
+                const float val = sc[int64_t(b) * ssg];
+                for (int k = 0; k < K; ++k) {
+                    const int pr = __builtin_amdgcn_readlane(part, k);
+                    if (pr < 0) continue;
+                    const int rw = __builtin_amdgcn_readlane(row, k);
+                    a.scales[pr][int64_t(rw) * G + b] = val;
+                }
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
@@ -427,18 +556,18 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & (kWave - 1);
-    const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int gw = blockIdx.x * 4 + wave_id();
     const int g = gw / a.nseg;
     const int seg = gw - g * a.nseg;
     if (g >= a.ntok) return;
-    const int s = src_of(a.tok_off, a.N, g);
-    const int t = g - a.tok_off[s];
     int sl_row = -1, sl_w = 0;
     if (lane < a.K) {
         const int2 sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
         sl_row = sl.x;
         sl_w = sl.y;
     }
+    const int s = src_of_uniform(a.tok_off, a.N, g);
+    const int t = g - a.tok_off[s];
     const int nvec = a.nvec;
     const int c0 = seg * kWave * VPL + lane;
     float acc[VPL][8];
@@ -534,6 +663,7 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.nblk = p.nblk;
     a.nvec = int(p.row_bytes / 16);
     a.G = p.G;
+    a.fp8 = p.fp8;
     a.row_bytes = p.row_bytes;
     a.err = p.err;
     a.counter = p.counter;
@@ -565,9 +695,10 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
 }
 
 template <int VMAX>
-int launch_scatter_v(const DispatchArgs &a, dim3 grid, hipStream_t st)
+int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_scatter<VMAX>, grid, dim3(256), 0, st, a);
+    constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
+    hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), size_t(E) * 12, st, a);
     return launched_ok();
 }
 
@@ -597,10 +728,12 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     const bool k32 = p.K > 8;
     const int vm = vmax_for(a.nvec);
     if (p.fused) {
-        const int nchunk = (p.ntok + kWave - 1) / kWave;
-        const size_t lds = size_t(nchunk) * p.E * 12 + size_t(p.E) * 4 + size_t(p.ntok) * 4;
-        dim3 grid(p.ntok > 0 ? (p.ntok + 3) / 4 : 1);
-        switch (vm) {
+        // one block per token; 256 threads hold the row, VMAX columns each
+        const int per = (a.nvec + 255) / 256;
+        const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+        const size_t lds = size_t(p.E) * 12 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
+        dim3 grid(p.ntok > 0 ? p.ntok : 1);
+        switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);
         case 2: return launch_fused_v<2>(a, k32, grid, lds, st);
         case 4: return launch_fused_v<4>(a, k32, grid, lds, st);
@@ -611,12 +744,11 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     if (k32) hipLaunchKernelGGL(k_layout<32>, dim3(p.nblk), dim3(512), lds, st, a);
     else hipLaunchKernelGGL(k_layout<8>, dim3(p.nblk), dim3(512), lds, st, a);
     if (launched_ok()) return 1;
-    dim3 grid((p.ntok + 3) / 4);
     switch (vm) {
-    case 1: return launch_scatter_v<1>(a, grid, st);
-    case 2: return launch_scatter_v<2>(a, grid, st);
-    case 4: return launch_scatter_v<4>(a, grid, st);
-    default: return launch_scatter_v<8>(a, grid, st);
+    case 1: return launch_scatter_v<1>(a, p.ntok, p.E, st);
+    case 2: return launch_scatter_v<2>(a, p.ntok, p.E, st);
+    case 4: return launch_scatter_v<4>(a, p.ntok, p.E, st);
+    default: return launch_scatter_v<8>(a, p.ntok, p.E, st);
     }
 }
 

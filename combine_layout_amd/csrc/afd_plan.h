@@ -18,9 +18,13 @@ constexpr int kMaxTopk = AFD_MAX_TOPK;
 // Tokens handled by one workgroup of the layout kernel (8 wavefronts of
 // 64 lanes, one token per lane; a wavefront's 64 tokens form one chunk).
 constexpr int kLayoutTile = 512;
-// Up to this many tokens per round the layout is rebuilt inside every
-// scatter workgroup (one kernel for the whole dispatch).
+// Small rounds rebuild the layout inside every scatter workgroup (one kernel
+// for the whole dispatch): at most this many tokens, ids (staged in LDS) and
+// experts, and rows of at most this many 16-byte columns.
 constexpr int kFusedMaxTokens = 512;
+constexpr int kFusedMaxIds = 4096;
+constexpr int kFusedMaxExperts = 256;
+constexpr int kFusedMaxCols = 2048;
 
 // Sticky route-error word: (s << 56) | (t << 24) | (k << 16) | code, so the
 // numeric minimum is the first offender in (source, token, k) order.

@@ -113,3 +113,43 @@ def test_parity_random_small(case):
     g = h.run_round(inst, rhc=(i % 2 == 0))
     ref = _oracle_ref(inst, g.receive_rows)
     assert check_round(inst, g, ref) == 0
+
+
+SPLIT = [(i,) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"m{c[0]}")
+def test_parity_random_split_path(case):
+    """Rounds above the one-kernel limits (more than 512 tokens, more than
+    4096 ids or more than 256 experts) take the tiled layout + scatter path."""
+    h = _gpu()
+    i = case[0]
+    rng = np.random.default_rng(77 + i)
+    F = int(rng.choice([1, 2, 3, 4]))
+    E = F * int(rng.choice([2, 8, 32, 128])) if i % 4 != 3 else 512
+    E = min(E, 512) // F * F
+    K = int(rng.choice([1, 4, 8, 12, 32])) if E >= 32 else int(rng.integers(1, min(8, E) + 1))
+    K = min(K, E)
+    N = int(rng.integers(1, 4))
+    T = [int(rng.integers(0, 700)) for _ in range(N)]
+    if sum(T) <= 512 and sum(T) * K <= 4096 and E <= 256:
+        T[0] += 600
+    bucket = max(T)
+    alpha = int(rng.choice([1, 3, 16, 128]))
+    dtype = "fp8" if i % 3 == 2 else "bf16"
+    inst = gen.random_small(200 + i, N=N, F=F, E=E, K=K, alpha=alpha, T=T, H=256 if i % 2 else 512,
+                            p_skip=0.1, dtype=dtype, bucket=bucket)
+    print(f"[parity split] m{i} T={T} E={E} F={F} K={K} a={alpha} {dtype}", flush=True)
+    g = h.run_round(inst, rhc=(i % 2 == 1))
+    ref = _oracle_ref(inst, g.receive_rows)
+    assert check_round(inst, g, ref) == 0
+
+
+@pytest.mark.parametrize("K", [12, 32])
+def test_parity_fused_wide_topk(K):
+    h = _gpu()
+    inst = gen.random_small(300 + K, N=2, F=2, E=64, K=K, alpha=8, T=[40, 63], H=512, p_skip=0.1)
+    print(f"[parity fused K={K}]", flush=True)
+    g = h.run_round(inst)
+    ref = _oracle_ref(inst, g.receive_rows)
+    assert check_round(inst, g, ref) == 0
