@@ -49,14 +49,28 @@ def live_choices(inst) -> int:
     return int((ids >= 0).sum())
 
 
-def round_bytes(cfg, L: int) -> dict:
-    """Algorithmic HBM bytes of one round, split by kernel role."""
+def byte_terms(cfg, L: int) -> dict:
+    """Each algorithmic byte stream of one round (ntok tokens, L live choices)."""
     ntok = sum(cfg.T)
     bx = 1 if cfg.dtype == "fp8" else 2
-    row = cfg.H * bx
     sc = 4 * (cfg.H // 128) if cfg.dtype == "fp8" else 0
-    dispatch = ntok * (row + sc) + ntok * 8 * cfg.K + ntok * 8 * cfg.K + L * (row + sc) + L * 4
-    combine = L * 2 * cfg.H + ntok * 2 * cfg.H + ntok * 8 * cfg.K
+    return {
+        "x_read": ntok * (cfg.H * bx + sc),          # source rows (+ scales), read once
+        "ids_weights_read": ntok * 8 * cfg.K,         # int32 ids + fp32 weights
+        "slot_map_write": ntok * 8 * cfg.K,
+        "rows_write": L * (cfg.H * bx + sc),          # expert-major rows (+ scales)
+        "row_weights_write": L * 4,
+        "replies_read": L * 2 * cfg.H,                # BF16 replies
+        "slot_map_read": ntok * 8 * cfg.K,
+        "out_write": ntok * 2 * cfg.H,                # BF16 result
+    }
+
+
+def round_bytes(cfg, L: int) -> dict:
+    """Algorithmic HBM bytes of one round, split by kernel role."""
+    t = byte_terms(cfg, L)
+    dispatch = t["x_read"] + t["ids_weights_read"] + t["slot_map_write"] + t["rows_write"] + t["row_weights_write"]
+    combine = t["replies_read"] + t["slot_map_read"] + t["out_write"]
     return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine}
 
 
@@ -255,20 +269,25 @@ def cpu_baseline(inst, budget_s=10.0):
 # ------------------------------------------------------------------ main ----
 
 def load_traffic(kernel, workload):
-    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE,
-    WRITE_SIZE) for this kernel and workload, if a summary with the current
-    kernel source digest is committed under profiles/."""
+    """HBM bytes per dispatch of `kernel` on `workload` measured with the
+    rocprofv3 counters FETCH_SIZE and WRITE_SIZE (scaled by a plain-copy
+    calibration), from the summaries under profiles/ -- None when no summary
+    covers it or the kernel source changed since the counters were taken."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        rec = json.load(fh)
     src = os.path.join(ROOT, "combine_layout_amd", "csrc", "afd_kernels.hip")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("kernel_source_sha256_16") != digest:
-        return None
-    return rec.get("bytes_per_launch")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
+        text = open(path).read()
+        if f"`{digest}`" not in text:
+            continue
+        for line in text.splitlines():
+            line = line.strip()
+            if line.startswith("traffic_bytes_per_dispatch "):
+                table = json.loads(line[len("traffic_bytes_per_dispatch "):])
+                if kernel in table:
+                    return table[kernel]
+    return None
 
 
 def main(argv=None):
@@ -282,6 +301,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip launch-floor and copy probes")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (read + write) ten times; used to "
+                         "calibrate the HBM byte counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -294,6 +316,11 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+
+    if args.copy_only:
+        gbps = copy_bandwidth(args.copy_only << 20, reps=10)
+        print(json.dumps({"copy_mib": args.copy_only, "copy_gbps": round(gbps, 1)}), flush=True)
+        return 0
 
     inst = gen.instance_by_name(args.workload)
     cfg = inst.cfg
@@ -317,7 +344,7 @@ def main(argv=None):
 
     kern = time_kernels_live(sets[-1])
     dom = max(kern, key=kern.get)
-    dom_name = {"dispatch": "k_fused" if sum(cfg.T) <= 512 else "k_layout+k_scatter", "combine": "k_combine"}[dom]
+    dom_name = {"dispatch": "k_fused" if sum(cfg.T) <= 512 else "k_scatter", "combine": "k_combine"}[dom]
     dom_bytes = nb[dom]
     dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom_name, args.workload)

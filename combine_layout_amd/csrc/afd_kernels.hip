@@ -17,7 +17,7 @@
 //   k_fused   dispatch for small rounds (<= kFusedMaxTokens tokens): every
 //             workgroup rebuilds the whole layout in LDS from the ids, then
 //             scatters its own four tokens.  One launch for the dispatch.
-//   k_layout  dispatch, larger rounds, step 1: 512-token tiles; per 64-token
+//   k_layout  dispatch, larger rounds, step 1: 256-token tiles; per 64-token
 //             chunk an LDS bit mask per expert gives each choice its rank
 //             (popcount of the lanes below it); the last tile to finish scans
 //             the tile counts into ends[] and per-tile row bases.
@@ -157,47 +157,39 @@ __device__ void block_exclusive_scan(int *vals, int n, int *wave_tot)
     __syncthreads();
 }
 
-// Route rule of the contract page for one token's K ids: -1 skips; other
-// negatives, ids >= E and repeats of an earlier valid id are errors and are
-// skipped too.  Returns the bit set of live choices and records the first
-// error (lowest k) of the token in `err`.  A repeat is caught by comparing
-// with the token's earlier ids in registers.
+// Copy of a kernel-argument pointer array into LDS (thread 0, constant
+// offsets), so lanes can look entries up by their own index.
+template <typename T, int M>
+__device__ __forceinline__ void table_to_lds(uint64_t *dst, T *const (&arr)[M])
+{
+#pragma unroll
+    for (int q = 0; q < M; ++q) dst[q] = reinterpret_cast<uint64_t>(arr[q]);
+}
+
+// Route rule of the contract page for one token's ids ev[0..KMAX), where
+// entries past K hold -1: -1 skips; other negatives, ids >= E and repeats of
+// an earlier valid id are errors and are skipped too.  Returns the bit set
+// of live choices and records the first error (lowest k) of the token in
+// `err`.  Branch-free: repeats are found by comparing with the earlier ids in
+// registers, and every decision is a select.
 template <int KMAX>
-__device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int K, int E, int s, int t, uint64_t &err)
+__device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int E, int s, int t, uint64_t &err)
 {
     uint32_t live = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) break;
         const int e = ev[k];
-        unsigned code = 0;
-        if (e == -1) {
-        } else if (e < -1) {
-            code = AFD_ROUTE_NEG;
-        } else if (e >= E) {
-            code = AFD_ROUTE_RANGE;
-        } else {
-            bool dup = false;
+        const bool valid = e >= 0 && e < E;
+        bool dup = false;
 #pragma unroll
-            for (int j = 0; j < k; ++j) dup |= ev[j] == e;
-            if (dup) code = AFD_ROUTE_DUP;
-            else live |= 1u << k;
-        }
-        if (code != 0 && err == kNoError) err = make_err(s, t, k, code);
+        for (int j = 0; j < k; ++j) dup |= ev[j] == e;
+        const unsigned code =
+            e < -1 ? unsigned(AFD_ROUTE_NEG) : e >= E ? unsigned(AFD_ROUTE_RANGE) : (valid && dup) ? unsigned(AFD_ROUTE_DUP) : 0u;
+        live |= (valid && !dup) ? (1u << k) : 0u;
+        const uint64_t cand = make_err(s, t, k, code);
+        err = (code != 0 && err == kNoError) ? cand : err;
     }
     return live;
-}
-
-// Set the token's lane bit in the per-expert masks of its chunk.
-template <int KMAX>
-__device__ __forceinline__ void mark_token(const int (&ev)[KMAX], int K, uint32_t live, unsigned long long *mask_row,
-                                           unsigned long long bit)
-{
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) break;
-        if ((live >> k) & 1u) atomicOr(&mask_row[ev[k]], bit);
-    }
 }
 
 // ------------------------------------------------------------- kernels ----
@@ -219,12 +211,13 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     __shared__ int s_tot[4];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ int s_row[kMaxTopk];
-    __shared__ float s_w[kMaxTopk];
     __shared__ uint32_t s_live;
+    __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
+    __shared__ uint64_t s_dst[kMaxTopk];   // destination row of choice k, 0 if skipped
     const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
-    int *hall = reinterpret_cast<int *>(lds);   // [E] live choices per expert
-    int *hbef = hall + E;                       // [E] ... in tokens before g
-    int *pfx = hbef + E;                        // [E] aligned counts, then their exclusive prefix
+    int *hall = reinterpret_cast<int *>(lds);   // [E + 1] live choices per expert (+ spare)
+    int *hbef = hall + E + 1;                   // [E + 1] ... in tokens before g
+    int *pfx = hbef + E + 1;                    // [E] aligned counts, then their exclusive prefix
     int *sids = pfx + E;                        // [ntok * K]
     float *sscale = reinterpret_cast<float *>(sids + size_t(ntok) * K);  // [G] (FP8)
 
@@ -258,32 +251,40 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
                 __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4, 0,
                                                  0);
     }
-    if (tid == 0 && blockIdx.x == 0)
-        for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
-    for (int i = tid; i < 2 * E; i += 256) hall[i] = 0;
+    // pointer tables, one per wavefront (lane 0)
+    if (lane == 0) {
+        if (wave == 0) table_to_lds(s_prow, a.rows);
+        if (wave == 1) table_to_lds(s_pw, a.roww);
+        if (wave == 2) table_to_lds(s_ps, a.scales);
+        if (wave == 3 && blockIdx.x == 0)
+            for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
+    }
+    for (int i = tid; i < 2 * (E + 1); i += 256) hall[i] = 0;
     if (myscale) sscale[tid] = scv;
     __syncthreads();
 
-    // 2. route check and the two histograms
+    // 2. route check and the two histograms (choices that are not live
+    // count into the spare slot at index E)
     uint64_t err = kNoError;
     for (int gg = tid; gg < ntok; gg += 256) {
         int ev[KMAX];
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) ev[k] = k < K ? sids[gg * K + k] : -1;
+        for (int k = 0; k < KMAX; ++k) {
+            const int val = sids[gg * K + (k < K ? k : K - 1)];
+            ev[k] = k < K ? val : -1;
+        }
         int ss = 0, tt = 0;
         if (blockIdx.x == 0) {
             ss = src_of_lds(s_off, N, gg);
             tt = gg - s_off[ss];
         }
-        const uint32_t live = classify_token<KMAX>(ev, K, E, ss, tt, err);
+        const uint32_t live = classify_token<KMAX>(ev, E, ss, tt, err);
         const bool before = gg < g;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k >= K) break;
-            if ((live >> k) & 1u) {
-                atomicAdd(&hall[ev[k]], 1);
-                if (before) atomicAdd(&hbef[ev[k]], 1);
-            }
+            const bool l = (live >> k) & 1u;
+            atomicAdd(&hall[l ? ev[k] : E], 1);
+            atomicAdd(&hbef[(l && before) ? ev[k] : E], 1);
         }
         if (gg == g) s_live = live;
     }
@@ -308,44 +309,53 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
             part = e / a.E_loc;
         }
         const int packed = part < 0 ? -1 : ((part << 24) | row);
-        s_row[tid] = packed;
-        s_w[tid] = wk;
         int2 sl;
         sl.x = packed;
         sl.y = __float_as_int(wk);
         reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + tid] = sl;
+        uint64_t d = 0;
+        if (part >= 0) {
+            d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
+            reinterpret_cast<float *>(s_pw[part])[row] = wk;
+        }
+        s_dst[tid] = d;
+        s_row[tid] = packed;
     }
     __syncthreads();
 
-    // 5. stores: the row to every live slot, its weight and scales
-    for (int k = 0; k < K; ++k) {
-        const int pr = uni(s_row[k]);
-        if (pr < 0) continue;
-        const int f = pr >> 24, row = pr & 0xFFFFFF;
-        const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[f] + int64_t(row) * a.row_bytes);
+    // 5. stores: the row to every live slot, and the FP8 scales
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (k >= K) break;
+        const uint64_t d = s_dst[k];
+        if (d == 0) continue;
+        const gptr<u32x4> dst = (gptr<u32x4>)d;
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
             if (c < a.nvec) dst[c] = v[i];
         }
-        if (tid == 0) a.roww[f][row] = s_w[k];
-        if (myscale) a.scales[f][int64_t(row) * G + tid] = sscale[tid];
+        if (myscale) {
+            const int pr = s_row[k];
+            reinterpret_cast<float *>(s_ps[pr >> 24])[int64_t(pr & 0xFFFFFF) * G + tid] = sscale[tid];
+        }
     }
 }
 
-// Tile histogram of larger rounds.  Block = 8 wavefronts = one 512-token
-// tile, lane = token.  blkcnt[tile][e] = live choices of expert e in the
+// Tile histogram of larger rounds.  Block = kLayoutTile / 64 wavefronts =
+// one tile of kLayoutTile tokens, lane = token.  blkcnt[tile][e] = live choices of expert e in the
 // tile; packed[g][k] = (expert << 16) | rank of the choice among the tile's
 // choices of that expert (source, token order), or -1.
 template <int KMAX>
-__global__ __launch_bounds__(512) void k_layout(DispatchArgs a)
+__global__ __launch_bounds__(kLayoutTile) void k_layout(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ const int32_t *s_ids[kMaxSources];
     const int E = a.E, K = a.K, N = a.N;
-    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [8][E]
-    int *pre = reinterpret_cast<int *>(mask + size_t(8) * E);                 // [8][E]
+    constexpr int NW = kLayoutTile / kWave;
+    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
+    int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int g = blockIdx.x * kLayoutTile + tid;
     const bool have = g < a.ntok;
@@ -354,48 +364,55 @@ __global__ __launch_bounds__(512) void k_layout(DispatchArgs a)
         for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
         for (int q = 0; q < N; ++q) s_ids[q] = a.ids[q];
     }
-    for (int i = tid; i < 8 * E; i += 512) mask[i] = 0ull;
+    for (int i = tid; i < NW * (E + 1); i += kLayoutTile) mask[i] = 0ull;
     __syncthreads();
 
     int ev[KMAX];
     int s = 0, t = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) ev[k] = -1;
     if (have) {
         s = src_of_lds(s_off, N, g);
         t = g - s_off[s];
         const gptr<const int32_t> idp = (gptr<const int32_t>)s_ids[s] + int64_t(t) * K;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) ev[k] = k < K ? idp[k] : -1;
+        for (int k = 0; k < KMAX; ++k) {
+            const int val = idp[k < K ? k : K - 1];
+            ev[k] = k < K ? val : -1;
+        }
     }
     uint32_t live = 0;
-    if (have) {
+    {
         uint64_t err = kNoError;
-        live = classify_token<KMAX>(ev, K, E, s, t, err);
+        live = classify_token<KMAX>(ev, E, s, t, err);
         if (err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
-        mark_token<KMAX>(ev, K, live, mask + size_t(wave) * E, 1ull << lane);
+        // mark the token's lane bit per live expert (others into the spare slot E)
+        unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        const unsigned long long bit = 1ull << lane;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E], bit);
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 512) {
+    for (int e = tid; e < E; e += kLayoutTile) {
         int run = 0;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
+        for (int w = 0; w < NW; ++w) {
             pre[w * E + e] = run;
-            run += __popcll(mask[w * E + e]);
+            run += __popcll(mask[w * (E + 1) + e]);
         }
         a.blkcnt[blockIdx.x * E + e] = run;
     }
     __syncthreads();
     if (have) {
         const unsigned long long below = (1ull << lane) - 1ull;
+        const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
         int32_t *pk = a.packed + int64_t(g) * K;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (k >= K) break;
-            int val = -1;
-            if ((live >> k) & 1u) {
-                const int e = ev[k];
-                val = (e << 16) | (pre[wave * E + e] + __popcll(mask[wave * E + e] & below));
-            }
-            pk[k] = val;
+            const bool l = (live >> k) & 1u;
+            const int e = l ? ev[k] : 0;
+            const int val = l ? ((e << 16) | (pre[wave * E + e] + __popcll(mrow[e] & below))) : -1;
+            if (k < K) pk[k] = val;
         }
     }
 }
@@ -415,6 +432,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     constexpr int TB = 4 * W;
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_tot[4];
+    __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     int *base = reinterpret_cast<int *>(lds);   // [E]
     int *A = base + a.E;                        // [E]
     int *Cs = A + a.E;                          // [E]
@@ -448,6 +466,12 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         }
     }
 
+    if (lane == 0) {
+        if (wave == 0) table_to_lds(s_prow, a.rows);
+        if (wave == 1) table_to_lds(s_pw, a.roww);
+        if (wave == 2) table_to_lds(s_ps, a.scales);
+    }
+
     // 2. this tile's first row of every expert
     for (int e = tid; e < E; e += 256) {
         int C = 0, before = 0;
@@ -469,16 +493,21 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     }
     __syncthreads();
 
-    // 3. slots and stores, token by token
+    // 3. slots and stores, token by token; lane k owns choice k and the
+    // address of its row, which the store loop broadcasts
 #pragma unroll
     for (int j = 0; j < W; ++j) {
         const int g = g_first + wave * W + j;
         if (g >= ntok) break;
         int part = -1, row = -1;
+        uint64_t d = 0, ds = 0;
         if (pk[j] >= 0) {
             const int e = pk[j] >> 16;
             row = base[e] + (pk[j] & 0xFFFF);
             part = e / a.E_loc;
+            d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
+            ds = s_ps[part] + uint64_t(row) * uint64_t(a.G) * 4u;
+            reinterpret_cast<float *>(s_pw[part])[row] = wk[j];
         }
         if (lane < K) {
             int2 sl;
@@ -486,17 +515,17 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
             sl.y = __float_as_int(wk[j]);
             reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
         }
+        const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
         for (int k = 0; k < K; ++k) {
-            const int pr = __builtin_amdgcn_readlane(part, k);
-            if (pr < 0) continue;
-            const int rw = __builtin_amdgcn_readlane(row, k);
-            const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[pr] + int64_t(rw) * a.row_bytes);
+            const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                                (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+            if (dk == 0) continue;
+            const gptr<u32x4> dst = (gptr<u32x4>)dk;
 #pragma unroll
             for (int i = 0; i < VMAX; ++i) {
                 const int c = i * kWave + lane;
                 if (c < nvec) dst[c] = v[j][i];
             }
-            if (lane == 0) a.roww[pr][rw] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk[j]), k));
         }
         // rows longer than 64 * VMAX columns: the remaining columns, chunk by chunk
         if (nvec > kWave * VMAX) {
@@ -511,10 +540,10 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
                     if (c < nvec) r[i] = xs[c];
                 }
                 for (int k = 0; k < K; ++k) {
-                    const int pr = __builtin_amdgcn_readlane(part, k);
-                    if (pr < 0) continue;
-                    const int rw = __builtin_amdgcn_readlane(row, k);
-                    const gptr<u32x4> dst = (gptr<u32x4>)(a.rows[pr] + int64_t(rw) * a.row_bytes);
+                    const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                                        (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+                    if (dk == 0) continue;
+                    const gptr<u32x4> dst = (gptr<u32x4>)dk;
 #pragma unroll
                     for (int i = 0; i < VMAX; ++i) {
                         const int c = cb + i * kWave + lane;
@@ -529,13 +558,14 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
             const gptr<const float> sc = (gptr<const float>)a.scale[s] + int64_t(t) * a.sst[s];
             const int64_t ssg = a.ssg[s];
             const int G = a.G;
+            const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
             for (int b = lane; b < G; b += kWave) {
                 const float val = sc[int64_t(b) * ssg];
                 for (int k = 0; k < K; ++k) {
-                    const int pr = __builtin_amdgcn_readlane(part, k);
-                    if (pr < 0) continue;
-                    const int rw = __builtin_amdgcn_readlane(row, k);
-                    a.scales[pr][int64_t(rw) * G + b] = val;
+                    const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                        (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                    if (sk == 0) continue;
+                    ((gptr<float>)sk)[b] = val;
                 }
             }
         }
@@ -551,25 +581,33 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 }
 
 // Combine: one wavefront per (token, segment of 64*VPL 16-byte columns).
+// Lane k < K loads the token's slot k and forms the address of its reply
+// row; the wavefront then issues every live row's loads before it
+// accumulates, in ascending k, with a float32 multiply and a separate add.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
 #pragma clang fp contract(off)
+    __shared__ uint64_t s_rp[kMaxParts];
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
     const int g = gw / a.nseg;
     const int seg = gw - g * a.nseg;
-    if (g >= a.ntok) return;
-    int sl_row = -1, sl_w = 0;
-    if (lane < a.K) {
-        const int2 sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
-        sl_row = sl.x;
-        sl_w = sl.y;
-    }
+    const bool live_wave = g < a.ntok;
+    int2 sl;
+    sl.x = -1;
+    sl.y = 0;
+    if (live_wave && lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
+    if (threadIdx.x == 0) table_to_lds(s_rp, a.reply);
+    __syncthreads();
+    if (!live_wave) return;
     const int s = src_of_uniform(a.tok_off, a.N, g);
     const int t = g - a.tok_off[s];
     const int nvec = a.nvec;
     const int c0 = seg * kWave * VPL + lane;
+    uint64_t raddr = 0;
+    if (sl.x >= 0) raddr = s_rp[sl.x >> 24] + uint64_t(sl.x & 0xFFFFFF) * uint64_t(a.H) * 2u;
+    const int rlo = int(uint32_t(raddr)), rhi = int(uint32_t(raddr >> 32));
     float acc[VPL][8];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -578,26 +616,22 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 
     for (int k0 = 0; k0 < a.K; k0 += 8) {
         u32x4 y[8][VPL];
+        uint64_t rk[8];
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const int pr = __builtin_amdgcn_readlane(sl_row, k0 + kk);
-            if (pr >= 0) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(a.reply[pr >> 24] + int64_t(pr & 0xFFFFFF) * a.H);
+            rk[kk] = uint64_t(uint32_t(__builtin_amdgcn_readlane(rlo, k0 + kk))) |
+                     (uint64_t(uint32_t(__builtin_amdgcn_readlane(rhi, k0 + kk))) << 32);
+            const gptr<const u32x4> src = (gptr<const u32x4>)rk[kk];
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int c = c0 + i * kWave;
-                    y[kk][i] = c < nvec ? src[c] : u32x4{0u, 0u, 0u, 0u};
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) y[kk][i] = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < VPL; ++i) {
+                const int c = c0 + i * kWave;
+                y[kk][i] = (rk[kk] != 0 && c < nvec) ? src[c] : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const int pr = __builtin_amdgcn_readlane(sl_row, k0 + kk);
-            if (pr < 0) continue;
-            const float w = __int_as_float(__builtin_amdgcn_readlane(sl_w, k0 + kk));
+            if (rk[kk] == 0) continue;
+            const float w = __int_as_float(__builtin_amdgcn_readlane(sl.y, k0 + kk));
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const uint32_t q[4] = {y[kk][i].x, y[kk][i].y, y[kk][i].z, y[kk][i].w};
@@ -613,7 +647,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
             }
         }
     }
-    u32x4 *o = reinterpret_cast<u32x4 *>(a.out[s] + int64_t(t) * a.H);
+    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(t) * a.H);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = c0 + i * kWave;
@@ -731,7 +765,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
-        const size_t lds = size_t(p.E) * 12 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
+        const size_t lds = size_t(p.E + 1) * 8 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
         dim3 grid(p.ntok > 0 ? p.ntok : 1);
         switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);
@@ -740,9 +774,10 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         default: return launch_fused_v<8>(a, k32, grid, lds, st);
         }
     }
-    const size_t lds = size_t(8) * p.E * 12;
-    if (k32) hipLaunchKernelGGL(k_layout<32>, dim3(p.nblk), dim3(512), lds, st, a);
-    else hipLaunchKernelGGL(k_layout<8>, dim3(p.nblk), dim3(512), lds, st, a);
+    constexpr int NW = kLayoutTile / kWave;
+    const size_t lds = size_t(NW) * (p.E + 1) * 8 + size_t(NW) * p.E * 4;
+    if (k32) hipLaunchKernelGGL(k_layout<32>, dim3(p.nblk), dim3(kLayoutTile), lds, st, a);
+    else hipLaunchKernelGGL(k_layout<8>, dim3(p.nblk), dim3(kLayoutTile), lds, st, a);
     if (launched_ok()) return 1;
     switch (vm) {
     case 1: return launch_scatter_v<1>(a, p.ntok, p.E, st);

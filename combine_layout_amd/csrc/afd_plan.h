@@ -15,9 +15,9 @@ constexpr int kMaxParts = AFD_MAX_PARTITIONS;
 constexpr int kMaxExperts = AFD_MAX_EXPERTS;
 constexpr int kMaxTopk = AFD_MAX_TOPK;
 
-// Tokens handled by one workgroup of the layout kernel (8 wavefronts of
+// Tokens handled by one workgroup of the layout kernel (4 wavefronts of
 // 64 lanes, one token per lane; a wavefront's 64 tokens form one chunk).
-constexpr int kLayoutTile = 512;
+constexpr int kLayoutTile = 256;
 // Small rounds rebuild the layout inside every scatter workgroup (one kernel
 // for the whole dispatch): at most this many tokens, ids (staged in LDS) and
 // experts, and rows of at most this many 16-byte columns.

@@ -379,14 +379,14 @@ def test_split_path_above_fused_limits(lib):
     lib.afd_fake_log_clear()
     assert x.dispatch(0, 300) == 0 and x.dispatch(1, 300) == 0
     assert x.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=2 T=300,300"]
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=3 T=300,300"]      # 256-token layout tiles
     x.destroy()
     c2 = cfg(N=1, F=2, E=32, K=16, cap=2048)
     y = Ctx(lib, c2)
     lib.afd_fake_log_clear()
     assert y.dispatch(0, 300) == 0                               # 4800 ids > the fused limit
     assert y.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=1 T=300"]
+    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=2 T=300"]
     y.destroy()
 
 
