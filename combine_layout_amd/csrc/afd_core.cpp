@@ -158,7 +158,8 @@ void build_plan(afd_ctx *c)
     p.ntok = p.tok_off[p.N];
     p.fused = p.ntok <= kFusedMaxTokens && int64_t(p.ntok) * p.K <= kFusedMaxIds && p.E <= kFusedMaxExperts &&
               p.row_bytes / 16 <= kFusedMaxCols;
-    p.nblk = (p.ntok + kLayoutTile - 1) / kLayoutTile;
+    p.tile = kLayoutTile;
+    p.nblk = (p.ntok + p.tile - 1) / p.tile;
     if (p.nblk < 1) p.nblk = 1;
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];
     for (int f = 0; f < p.F; ++f) {

@@ -29,7 +29,10 @@
 //   k_copy    inbox -> caller output (single-partition collect without view).
 //
 // Nothing here uses MFMA: the round is data movement plus one multiply-add
-// per reply element, bound by HBM bandwidth.
+// per reply element, bound by HBM bandwidth.  Expanded rows are written and
+// replies read with non-temporal hints: each byte is touched once, and
+// keeping them out of the caches stops a round's row writes from evicting
+// (and writing back into) the next kernel's working set.
 
 #include <hip/hip_runtime.h>
 
@@ -58,7 +61,7 @@ struct DispatchArgs {
     float *scales[kMaxParts];
     float *roww[kMaxParts];
     int tok_off[kMaxSources + 1];
-    int N, ntok, K, E, E_loc, alpha, nblk, nvec, G, fp8;
+    int N, ntok, K, E, E_loc, alpha, nblk, nvec, G, fp8, tile;
     int64_t row_bytes;
     uint64_t *err;
     uint32_t *counter;
@@ -118,6 +121,17 @@ __device__ __forceinline__ uint64_t make_err(int s, int t, int k, unsigned code)
 
 __device__ __forceinline__ int align_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a full
+// workgroup fence: it waits for every outstanding global load and store of
+// the wave (the vector-memory counter), which would stall on row loads and
+// store acknowledgements that the LDS phase does not need.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum of vals[0..n) (LDS), in place, by a block of BLOCK
 // threads; each thread owns ceil(n / BLOCK) consecutive entries.
 template <int BLOCK>
@@ -136,7 +150,7 @@ __device__ void block_exclusive_scan(int *vals, int n, int *wave_tot)
         if (lane >= d) x += y;
     }
     if (lane == kWave - 1) wave_tot[tid / kWave] = x;
-    __syncthreads();
+    lds_barrier();
     if (tid < kWave) {
         const int v = tid < BLOCK / kWave ? wave_tot[tid] : 0;
         int xi = v;
@@ -147,14 +161,14 @@ __device__ void block_exclusive_scan(int *vals, int n, int *wave_tot)
         }
         if (tid < BLOCK / kWave) wave_tot[tid] = xi - v;
     }
-    __syncthreads();
+    lds_barrier();
     int run = wave_tot[tid / kWave] + x - sum;
     for (int i = lo; i < hi; ++i) {
         const int v = vals[i];
         vals[i] = run;
         run += v;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // Copy of a kernel-argument pointer array into LDS (thread 0, constant
@@ -289,12 +303,12 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         if (gg == g) s_live = live;
     }
     if (blockIdx.x == 0 && err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
-    __syncthreads();
+    lds_barrier();
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
     // partitions); expert e starts at pfx[e] - pfx[first expert of its part]
     for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hall[e], a.alpha);
-    __syncthreads();
+    lds_barrier();
     block_exclusive_scan<256>(pfx, E, s_tot);
     if (blockIdx.x == 0)
         for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + hall[e];
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         s_dst[tid] = d;
         s_row[tid] = packed;
     }
-    __syncthreads();
+    lds_barrier();
 
     // 5. stores: the row to every live slot, and the FP8 scales
 #pragma unroll
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
-            if (c < a.nvec) dst[c] = v[i];
+            if (c < a.nvec) __builtin_nontemporal_store(v[i], &dst[c]);
         }
         if (myscale) {
             const int pr = s_row[k];
@@ -342,30 +356,30 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     }
 }
 
-// Tile histogram of larger rounds.  Block = kLayoutTile / 64 wavefronts =
-// one tile of kLayoutTile tokens, lane = token.  blkcnt[tile][e] = live choices of expert e in the
-// tile; packed[g][k] = (expert << 16) | rank of the choice among the tile's
-// choices of that expert (source, token order), or -1.
-template <int KMAX>
-__global__ __launch_bounds__(kLayoutTile) void k_layout(DispatchArgs a)
+// Tile histogram of larger rounds.  Block = NW wavefronts = one tile of
+// 64 * NW tokens, lane = token.  blkcnt[tile][e] = live choices of expert e
+// in the tile; packed[g][k] = (expert << 16) | rank of the choice among the
+// tile's choices of that expert (source, token order), or -1.
+template <int KMAX, int NW>
+__global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ const int32_t *s_ids[kMaxSources];
     const int E = a.E, K = a.K, N = a.N;
-    constexpr int NW = kLayoutTile / kWave;
+    constexpr int TILE = NW * kWave;
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
     int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-    const int g = blockIdx.x * kLayoutTile + tid;
+    const int g = blockIdx.x * TILE + tid;
     const bool have = g < a.ntok;
 
     if (tid == 0) {
         for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
         for (int q = 0; q < N; ++q) s_ids[q] = a.ids[q];
     }
-    for (int i = tid; i < NW * (E + 1); i += kLayoutTile) mask[i] = 0ull;
-    __syncthreads();
+    for (int i = tid; i < NW * (E + 1); i += TILE) mask[i] = 0ull;
+    lds_barrier();
 
     int ev[KMAX];
     int s = 0, t = 0;
@@ -392,8 +406,8 @@ __global__ __launch_bounds__(kLayoutTile) void k_layout(DispatchArgs a)
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E], bit);
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kLayoutTile) {
+    lds_barrier();
+    for (int e = tid; e < E; e += TILE) {
         int run = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -402,7 +416,7 @@ __global__ __launch_bounds__(kLayoutTile) void k_layout(DispatchArgs a)
         }
         a.blkcnt[blockIdx.x * E + e] = run;
     }
-    __syncthreads();
+    lds_barrier();
     if (have) {
         const unsigned long long below = (1ull << lane) - 1ull;
         const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
@@ -419,53 +433,62 @@ __global__ __launch_bounds__(kLayoutTile) void k_layout(DispatchArgs a)
 
 // Scatter of larger rounds.  Block = 4 wavefronts; wavefront w handles the
 // W = 8 / VMAX consecutive tokens starting at block_first + w * W (a block's
-// tokens lie in one layout tile).  Every block first turns the tile counts
-// into this tile's first row per expert:
+// tokens lie in one layout tile).  Every block turns the tile counts into
+// this tile's first row per expert itself:
 //   base[e] = start_e + sum of counts of e in earlier tiles,
 //   start_e = aligned prefix of the partition's experts before e,
-// which needs no communication between blocks.  The rows, ids' ranks and
-// weights are requested before that scan; the stores follow it.
+// which needs no communication between blocks.  The tile counts are
+// requested first and the rows, ranks and weights right after, so the scan
+// (LDS-only barriers) runs while the rows are still in flight.
 template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 {
     constexpr int W = VMAX >= 8 ? 1 : 8 / VMAX;
     constexpr int TB = 4 * W;
+    constexpr int CPT = 4;                      // tile counts fetched per thread up front
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_tot[4];
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
+    const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok, nblk = a.nblk;
     int *base = reinterpret_cast<int *>(lds);   // [E]
-    int *A = base + a.E;                        // [E]
-    int *Cs = A + a.E;                          // [E]
+    int *A = base + E;                          // [E]
+    int *Cs = A + E;                            // [E]
+    int *cnt = Cs + E;                          // [nblk * E] when it fits 256 * CPT
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
-    const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok;
     const int g_first = blockIdx.x * TB;
-    const int tile = g_first / kLayoutTile;
+    const int tile = g_first / a.tile;
+    const int ncnt = nblk * E;
+    const bool staged = ncnt <= 256 * CPT;
 
-    // 1. request the rows and the ranks of this wavefront's tokens
+    // 1. tile counts first, then the rows, ranks and weights of this
+    // wavefront's tokens (a fixed number of loads each, so the scan below
+    // waits for the counts only)
+    int cv[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int idx = tid + j * 256;
+        cv[j] = a.blkcnt[idx < ncnt ? idx : 0];
+    }
     u32x4 v[W][VMAX];
     int pk[W];
     float wk[W];
 #pragma unroll
     for (int j = 0; j < W; ++j) {
-        const int g = g_first + wave * W + j;
-        pk[j] = -1;
-        wk[j] = 0.0f;
-        if (g < ntok) {
-            const int s = src_of_uniform(a.tok_off, a.N, g);
-            const int t = g - a.tok_off[s];
-            const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
+        const int gj = g_first + wave * W + j;
+        const int g = gj < ntok ? gj : ntok - 1;
+        const int s = src_of_uniform(a.tok_off, a.N, g);
+        const int t = g - a.tok_off[s];
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
 #pragma unroll
-            for (int i = 0; i < VMAX; ++i) {
-                const int c = i * kWave + lane;
-                if (c < nvec) v[j][i] = xs[c];
-            }
-            if (lane < K) {
-                pk[j] = a.packed[int64_t(g) * K + lane];
-                wk[j] = a.w[s][int64_t(t) * K + lane];
-            }
+        for (int i = 0; i < VMAX; ++i) {
+            const int c = i * kWave + lane;
+            v[j][i] = xs[c < nvec ? c : 0];
         }
+        const int kl = lane < K ? lane : 0;
+        pk[j] = a.packed[int64_t(g) * K + kl];
+        wk[j] = a.w[s][int64_t(t) * K + kl];
+        if (lane >= K || gj >= ntok) pk[j] = -1;
     }
-
     if (lane == 0) {
         if (wave == 0) table_to_lds(s_prow, a.rows);
         if (wave == 1) table_to_lds(s_pw, a.roww);
@@ -473,10 +496,18 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     }
 
     // 2. this tile's first row of every expert
+    if (staged) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int idx = tid + j * 256;
+            if (idx < ncnt) cnt[idx] = cv[j];
+        }
+    }
+    lds_barrier();
     for (int e = tid; e < E; e += 256) {
         int C = 0, before = 0;
-        for (int b = 0; b < a.nblk; ++b) {
-            const int c = a.blkcnt[b * E + e];
+        for (int b = 0; b < nblk; ++b) {
+            const int c = staged ? cnt[b * E + e] : a.blkcnt[b * E + e];
             C += c;
             before += b < tile ? c : 0;
         }
@@ -484,14 +515,14 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         Cs[e] = C;
         base[e] = before;
     }
-    __syncthreads();
+    lds_barrier();
     block_exclusive_scan<256>(A, E, s_tot);
     for (int e = tid; e < E; e += 256) {
         const int start = A[e] - A[(e / a.E_loc) * a.E_loc];
         base[e] += start;
         if (blockIdx.x == 0) a.ends[e] = start + Cs[e];
     }
-    __syncthreads();
+    lds_barrier();
 
     // 3. slots and stores, token by token; lane k owns choice k and the
     // address of its row, which the store loop broadcasts
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 #pragma unroll
             for (int i = 0; i < VMAX; ++i) {
                 const int c = i * kWave + lane;
-                if (c < nvec) dst[c] = v[j][i];
+                if (c < nvec) __builtin_nontemporal_store(v[j][i], &dst[c]);
             }
         }
         // rows longer than 64 * VMAX columns: the remaining columns, chunk by chunk
@@ -547,7 +578,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 #pragma unroll
                     for (int i = 0; i < VMAX; ++i) {
                         const int c = cb + i * kWave + lane;
-                        if (c < nvec) dst[c] = r[i];
+                        if (c < nvec) __builtin_nontemporal_store(r[i], &dst[c]);
                     }
                 }
             }
@@ -625,7 +656,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int c = c0 + i * kWave;
-                y[kk][i] = (rk[kk] != 0 && c < nvec) ? src[c] : u32x4{0u, 0u, 0u, 0u};
+                y[kk][i] = (rk[kk] != 0 && c < nvec) ? __builtin_nontemporal_load(&src[c]) : u32x4{0u, 0u, 0u, 0u};
             }
         }
 #pragma unroll
@@ -695,6 +726,7 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.E_loc = p.E_loc;
     a.alpha = p.alpha;
     a.nblk = p.nblk;
+    a.tile = p.tile;
     a.nvec = int(p.row_bytes / 16);
     a.G = p.G;
     a.fp8 = p.fp8;
@@ -732,7 +764,9 @@ template <int VMAX>
 int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
-    hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), size_t(E) * 12, st, a);
+    const size_t ncnt = size_t(a.nblk) * E;
+    const size_t lds = size_t(E) * 12 + (ncnt <= 1024 ? ncnt * 4 : 0);
+    hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), lds, st, a);
     return launched_ok();
 }
 
@@ -774,10 +808,11 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         default: return launch_fused_v<8>(a, k32, grid, lds, st);
         }
     }
-    constexpr int NW = kLayoutTile / kWave;
-    const size_t lds = size_t(NW) * (p.E + 1) * 8 + size_t(NW) * p.E * 4;
-    if (k32) hipLaunchKernelGGL(k_layout<32>, dim3(p.nblk), dim3(kLayoutTile), lds, st, a);
-    else hipLaunchKernelGGL(k_layout<8>, dim3(p.nblk), dim3(kLayoutTile), lds, st, a);
+    {
+        const size_t lds = size_t(4) * (p.E + 1) * 8 + size_t(4) * p.E * 4;
+        if (k32) hipLaunchKernelGGL((k_layout<32, 4>), dim3(p.nblk), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((k_layout<8, 4>), dim3(p.nblk), dim3(256), lds, st, a);
+    }
     if (launched_ok()) return 1;
     switch (vm) {
     case 1: return launch_scatter_v<1>(a, p.ntok, p.E, st);
@@ -809,16 +844,10 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     a.H = p.H;
     a.nvec = p.H / 8;
     a.slot = p.slot;
-    const int64_t waves1 = int64_t(p.ntok) * ((a.nvec + kWave - 1) / kWave);
-    int vpl = 1;
-    if (waves1 >= 32768) vpl = 4;
-    else if (waves1 >= 8192) vpl = 2;
-    a.nseg = (a.nvec + kWave * vpl - 1) / (kWave * vpl);
+    a.nseg = (a.nvec + kWave - 1) / kWave;
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
-    if (vpl == 4) hipLaunchKernelGGL(k_combine<4>, grid, dim3(256), 0, st, a);
-    else if (vpl == 2) hipLaunchKernelGGL(k_combine<2>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, st, a);
     return launched_ok();
 }
 

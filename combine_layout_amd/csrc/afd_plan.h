@@ -15,8 +15,8 @@ constexpr int kMaxParts = AFD_MAX_PARTITIONS;
 constexpr int kMaxExperts = AFD_MAX_EXPERTS;
 constexpr int kMaxTopk = AFD_MAX_TOPK;
 
-// Tokens handled by one workgroup of the layout kernel (4 wavefronts of
-// 64 lanes, one token per lane; a wavefront's 64 tokens form one chunk).
+// Tokens handled by one workgroup of the layout kernel (4 wavefronts of 64
+// lanes, one token per lane; a wavefront's 64 tokens form one chunk).
 constexpr int kLayoutTile = 256;
 // Small rounds rebuild the layout inside every scatter workgroup (one kernel
 // for the whole dispatch): at most this many tokens, ids (staged in LDS) and
@@ -58,6 +58,7 @@ struct RoundPlan {
     int tok_off[kMaxSources + 1] = {};
     bool fused = false;      // one-kernel dispatch
     int nblk = 0;            // layout tiles (split path)
+    int tile = 0;            // tokens per layout tile
     // per source
     const void *x[kMaxSources] = {};
     const int32_t *ids[kMaxSources] = {};
