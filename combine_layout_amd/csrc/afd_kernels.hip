@@ -50,13 +50,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- args ----
 
+// One record per source, 64 bytes: a kernel reads the record of a source
+// it has just identified with a single scalar load.
+struct SourceArgs {
+    const uint8_t *x;        // [T, row_bytes]
+    const float *w;          // [T, K]
+    const int32_t *ids;      // [T, K]
+    const float *scale;      // FP8 only: scale of (t, block b) at t * sst + b * ssg
+    int64_t sst, ssg;
+    int64_t off;             // first token of the source in the round's token order
+    int64_t pad;
+};
+
 struct DispatchArgs {
-    const int32_t *ids[kMaxSources];
-    const uint8_t *x[kMaxSources];
-    const float *w[kMaxSources];
-    const float *scale[kMaxSources];
-    int64_t sst[kMaxSources];
-    int64_t ssg[kMaxSources];
+    SourceArgs src[kMaxSources];
     uint8_t *rows[kMaxParts];
     float *scales[kMaxParts];
     float *roww[kMaxParts];
@@ -95,23 +102,46 @@ using lptr = __attribute__((address_space(3))) T *;
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int wave_id() { return uni(threadIdx.x / kWave); }
 
-// Source of global token g (g uniform): the number of sources q >= 1 whose
-// first token is at or before g (empty sources share their successor's
-// offset).  Only constant indices into the kernarg array.
-__device__ __forceinline__ int src_of_uniform(const int (&tok_off)[kMaxSources + 1], int N, int g)
-{
-    int s = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxSources; ++q) s += (q < N && g >= tok_off[q]) ? 1 : 0;
-    return uni(s);
-}
-
-// The same from an LDS copy of the offsets, for per-lane tokens.
+// Source of global token g from an LDS copy of the token offsets.
 __device__ __forceinline__ int src_of_lds(const int *tok_off, int N, int g)
 {
     int s = 0;
     for (int q = 1; q < N; ++q) s += g >= tok_off[q] ? 1 : 0;
     return s;
+}
+
+// Source of global token g for a wave-uniform g: the number of sources q >= 1
+// whose first token is at or before g (empty sources share their
+// successor's offset).  The offsets are read at constant offsets, with the
+// kernel's first scalar loads.
+template <typename Args>
+__device__ __forceinline__ int source_of(const Args &a, int g)
+{
+    int s = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxSources; ++q) s += (q < a.N && g >= a.tok_off[q]) ? 1 : 0;
+    return uni(s);
+}
+
+// Id pointer and first token of the source of a per-lane token g: per-lane
+// selects over records read at constant offsets (a per-lane index into the
+// kernel arguments would become a dependent vector load per lane).
+struct LaneSource {
+    const int32_t *ids;
+    int s, off;
+};
+
+__device__ __forceinline__ LaneSource lane_source(const DispatchArgs &a, int g)
+{
+    LaneSource r{a.src[0].ids, 0, 0};
+#pragma unroll
+    for (int q = 1; q < kMaxSources; ++q) {
+        const bool in = q < a.N && g >= a.tok_off[q];
+        r.ids = in ? a.src[q].ids : r.ids;
+        r.s = in ? q : r.s;
+        r.off = in ? a.tok_off[q] : r.off;
+    }
+    return r;
 }
 
 __device__ __forceinline__ uint64_t make_err(int s, int t, int k, unsigned code)
@@ -238,13 +268,14 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
     const bool mine = g < ntok;
-    const int s = mine ? src_of_uniform(a.tok_off, N, g) : 0;
-    const int t = g - a.tok_off[s];
+    const int s = source_of(a, mine ? g : 0);
+    const SourceArgs &src = a.src[s];
+    const int t = g - int(src.off);
 
     // 1. request every load: row, weights, scales, all ids
     u32x4 v[VMAX];
     if (mine) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
@@ -252,14 +283,14 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         }
     }
     float wk = 0.0f;
-    if (mine && tid < K) wk = a.w[s][int64_t(t) * K + tid];
+    if (mine && tid < K) wk = src.w[int64_t(t) * K + tid];
     float scv = 0.0f;
     const bool myscale = mine && a.fp8 && tid < G;
-    if (myscale) scv = a.scale[s][int64_t(t) * a.sst[s] + int64_t(tid) * a.ssg[s]];
+    if (myscale) scv = src.scale[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
     for (int q = 0; q < N; ++q) {
         const int lo = a.tok_off[q] * K;
         const int n = a.tok_off[q + 1] * K - lo;
-        const gptr<const int32_t> src = (gptr<const int32_t>)a.ids[q];
+        const gptr<const int32_t> src = (gptr<const int32_t>)a.src[q].ids;
         for (int base = wave * kWave; base < n; base += 256)
             if (base + lane < n)
                 __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4, 0,
@@ -364,9 +395,7 @@ template <int KMAX, int NW>
 __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int s_off[kMaxSources + 1];
-    __shared__ const int32_t *s_ids[kMaxSources];
-    const int E = a.E, K = a.K, N = a.N;
+    const int E = a.E, K = a.K;
     constexpr int TILE = NW * kWave;
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
     int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
@@ -374,27 +403,23 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     const int g = blockIdx.x * TILE + tid;
     const bool have = g < a.ntok;
 
-    if (tid == 0) {
-        for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
-        for (int q = 0; q < N; ++q) s_ids[q] = a.ids[q];
-    }
-    for (int i = tid; i < NW * (E + 1); i += TILE) mask[i] = 0ull;
-    lds_barrier();
-
     int ev[KMAX];
     int s = 0, t = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) ev[k] = -1;
     if (have) {
-        s = src_of_lds(s_off, N, g);
-        t = g - s_off[s];
-        const gptr<const int32_t> idp = (gptr<const int32_t>)s_ids[s] + int64_t(t) * K;
+        const LaneSource src = lane_source(a, g);
+        s = src.s;
+        t = g - src.off;
+        const gptr<const int32_t> idp = (gptr<const int32_t>)src.ids + int64_t(t) * K;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             const int val = idp[k < K ? k : K - 1];
             ev[k] = k < K ? val : -1;
         }
     }
+    for (int i = tid; i < NW * (E + 1); i += TILE) mask[i] = 0ull;
+    lds_barrier();
     uint32_t live = 0;
     {
         uint64_t err = kNoError;
@@ -472,13 +497,14 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     u32x4 v[W][VMAX];
     int pk[W];
     float wk[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
+    // The wavefront's tokens nearly always share a source: then one record
+    // lookup serves all of them (per-token lookups would each wait on a
+    // scalar load).
+    auto load_token = [&](int j, const SourceArgs &src) {
         const int gj = g_first + wave * W + j;
         const int g = gj < ntok ? gj : ntok - 1;
-        const int s = src_of_uniform(a.tok_off, a.N, g);
-        const int t = g - a.tok_off[s];
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(a.x[s] + int64_t(t) * a.row_bytes);
+        const int t = g - int(src.off);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = i * kWave + lane;
@@ -486,8 +512,24 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         }
         const int kl = lane < K ? lane : 0;
         pk[j] = a.packed[int64_t(g) * K + kl];
-        wk[j] = a.w[s][int64_t(t) * K + kl];
+        wk[j] = src.w[int64_t(t) * K + kl];
         if (lane >= K || gj >= ntok) pk[j] = -1;
+    };
+    {
+        const int g_lo = g_first + wave * W < ntok ? g_first + wave * W : ntok - 1;
+        const int g_hi = g_first + wave * W + W - 1 < ntok ? g_first + wave * W + W - 1 : ntok - 1;
+        const int s_lo = source_of(a, g_lo);
+        if (s_lo == source_of(a, g_hi)) {
+            const SourceArgs &src = a.src[s_lo];
+#pragma unroll
+            for (int j = 0; j < W; ++j) load_token(j, src);
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                const int gj = g_first + wave * W + j;
+                load_token(j, a.src[source_of(a, gj < ntok ? gj : ntok - 1)]);
+            }
+        }
     }
     if (lane == 0) {
         if (wave == 0) table_to_lds(s_prow, a.rows);
@@ -560,9 +602,8 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         }
         // rows longer than 64 * VMAX columns: the remaining columns, chunk by chunk
         if (nvec > kWave * VMAX) {
-            const int s = src_of_uniform(a.tok_off, a.N, g);
-            const gptr<const u32x4> xs =
-                (gptr<const u32x4>)(a.x[s] + int64_t(g - a.tok_off[s]) * a.row_bytes);
+            const SourceArgs &src = a.src[source_of(a, g)];
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + (g - src.off) * a.row_bytes);
             for (int cb = kWave * VMAX; cb < nvec; cb += kWave * VMAX) {
                 u32x4 r[VMAX];
 #pragma unroll
@@ -584,10 +625,10 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
             }
         }
         if (a.fp8) {
-            const int s = src_of_uniform(a.tok_off, a.N, g);
-            const int t = g - a.tok_off[s];
-            const gptr<const float> sc = (gptr<const float>)a.scale[s] + int64_t(t) * a.sst[s];
-            const int64_t ssg = a.ssg[s];
+            const SourceArgs &src = a.src[source_of(a, g)];
+            const int t = g - int(src.off);
+            const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+            const int64_t ssg = src.ssg;
             const int G = a.G;
             const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
             for (int b = lane; b < G; b += kWave) {
@@ -632,7 +673,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     if (threadIdx.x == 0) table_to_lds(s_rp, a.reply);
     __syncthreads();
     if (!live_wave) return;
-    const int s = src_of_uniform(a.tok_off, a.N, g);
+    const int s = source_of(a, g);
     const int t = g - a.tok_off[s];
     const int nvec = a.nvec;
     const int c0 = seg * kWave * VPL + lane;
@@ -706,12 +747,14 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     DispatchArgs a;
     std::memset(&a, 0, sizeof(a));
     for (int s = 0; s < p.N; ++s) {
-        a.ids[s] = p.ids[s];
-        a.x[s] = static_cast<const uint8_t *>(p.x[s]);
-        a.w[s] = p.w[s];
-        a.scale[s] = p.fp8 ? p.scale[s] : nullptr;
-        a.sst[s] = p.sst[s];
-        a.ssg[s] = p.ssg[s];
+        SourceArgs &r = a.src[s];
+        r.ids = p.ids[s];
+        r.x = static_cast<const uint8_t *>(p.x[s]);
+        r.w = p.w[s];
+        r.scale = p.fp8 ? p.scale[s] : nullptr;
+        r.sst = p.sst[s];
+        r.ssg = p.ssg[s];
+        r.off = p.tok_off[s];
     }
     for (int f = 0; f < p.F; ++f) {
         a.rows[f] = static_cast<uint8_t *>(p.rows[f]);
