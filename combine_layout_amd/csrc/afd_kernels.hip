@@ -162,41 +162,39 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Exclusive prefix sum of vals[0..n) (LDS), in place, by a block of BLOCK
-// threads; each thread owns ceil(n / BLOCK) consecutive entries.
-template <int BLOCK>
-__device__ void block_exclusive_scan(int *vals, int n, int *wave_tot)
+// Inclusive prefix sum over the 64 lanes of a wavefront: DPP row shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then lane 15 of each row added into
+// the next row (rows 1, 3) and lane 31 into rows 2, 3.  Lanes without a
+// source lane read 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x)
 {
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int per = (n + BLOCK - 1) / BLOCK;
-    const int lo = tid * per;
-    const int hi = lo + per < n ? lo + per : n;
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += vals[i];
-    int x = sum;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) wave_tot[tid / kWave] = x;
-    lds_barrier();
-    if (tid < kWave) {
-        const int v = tid < BLOCK / kWave ? wave_tot[tid] : 0;
-        int xi = v;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int y = __shfl_up(xi, d, kWave);
-            if (tid >= d) xi += y;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum of vals[0..n) (LDS, visible to the block), in place.
+// Wavefront 0 does it alone, lane l owning ceil(n / 64) consecutive entries;
+// one barrier then publishes the result to the block.
+__device__ void block_exclusive_scan(int *vals, int n)
+{
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const int per = (n + kWave - 1) / kWave;
+        const int lo = lane * per;
+        const int hi = lo + per < n ? lo + per : n;
+        int sum = 0;
+        for (int i = lo; i < hi; ++i) sum += vals[i];
+        int run = wave_inclusive_scan(sum) - sum;
+        for (int i = lo; i < hi; ++i) {
+            const int v = vals[i];
+            vals[i] = run;
+            run += v;
         }
-        if (tid < BLOCK / kWave) wave_tot[tid] = xi - v;
-    }
-    lds_barrier();
-    int run = wave_tot[tid / kWave] + x - sum;
-    for (int i = lo; i < hi; ++i) {
-        const int v = vals[i];
-        vals[i] = run;
-        run += v;
     }
     lds_barrier();
 }
@@ -243,25 +241,25 @@ __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int E,
 // each thread holding up to VMAX 16-byte columns of the row.  The row, the
 // token's weights and scales and every id of the round (copied straight
 // into LDS) are requested at entry, so a block waits on memory once before
-// its stores.  The block then needs only two histograms of the round's live
+// its stores.  The block then needs two histograms of the round's live
 // choices: over all tokens (for the aligned starts of every expert) and over
 // the tokens before g (the rank of g's row inside each of its experts, since
 // a token holds an expert at most once):
 //   row(g, e) = start_e + #{live choices of e in tokens before g}.
+// Both are kept in one LDS word per expert (all tokens in the low 16 bits,
+// earlier tokens in the high 16), so each choice costs one atomic.
 template <int VMAX, int KMAX>
 __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int s_tot[4];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ int s_row[kMaxTopk];
     __shared__ uint32_t s_live;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     __shared__ uint64_t s_dst[kMaxTopk];   // destination row of choice k, 0 if skipped
     const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
-    int *hall = reinterpret_cast<int *>(lds);   // [E + 1] live choices per expert (+ spare)
-    int *hbef = hall + E + 1;                   // [E + 1] ... in tokens before g
-    int *pfx = hbef + E + 1;                    // [E] aligned counts, then their exclusive prefix
+    int *hist = reinterpret_cast<int *>(lds);   // [E + 1] per expert (+ spare): all | before << 16
+    int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
     int *sids = pfx + E;                        // [ntok * K]
     float *sscale = reinterpret_cast<float *>(sids + size_t(ntok) * K);  // [G] (FP8)
 
@@ -304,7 +302,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         if (wave == 3 && blockIdx.x == 0)
             for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
     }
-    for (int i = tid; i < 2 * (E + 1); i += 256) hall[i] = 0;
+    for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
     if (myscale) sscale[tid] = scv;
     __syncthreads();
 
@@ -324,13 +322,9 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
             tt = gg - s_off[ss];
         }
         const uint32_t live = classify_token<KMAX>(ev, E, ss, tt, err);
-        const bool before = gg < g;
+        const int inc = gg < g ? 0x10001 : 1;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const bool l = (live >> k) & 1u;
-            atomicAdd(&hall[l ? ev[k] : E], 1);
-            atomicAdd(&hbef[(l && before) ? ev[k] : E], 1);
-        }
+        for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
         if (gg == g) s_live = live;
     }
     if (blockIdx.x == 0 && err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
@@ -338,11 +332,11 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
     // partitions); expert e starts at pfx[e] - pfx[first expert of its part]
-    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hall[e], a.alpha);
+    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hist[e] & 0xFFFF, a.alpha);
     lds_barrier();
-    block_exclusive_scan<256>(pfx, E, s_tot);
+    block_exclusive_scan(pfx, E);
     if (blockIdx.x == 0)
-        for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + hall[e];
+        for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] & 0xFFFF);
     if (!mine) return;
 
     // 4. slot of choice k (thread k)
@@ -350,7 +344,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         int part = -1, row = -1;
         if ((s_live >> tid) & 1u) {
             const int e = sids[g * K + tid];
-            row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + hbef[e];
+            row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] >> 16);
             part = e / a.E_loc;
         }
         const int packed = part < 0 ? -1 : ((part << 24) | row);
@@ -472,7 +466,6 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     constexpr int TB = 4 * W;
     constexpr int CPT = 4;                      // tile counts fetched per thread up front
     extern __shared__ __align__(16) unsigned char lds[];
-    __shared__ int s_tot[4];
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok, nblk = a.nblk;
     int *base = reinterpret_cast<int *>(lds);   // [E]
@@ -558,7 +551,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         base[e] = before;
     }
     lds_barrier();
-    block_exclusive_scan<256>(A, E, s_tot);
+    block_exclusive_scan(A, E);
     for (int e = tid; e < E; e += 256) {
         const int start = A[e] - A[(e / a.E_loc) * a.E_loc];
         base[e] += start;
@@ -842,7 +835,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
-        const size_t lds = size_t(p.E + 1) * 8 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
+        const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
         dim3 grid(p.ntok > 0 ? p.ntok : 1);
         switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);
