@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 }
 
 // Tile histogram of larger rounds.  Block = NW wavefronts = one tile of
-// 64 * NW tokens, lane = token.  blkcnt[tile][e] = live choices of expert e
+// 64 * NW tokens, lane = token.  blkcnt[e][tile] = live choices of expert e
 // in the tile; packed[g][k] = (expert << 16) | rank of the choice among the
 // tile's choices of that expert (source, token order), or -1.
 template <int KMAX, int NW>
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
             pre[w * E + e] = run;
             run += __popcll(mask[w * (E + 1) + e]);
         }
-        a.blkcnt[blockIdx.x * E + e] = run;
+        a.blkcnt[e * a.nblk + blockIdx.x] = run;
     }
     lds_barrier();
     if (have) {
@@ -464,28 +464,26 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 {
     constexpr int W = VMAX >= 8 ? 1 : 8 / VMAX;
     constexpr int TB = 4 * W;
-    constexpr int CPT = 4;                      // tile counts fetched per thread up front
+    constexpr int PRE = 32;                     // tile counts of its expert a thread requests at entry
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok, nblk = a.nblk;
     int *base = reinterpret_cast<int *>(lds);   // [E]
     int *A = base + E;                          // [E]
     int *Cs = A + E;                            // [E]
-    int *cnt = Cs + E;                          // [nblk * E] when it fits 256 * CPT
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g_first = blockIdx.x * TB;
     const int tile = g_first / a.tile;
-    const int ncnt = nblk * E;
-    const bool staged = ncnt <= 256 * CPT;
+    const bool pre_all = nblk <= PRE;
 
-    // 1. tile counts first, then the rows, ranks and weights of this
-    // wavefront's tokens (a fixed number of loads each, so the scan below
-    // waits for the counts only)
-    int cv[CPT];
+    // 1. tile counts first (thread e: expert e's run of nblk counts, one
+    // independent load each), then the rows, ranks and weights of this
+    // wavefront's tokens, so the sums below wait for the counts only
+    int cv[PRE];
+    {
+        const gptr<const int32_t> cp = (gptr<const int32_t>)a.blkcnt + int64_t(tid < E ? tid : 0) * nblk;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int idx = tid + j * 256;
-        cv[j] = a.blkcnt[idx < ncnt ? idx : 0];
+        for (int b = 0; b < PRE; ++b) cv[b] = b < nblk ? cp[b] : 0;
     }
     u32x4 v[W][VMAX];
     int pk[W];
@@ -531,20 +529,21 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     }
 
     // 2. this tile's first row of every expert
-    if (staged) {
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int idx = tid + j * 256;
-            if (idx < ncnt) cnt[idx] = cv[j];
-        }
-    }
-    lds_barrier();
     for (int e = tid; e < E; e += 256) {
         int C = 0, before = 0;
-        for (int b = 0; b < nblk; ++b) {
-            const int c = staged ? cnt[b * E + e] : a.blkcnt[b * E + e];
-            C += c;
-            before += b < tile ? c : 0;
+        if (e == tid && pre_all) {
+#pragma unroll
+            for (int b = 0; b < PRE; ++b) {
+                C += cv[b];
+                before += b < tile ? cv[b] : 0;
+            }
+        } else {
+            const gptr<const int32_t> cp = (gptr<const int32_t>)a.blkcnt + int64_t(e) * nblk;
+            for (int b = 0; b < nblk; ++b) {
+                const int c = cp[b];
+                C += c;
+                before += b < tile ? c : 0;
+            }
         }
         A[e] = align_up_i(C, a.alpha);
         Cs[e] = C;
@@ -800,8 +799,7 @@ template <int VMAX>
 int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
-    const size_t ncnt = size_t(a.nblk) * E;
-    const size_t lds = size_t(E) * 12 + (ncnt <= 1024 ? ncnt * 4 : 0);
+    const size_t lds = size_t(E) * 12;
     hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), lds, st, a);
     return launched_ok();
 }

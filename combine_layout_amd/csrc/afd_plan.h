@@ -37,7 +37,7 @@ struct WorkspacePlan {
     size_t err = 0;        // uint64 sticky route-error word
     size_t counter = 0;    // uint32 arrival counter of the layout kernel
     size_t ends = 0;       // int32 [E]
-    size_t blkcnt = 0;     // int32 [nblk_max][E] live choices per layout tile
+    size_t blkcnt = 0;     // int32 [E][nblk] live choices per layout tile (expert-major)
     size_t blkbase = 0;    // int32 [nblk_max][E] first row of each tile's run
     size_t packed = 0;     // int32 [N*capacity*K] (expert << 16 | rank in tile), -1 skipped
     size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}
