@@ -99,27 +99,28 @@ class RoundSet:
             self.buf.source_collect(s, view=view)
         torch.cuda.synchronize()
 
-    def round(self, mark=None):
-        """Enqueue one full round on the current stream.  `mark(kind)` is
-        called right before and after the calls that launch kernels."""
+    def dispatch_phase(self):
+        """Every source dispatch and worker receive of a round (the receive
+        launches the dispatch kernels); returns the receipts."""
         c = self.cfg
         b = self.buf
         for s, (x, ids, w, scl) in enumerate(self.dev):
             b.source_dispatch(s, x, ids, w, scl, bucket=c.bucket, out=self.outs[s])
-        if mark:
-            mark("dispatch", 0)
-        recs = [b.worker_receive(f, bucket=c.bucket) for f in range(c.F)]
-        if mark:
-            mark("dispatch", 1)
-        for f in range(c.F - 1):
+        return [b.worker_receive(f, bucket=c.bucket) for f in range(c.F)]
+
+    def combine_phase(self, recs):
+        """Every worker reply (the last launches the combine) and source
+        collect of a round."""
+        c = self.cfg
+        b = self.buf
+        for f in range(c.F):
             b.worker_reply(f, self.replies[f], recs[f].receipt)
-        if mark:
-            mark("combine", 0)
-        b.worker_reply(c.F - 1, self.replies[c.F - 1], recs[c.F - 1].receipt)
-        if mark:
-            mark("combine", 1)
         for s in range(c.N):
             b.source_collect(s, view=self.view)
+
+    def round(self):
+        """Enqueue one full round on the current stream."""
+        self.combine_phase(self.dispatch_phase())
 
 
 def capture(sets, order):
@@ -163,33 +164,54 @@ def time_graph_rounds(sets, order, steps, warmup):
     return t0.elapsed_time(t1) * 1e3 / steps  # us per round
 
 
-def time_kernels_live(rs, rounds=64):
-    """Average duration of the dispatch and combine launches of a round,
-    from HIP events recorded around the calls that enqueue them, on the
-    stream they run on.  A sleep kernel first holds the stream so that the
-    host enqueues every round ahead of the GPU and the events bracket only
-    device work."""
+def capture_phase(sets, order, phase):
+    """One graph holding only the `phase` ("dispatch" or "combine") launches
+    of the rounds in `order`.  The other phase of each round is issued on a
+    side stream outside the capture, so every round still passes through
+    the library in order; inputs are unchanged between rounds, so the
+    captured launches read and write what the full rounds do."""
     import torch
-    st = torch.cuda.current_stream()
-    evs = []
-
-    def mark(kind, edge):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(st)
-        evs.append((kind, edge, e))
-
-    rs.round()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))
-    for _ in range(rounds):
-        rs.round(mark)
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        for i in order:
+            rs = sets[i]
+            if phase == "dispatch":
+                recs = rs.dispatch_phase()
+                with torch.cuda.stream(side):
+                    rs.combine_phase(recs)
+            else:
+                with torch.cuda.stream(side):
+                    recs = rs.dispatch_phase()
+                rs.combine_phase(recs)
     torch.cuda.synchronize()
-    acc = {"dispatch": [], "combine": []}
-    for i in range(0, len(evs), 2):
-        (k0, _, e0), (k1, _, e1) = evs[i], evs[i + 1]
-        assert k0 == k1
-        acc[k0].append(e0.elapsed_time(e1) * 1e3)
-    return {k: float(np.mean(v)) for k, v in acc.items()}
+    return g
+
+
+def time_kernels_live(sets, launches=48, reps=8):
+    """Average duration of one dispatch and one combine launch, from HIP
+    events around replays of graphs that hold `launches` launches of a
+    single phase back to back (cycling over the input sets, as the cold
+    rounds do), so the events bracket device work only and their own cost
+    is spread over many launches."""
+    import torch
+    order = [i % len(sets) for i in range(launches)]
+    out = {}
+    for phase in ("dispatch", "combine"):
+        g = capture_phase(sets, order, phase)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        out[phase] = t0.elapsed_time(t1) * 1e3 / (reps * launches)
+        del g
+    return out
 
 
 def launch_floor(G=32, steps=3200):
@@ -342,9 +364,14 @@ def main(argv=None):
     cold_us = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
     print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round", file=sys.stderr, flush=True)
 
-    kern = time_kernels_live(sets[-1])
-    dom = max(kern, key=kern.get)
-    dom_name = {"dispatch": "k_fused" if sum(cfg.T) <= 512 else "k_scatter", "combine": "k_combine"}[dom]
+    kern = time_kernels_live(sets)
+    # the roofline kernel: the phase with the most algorithmic bytes among
+    # those that are one kernel (the combine always; the dispatch when the
+    # one-kernel path runs it)
+    row_cols = cfg.H * (1 if cfg.dtype == "fp8" else 2) // 16
+    fused = sum(cfg.T) <= 512 and sum(cfg.T) * cfg.K <= 4096 and cfg.E <= 256 and row_cols <= 2048
+    dom = "dispatch" if fused and nb["dispatch"] >= nb["combine"] else "combine"
+    dom_name = {"dispatch": "k_fused", "combine": "k_combine"}[dom]
     dom_bytes = nb[dom]
     dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom_name, args.workload)
