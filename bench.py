@@ -290,15 +290,28 @@ def cpu_baseline(inst, budget_s=10.0):
 
 # ------------------------------------------------------------------ main ----
 
+def kernel_digest():
+    """First 16 hex digits of the SHA-256 of the kernel source's code: the
+    text of combine_layout_amd/csrc/afd_kernels.hip with // comments,
+    trailing blanks and empty lines removed, so comment edits keep it."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "combine_layout_amd", "csrc", "afd_kernels.hip")
+    lines = []
+    for line in open(src).read().splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def load_traffic(kernel, workload):
     """HBM bytes per dispatch of `kernel` on `workload` measured with the
     rocprofv3 counters FETCH_SIZE and WRITE_SIZE (scaled by a plain-copy
     calibration), from the summaries under profiles/ -- None when no summary
     covers it or the kernel source changed since the counters were taken."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "combine_layout_amd", "csrc", "afd_kernels.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    digest = kernel_digest()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
         text = open(path).read()
         if f"`{digest}`" not in text:

@@ -19,10 +19,12 @@
 //             scatters its own four tokens.  One launch for the dispatch.
 //   k_layout  dispatch, larger rounds, step 1: 256-token tiles; per 64-token
 //             chunk an LDS bit mask per expert gives each choice its rank
-//             (popcount of the lanes below it); the last tile to finish scans
-//             the tile counts into ends[] and per-tile row bases.
-//   k_scatter dispatch, step 2: one wavefront per token copies the row once
-//             from HBM into registers and stores it to each live slot.
+//             (popcount of the lanes below it); writes each tile's count per
+//             expert and every choice's rank inside its tile.
+//   k_scatter dispatch, step 2: every workgroup sums the tile counts into
+//             its tile's first row per expert (and ends[]), then one
+//             wavefront per token copies the row once from HBM into
+//             registers and stores it to each live slot.
 //   k_combine one wavefront per (token, column segment): gathers the live
 //             reply rows with 16-byte loads, float32 multiply-then-add in
 //             ascending k, rounds once to bfloat16.
