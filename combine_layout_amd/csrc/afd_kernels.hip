@@ -255,15 +255,12 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 {
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
-    __shared__ int s_row[kMaxTopk];
     __shared__ uint32_t s_live;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
-    __shared__ uint64_t s_dst[kMaxTopk];   // destination row of choice k, 0 if skipped
     const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
     int *hist = reinterpret_cast<int *>(lds);   // [E + 1] per expert (+ spare): all | before << 16
     int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
     int *sids = pfx + E;                        // [ntok * K]
-    float *sscale = reinterpret_cast<float *>(sids + size_t(ntok) * K);  // [G] (FP8)
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
@@ -305,7 +302,6 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
             for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
     }
     for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
-    if (myscale) sscale[tid] = scv;
     __syncthreads();
 
     // 2. route check and the two histograms (choices that are not live
@@ -341,44 +337,44 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] & 0xFFFF);
     if (!mine) return;
 
-    // 4. slot of choice k (thread k)
-    if (tid < K) {
-        int part = -1, row = -1;
-        if ((s_live >> tid) & 1u) {
-            const int e = sids[g * K + tid];
-            row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] >> 16);
-            part = e / a.E_loc;
-        }
-        const int packed = part < 0 ? -1 : ((part << 24) | row);
+    // 4. slot of choice k: lane k of every wavefront computes it (those of
+    // wavefront 0 also write the slot map and the row weight); the stores
+    // below take each wavefront's own addresses by lane broadcast
+    uint64_t d = 0, ds = 0;
+    int packed = -1;
+    if (lane < K && ((s_live >> lane) & 1u)) {
+        const int e = sids[g * K + lane];
+        const int row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] >> 16);
+        const int part = e / a.E_loc;
+        packed = (part << 24) | row;
+        d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
+        ds = s_ps[part] + uint64_t(row) * uint64_t(G) * 4u;
+        if (wave == 0) reinterpret_cast<float *>(s_pw[part])[row] = wk;
+    }
+    if (wave == 0 && lane < K) {
         int2 sl;
         sl.x = packed;
         sl.y = __float_as_int(wk);
-        reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + tid] = sl;
-        uint64_t d = 0;
-        if (part >= 0) {
-            d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
-            reinterpret_cast<float *>(s_pw[part])[row] = wk;
-        }
-        s_dst[tid] = d;
-        s_row[tid] = packed;
+        reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
     }
-    lds_barrier();
 
     // 5. stores: the row to every live slot, and the FP8 scales
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) break;
-        const uint64_t d = s_dst[k];
-        if (d == 0) continue;
-        const gptr<u32x4> dst = (gptr<u32x4>)d;
+    const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
+    const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
+    for (int k = 0; k < K; ++k) {
+        const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+        if (dk == 0) continue;
+        const gptr<u32x4> dst = (gptr<u32x4>)dk;
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
             if (c < a.nvec) __builtin_nontemporal_store(v[i], &dst[c]);
         }
         if (myscale) {
-            const int pr = s_row[k];
-            reinterpret_cast<float *>(s_ps[pr >> 24])[int64_t(pr & 0xFFFFFF) * G + tid] = sscale[tid];
+            const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+            ((gptr<float>)sk)[tid] = scv;
         }
     }
 }
@@ -835,7 +831,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
-        const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4 + size_t(p.G) * 4;
+        const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4;
         dim3 grid(p.ntok > 0 ? p.ntok : 1);
         switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);
