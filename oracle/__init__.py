@@ -31,7 +31,7 @@ def build(force: bool = True) -> str:
     os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
-                           "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp])
+                           "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp, "-lm"])
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -141,6 +141,73 @@ def combine(w_all: np.ndarray, lay: Layout, H: int, ys: List[np.ndarray]) -> np.
     return out
 
 
+# ---- per-stage combine (design page, sections 6 and 19) ----
+
+COMBINE_ONCE, COMBINE_PER_STAGE, COMBINE_PER_STAGE_FP8 = "once", "per_stage", "per_stage_fp8"
+
+
+def fp8_row_bytes(H: int) -> int:
+    """Bytes of one FP8 partial row: H codes, H/128 scale bytes, padding to 32."""
+    lib().orc_fp8_row_bytes.restype = ctypes.c_int64
+    return int(lib().orc_fp8_row_bytes(H))
+
+
+def combine_partials(w_all: np.ndarray, lay: Layout, H: int, F: int, ys: List[np.ndarray]):
+    """Stage one: BF16 partial [F, ntok, H] of every partition and token, and
+    has [F, ntok] (1 where the token has a live choice in that partition;
+    other rows stay 0)."""
+    ntok, K = lay.slot_part.shape
+    partial = np.zeros((F, ntok, H), np.uint16)
+    has = np.zeros((F, ntok), np.uint8)
+    if ntok:
+        ys = [np.ascontiguousarray(y, np.uint16) for y in ys]
+        lib().orc_combine_partials(ctypes.c_int64(ntok), K, H, F, _p(np.ascontiguousarray(w_all, np.float32)),
+                                   _p(lay.slot_part), _p(lay.slot_row), _ptr_array(ys), _p(partial), _p(has))
+    return partial, has
+
+
+def quantize_fp8_rows(partial_rows: np.ndarray) -> np.ndarray:
+    """FP8 form (codes, scale bytes, zero padding) of BF16 rows [n, H]."""
+    partial_rows = np.ascontiguousarray(partial_rows, np.uint16)
+    n, H = partial_rows.shape
+    out = np.zeros((n, fp8_row_bytes(H)), np.uint8)
+    for i in range(n):
+        lib().orc_quantize_fp8_row(H, _p(partial_rows[i]), _p(out[i]))
+    return out
+
+
+def quantize_partials(partial: np.ndarray, has: np.ndarray) -> np.ndarray:
+    """FP8 rows [F, ntok, row bytes] of the partials that exist (others 0)."""
+    F, ntok, H = partial.shape
+    q = np.zeros((F, ntok, fp8_row_bytes(H)), np.uint8)
+    for f in range(F):
+        idx = np.nonzero(has[f])[0]
+        if len(idx):
+            q[f, idx] = quantize_fp8_rows(partial[f, idx])
+    return q
+
+
+def combine_stages(lay: Layout, H: int, partial: Optional[np.ndarray], qrows: Optional[np.ndarray]) -> np.ndarray:
+    """Stage two: the BF16 result [ntok, H] from the BF16 partials
+    (qrows None) or from their FP8 rows."""
+    ntok, K = lay.slot_part.shape
+    out = np.zeros((ntok, H), np.uint16)
+    if ntok:
+        fp8 = qrows is not None
+        pa = np.ascontiguousarray(partial if partial is not None else np.zeros(1), np.uint16)
+        qa = np.ascontiguousarray(qrows if fp8 else np.zeros(1), np.uint8)
+        lib().orc_combine_stages(ctypes.c_int64(ntok), K, H, 1 if fp8 else 0, _p(lay.slot_part), _p(pa), _p(qa),
+                                 _p(out))
+    return out
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.zeros(v.shape, np.uint8)
+    lib().orc_e4m3_encode(_p(v), _p(out), ctypes.c_int64(v.size))
+    return out
+
+
 def bf16_round(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, np.float32)
     out = np.zeros(v.shape, np.uint16)
@@ -156,7 +223,7 @@ def e4m3_decode(q: np.ndarray) -> np.ndarray:
 
 
 class RoundResult:
-    def __init__(self, lay, rows, roww, scales, ys, out, rows_cap):
+    def __init__(self, lay, rows, roww, scales, ys, out, rows_cap, partial=None, has=None, qrows=None):
         self.layout = lay
         self.rows = rows
         self.row_weights = roww
@@ -164,11 +231,16 @@ class RoundResult:
         self.replies = ys
         self.out = out          # uint16 [ntok, H]
         self.rows_cap = rows_cap
+        self.partial = partial  # per-stage combine: uint16 [F, ntok, H]
+        self.has = has          # uint8 [F, ntok]
+        self.qrows = qrows      # FP8 partial rows: uint8 [F, ntok, row bytes]
 
 
-def run_round(inst, rows_cap: Optional[Sequence[int]] = None) -> RoundResult:
+def run_round(inst, rows_cap: Optional[Sequence[int]] = None, combine_mode: str = COMBINE_ONCE) -> RoundResult:
     """The whole round for a generated instance (synthetic.gen.Instance):
-    layout -> dispatch (+scales) -> identity experts -> combine."""
+    layout -> dispatch (+scales) -> identity experts -> combine, the combine
+    rounding once (COMBINE_ONCE) or once per stage with BF16 or FP8
+    partials."""
     cfg = inst.cfg
     fp8 = cfg.dtype == "fp8"
     T = [len(s.ids) for s in inst.sources]
@@ -190,5 +262,9 @@ def run_round(inst, rows_cap: Optional[Sequence[int]] = None) -> RoundResult:
         y = np.zeros((rows_cap[f], H), np.uint16)
         identity_experts(fp8, E, F, f, cfg.alpha, H, lay.ends, rows[f], scales[f] if fp8 else None, y)
         ys.append(y)
-    out = combine(w, lay, H, ys)
-    return RoundResult(lay, rows, roww, scales, ys, out, rows_cap)
+    if combine_mode == COMBINE_ONCE:
+        return RoundResult(lay, rows, roww, scales, ys, combine(w, lay, H, ys), rows_cap)
+    partial, has = combine_partials(w, lay, H, F, ys)
+    qrows = quantize_partials(partial, has) if combine_mode == COMBINE_PER_STAGE_FP8 else None
+    out = combine_stages(lay, H, None if qrows is not None else partial, qrows)
+    return RoundResult(lay, rows, roww, scales, ys, out, rows_cap, partial, has, qrows)

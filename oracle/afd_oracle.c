@@ -14,15 +14,19 @@
  * Pins (tests/): layout against an independent brute-force sort and
  * invariants; combine against the float64 closed form with identity experts,
  * a scipy.sparse routing-matrix product and exact special cases; number
- * formats against torch's casts.  The pages' own per-stage rounding of the
- * multi-GPU combine is not modelled here ("parity unpinned" for that
- * variant; this oracle rounds once).
+ * formats against torch's casts.  The per-stage combine (one BF16 partial
+ * per FFN partition, optionally carried as E4M3 with power-of-two scales,
+ * then a float32 sum of the partials) is pinned by composition with the
+ * pinned single-rounding combine, an E4M3 encoder checked against torch's
+ * cast, scale exponents against their closed form, and hand-derived values
+ * that fix the order in which partials are added.
  *
  * Notation: N sources (s), T[s] tokens each, K choices per token, E experts,
  * F partitions owning E_loc = E/F consecutive experts each, alignment alpha,
  * hidden size H.  Tokens are numbered globally g = sum_{s'<s} T[s'] + t, so
  * increasing g is the (source, token) order.
  */
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
@@ -357,4 +361,175 @@ void orc_e4m3_decode(const uint8_t *in, float *out, int64_t n)
 {
     int64_t i;
     for (i = 0; i < n; ++i) out[i] = e4m3_to_f32(in[i]);
+}
+
+/* ---- per-stage combine (design page: two-domain rounding in section 6, ---
+ * ---- FP8 combine replies in section 19) --------------------------------- */
+
+/*
+ * float8_e4m3fn encoding: the representable value nearest to v, ties to the
+ * even code (even mantissa).  Magnitudes at or above 448, the largest finite
+ * value, give 448 (only an infinite input reaches that here: the scaling
+ * below keeps every finite input within 448).  NaN keeps its sign and gives
+ * the NaN code.  Found by a binary search over the 127 non-negative codes,
+ * whose values increase with the code.
+ */
+static uint8_t f32_to_e4m3_rne(float v)
+{
+    uint32_t u;
+    uint8_t sign;
+    double a, lo_v, hi_v;
+    int lo = 0, hi = 126, c;
+    memcpy(&u, &v, 4);
+    sign = (u >> 31) ? 0x80 : 0x00;
+    if (v != v) return (uint8_t)(sign | 0x7F);
+    a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    while (lo < hi) {                       /* largest code with value <= a */
+        int mid = (lo + hi + 1) / 2;
+        if ((double)e4m3_to_f32((uint8_t)mid) <= a) lo = mid;
+        else hi = mid - 1;
+    }
+    c = lo;
+    lo_v = (double)e4m3_to_f32((uint8_t)c);
+    if (lo_v != a) {
+        hi_v = (double)e4m3_to_f32((uint8_t)(c + 1));
+        if (hi_v - a < a - lo_v || (hi_v - a == a - lo_v && ((c + 1) & 1) == 0)) c = c + 1;
+    }
+    return (uint8_t)(sign | c);
+}
+
+/*
+ * Exponent e of a 128-element group's power-of-two scale (section 19): the
+ * smallest integer with amax <= 448 * 2^e, but at least -117, so that every
+ * nonzero dequantised value stays a normal float32; an infinite amax takes
+ * the top scale 2^120, the largest exponent any finite BF16 amax needs.
+ */
+static int fp8_group_exponent(float amax)
+{
+    int e = -117;
+    if (isinf(amax)) return 120;
+    while ((double)amax > 448.0 * ldexp(1.0, e)) e += 1;
+    return e;
+}
+
+/* Bytes of one FP8 partial row (section 19's row format): H codes, then one
+ * scale byte 127 + e per group, padded to a multiple of 32. */
+int64_t orc_fp8_row_bytes(int H)
+{
+    return (int64_t)H + (H / 128 + 31) / 32 * 32;
+}
+
+/*
+ * orc_combine_partials: stage one, on the FFN side.  Partition f reduces
+ * each token's live rows that it holds (design page, section 6: the
+ * hybrid combine rounds each FFN partial to BF16 before the cross-domain
+ * sum):
+ *     partial[f][g][h] = bf16( sum over live k of g with slot_part == f,
+ *                              ascending, of w[g][k] * y_f[row][h] )
+ * in float32 from +0, each product rounded and then added.  has[f*ntok+g]
+ * is 1 when token g has a live choice in f (only then is the row written).
+ */
+void orc_combine_partials(int64_t ntok, int K, int H, int F, const float *w, const int32_t *slot_part,
+                          const int32_t *slot_row, const uint16_t *const *y, uint16_t *partial, uint8_t *has)
+{
+    int64_t g;
+    int k, h, f;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (f = 0; f < F; ++f) {
+        for (g = 0; g < ntok; ++g) {
+            int any = 0;
+            for (h = 0; h < H; ++h) acc[h] = 0.0f;
+            for (k = 0; k < K; ++k) {
+                int32_t row = slot_row[g * K + k];
+                float wt = w[g * K + k];
+                if (slot_part[g * K + k] != f) continue;
+                any = 1;
+                for (h = 0; h < H; ++h) {
+                    float prod = wt * bf16_to_f32(y[f][(int64_t)row * H + h]);
+                    acc[h] = acc[h] + prod;
+                }
+            }
+            has[(int64_t)f * ntok + g] = (uint8_t)any;
+            if (!any) continue;
+            for (h = 0; h < H; ++h) partial[((int64_t)f * ntok + g) * H + h] = f32_to_bf16_rne(acc[h]);
+        }
+    }
+    free(acc);
+}
+
+/*
+ * orc_quantize_fp8_row: the FP8 form of one BF16 partial row (section 19).
+ * Per group of 128 elements: amax over the magnitudes of its non-NaN
+ * elements (0 if none), e = fp8_group_exponent(amax), code of element i =
+ * e4m3(v_i * 2^-e) (the scaling is exact), scale byte 127 + e stored after
+ * the H codes; the row's padding bytes are zero.
+ */
+void orc_quantize_fp8_row(int H, const uint16_t *partial, uint8_t *dst)
+{
+    int G = H / 128, b, i;
+    int64_t n = orc_fp8_row_bytes(H);
+    for (i = H + G; i < n; ++i) dst[i] = 0;
+    for (b = 0; b < G; ++b) {
+        float amax = 0.0f;
+        int e;
+        for (i = 0; i < 128; ++i) {
+            float v = fabsf(bf16_to_f32(partial[b * 128 + i]));
+            if (v == v && v > amax) amax = v;
+        }
+        e = fp8_group_exponent(amax);
+        for (i = 0; i < 128; ++i)
+            dst[b * 128 + i] = f32_to_e4m3_rne(ldexpf(bf16_to_f32(partial[b * 128 + i]), -e));
+        dst[H + b] = (uint8_t)(127 + e);
+    }
+}
+
+/*
+ * orc_combine_stages: stage two, on the source side (section 19: the
+ * source dequantises each FFN row and sums the rows in float32 in slot
+ * order, the ascending order of the last top-k lane that maps to each
+ * partition, then rounds once to BF16).  For token g the partitions holding
+ * a live choice are visited in ascending order of their last live k;
+ *     out[g][h] = bf16( +0 + value_f0[h] + value_f1[h] + ... )
+ * where value is the BF16 partial (fp8 = 0) or, from the FP8 row,
+ * e4m3(code) * 2^(scale byte - 127) (fp8 = 1).  Tokens without a live
+ * choice give +0.  partial is [F][ntok][H] BF16; qrows is [F][ntok][row]
+ * bytes with row = orc_fp8_row_bytes(H).
+ */
+void orc_combine_stages(int64_t ntok, int K, int H, int fp8, const int32_t *slot_part,
+                        const uint16_t *partial, const uint8_t *qrows, uint16_t *out)
+{
+    int64_t g, rb = orc_fp8_row_bytes(H);
+    int k, kk, h;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (g = 0; g < ntok; ++g) {
+        for (h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (k = 0; k < K; ++k) {
+            int32_t f = slot_part[g * K + k];
+            int last = 1;
+            if (f < 0) continue;
+            for (kk = k + 1; kk < K; ++kk)
+                if (slot_part[g * K + kk] == f) last = 0;
+            if (!last) continue;
+            for (h = 0; h < H; ++h) {
+                float v;
+                if (fp8) {
+                    const uint8_t *row = qrows + ((int64_t)f * ntok + g) * rb;
+                    v = ldexpf(e4m3_to_f32(row[h]), (int)row[H + h / 128] - 127);
+                } else {
+                    v = bf16_to_f32(partial[((int64_t)f * ntok + g) * H + h]);
+                }
+                acc[h] = acc[h] + v;
+            }
+        }
+        for (h = 0; h < H; ++h) out[g * H + h] = f32_to_bf16_rne(acc[h]);
+    }
+    free(acc);
+}
+
+/* Exposed for the encoder pin. */
+void orc_e4m3_encode(const float *in, uint8_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = f32_to_e4m3_rne(in[i]);
 }

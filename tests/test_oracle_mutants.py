@@ -15,6 +15,7 @@ import pytest
 import oracle
 from tests import test_oracle_combine as tc
 from tests import test_oracle_layout as tl
+from tests import test_oracle_staged as ts
 
 _SRC = os.path.join(os.path.dirname(oracle.__file__), "afd_oracle.c")
 
@@ -34,6 +35,20 @@ MUTANTS = {
     "expert_scale_off_by_one": ("return 1.0f + (float)e / (float)E;", "return 1.0f + (float)(e + 1) / (float)E;"),
     "bf16_round_half_up": ("u += 0x7FFFu + lsb;", "u += 0x8000u;"),
     "scales_ignore_stride": ("(int64_t)b * stride_g[s]]", "(int64_t)b]"),
+    # per-stage combine
+    "partial_rounding_drops_lsb": ("partial[((int64_t)f * ntok + g) * H + h] = f32_to_bf16_rne(acc[h]);",
+                                   "partial[((int64_t)f * ntok + g) * H + h] = (uint16_t)(f32_to_bf16_rne(acc[h]) & 0xFFFE);"),
+    "stages_first_lane_order": ("for (kk = k + 1; kk < K; ++kk)", "for (kk = 0; kk < k; ++kk)"),
+    "stages_skip_rounding_stage": ("v = bf16_to_f32(partial[((int64_t)f * ntok + g) * H + h]);",
+                                   "v = bf16_to_f32(partial[((int64_t)f * ntok + g) * H + h]) * 1.00390625f;"),
+    "fp8_clamp_off_by_one": ("int e = -117;", "int e = -116;"),
+    "fp8_exponent_off_by_one": ("while ((double)amax > 448.0 * ldexp(1.0, e)) e += 1;",
+                                "while ((double)amax > 224.0 * ldexp(1.0, e)) e += 1;"),
+    "fp8_scale_not_applied": ("f32_to_e4m3_rne(ldexpf(bf16_to_f32(partial[b * 128 + i]), -e));",
+                              "f32_to_e4m3_rne(ldexpf(bf16_to_f32(partial[b * 128 + i]), -e - (i == 5)));"),
+    "fp8_dequant_bias": ("(int)row[H + h / 128] - 127);", "(int)row[H + h / 128] - 126);"),
+    "fp8_ties_up": ("((c + 1) & 1) == 0)) c = c + 1;", "1)) c = c + 1;"),
+    "fp8_nan_in_amax": ("if (v == v && v > amax) amax = v;", "if (v > amax || v != v) amax = v;"),
 }
 
 
@@ -50,6 +65,14 @@ def _pins():
             tc.test_combine_exact_special_cases, tc.test_padding_rows_never_read,
             tc.test_oracle_number_formats, tl.test_first_offender_codes,
             tl.test_single_source_single_partition_is_stable_argsort]
+    out += [ts.test_e4m3_encoder_matches_torch, ts.test_quantization_error_bound,
+            ts.test_stage_two_order_is_last_lane, ts.test_fp8_partials_exact_for_short_integers,
+            ts.test_single_partition_reduces_to_single_rounding,
+            lambda: ts.test_quantized_rows_match_torch_and_closed_form(256)]
+    for i in (0, 3, 4):
+        out.append(lambda i=i: ts.test_partials_equal_masked_single_rounding_combine(i))
+        out.append(lambda i=i: ts.test_stage_two_equals_single_rounding_combine_of_partials(i, False))
+        out.append(lambda i=i: ts.test_stage_two_equals_single_rounding_combine_of_partials(i, True))
     return out
 
 
@@ -62,7 +85,7 @@ def test_pins_catch_mutant(name):
         path = os.path.join(d, "mut.c")
         lib = os.path.join(d, "libmut.so")
         open(path, "w").write(src.replace(old, new))
-        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared", path, "-o", lib])
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared", path, "-o", lib, "-lm"])
         import ctypes
         saved = oracle._lib
         oracle._lib = ctypes.CDLL(lib)
