@@ -66,12 +66,27 @@ def byte_terms(cfg, L: int) -> dict:
     }
 
 
-def round_bytes(cfg, L: int) -> dict:
-    """Algorithmic HBM bytes of one round, split by kernel role."""
+def partial_rows(inst) -> int:
+    """Number of (token, partition) pairs with a live choice: the partial rows
+    a per-stage combine writes and reads."""
+    ids = np.concatenate([s.ids for s in inst.sources])
+    E_loc = inst.cfg.E // inst.cfg.F
+    part = np.where(ids >= 0, ids // E_loc, -1)
+    return int(sum((part == f).any(axis=1).sum() for f in range(inst.cfg.F)))
+
+
+def round_bytes(cfg, L: int, combine: str = "once", n_partial: int = 0) -> dict:
+    """Algorithmic HBM bytes of one round, split by kernel role.  The
+    per-stage combine also writes and reads one partial row per (token,
+    partition) with a live choice (BF16, or H codes + scale bytes padded to
+    32), and every partition's stage one reads the slot map."""
     t = byte_terms(cfg, L)
     dispatch = t["x_read"] + t["ids_weights_read"] + t["slot_map_write"] + t["rows_write"] + t["row_weights_write"]
-    combine = t["replies_read"] + t["slot_map_read"] + t["out_write"]
-    return {"dispatch": dispatch, "combine": combine, "total": dispatch + combine}
+    combine_b = t["replies_read"] + t["slot_map_read"] + t["out_write"]
+    if combine != "once":
+        prow = 2 * cfg.H if combine == "per_stage" else cfg.H + (cfg.H // 128 + 31) // 32 * 32
+        combine_b += 2 * n_partial * prow + cfg.F * t["slot_map_read"]
+    return {"dispatch": dispatch, "combine": combine_b, "total": dispatch + combine_b}
 
 
 # ----------------------------------------------------------- GPU harness ----
@@ -79,14 +94,14 @@ def round_bytes(cfg, L: int) -> dict:
 class RoundSet:
     """One independent set of inputs, outputs, arenas and replies."""
 
-    def __init__(self, inst, view):
+    def __init__(self, inst, view, combine="once"):
         import torch
         from tests import gpu_harness as h
         self.inst = inst
         self.cfg = inst.cfg
         self.view = view
         self.dev = h.upload(inst)
-        self.buf = h.make_buffer(inst)
+        self.buf = h.make_buffer(inst, combine=combine)
         self.outs = [torch.empty((T, self.cfg.H), dtype=torch.bfloat16, device="cuda") for T in self.cfg.T]
         # one eager round to obtain the receive layout, then the replies
         for s, (x, ids, w, scl) in enumerate(self.dev):
@@ -331,6 +346,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=3200)
     ap.add_argument("--warmup", type=int, default=320)
     ap.add_argument("--workload", default="2a2f_decode", choices=gen.WORKLOADS)
+    ap.add_argument("--combine", default="once", choices=["once", "per_stage", "per_stage_fp8"],
+                    help="combine rounding: once (default), or per stage with BF16 or FP8 partials")
     ap.add_argument("--graph-rounds", type=int, default=0, help="rounds per captured graph (default by size)")
     ap.add_argument("--cold-bytes", type=float, default=512e6, help="bytes the cold rotation spans")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
@@ -360,7 +377,10 @@ def main(argv=None):
     inst = gen.instance_by_name(args.workload)
     cfg = inst.cfg
     L = live_choices(inst)
-    nb = round_bytes(cfg, L)
+    if args.combine != "once" and cfg.F < 2:
+        print("the per-stage combine needs two or more partitions", file=sys.stderr)
+        return 2
+    nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else 0)
     view = cfg.F == 1
     print(f"[bench] {args.workload}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} "
           f"alpha={cfg.alpha} dtype={cfg.dtype} L={L} bytes/round={nb['total']}", file=sys.stderr, flush=True)
@@ -369,11 +389,11 @@ def main(argv=None):
     G = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
     G = max(G, S) if S > 1 else G
     G = int(math.ceil(G / S) * S)
-    sets = [RoundSet(inst, view)]
+    sets = [RoundSet(inst, view, args.combine)]
     hot_us = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
     print(f"[bench] hot: {hot_us:.3f} us/round", file=sys.stderr, flush=True)
     for _ in range(S - 1):
-        sets.append(RoundSet(inst, view))
+        sets.append(RoundSet(inst, view, args.combine))
     cold_us = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
     print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round", file=sys.stderr, flush=True)
 
@@ -385,6 +405,10 @@ def main(argv=None):
     fused = sum(cfg.T) <= 512 and sum(cfg.T) * cfg.K <= 4096 and cfg.E <= 256 and row_cols <= 2048
     dom = "dispatch" if fused and nb["dispatch"] >= nb["combine"] else "combine"
     dom_name = {"dispatch": "k_fused", "combine": "k_combine"}[dom]
+    if args.combine != "once":
+        # the per-stage combine is F stage-one and N stage-two launches: the
+        # phase as a whole
+        dom, dom_name = "combine", "k_partial+k_final"
     dom_bytes = nb[dom]
     dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
     traffic = load_traffic(dom_name, args.workload)
@@ -411,7 +435,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
                    "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
                    "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
-                   "rounds_per_graph": G},
+                   "rounds_per_graph": G, "combine": args.combine},
         "us_per_round": round(cold_us, 3),
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_round_hot": round(hot_us, 3),

@@ -17,6 +17,9 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "afd.h")
 
 AFD_OK, AFD_E_ARG, AFD_E_SHAPE, AFD_E_ORDER, AFD_E_CAPACITY, AFD_E_ROUTE, AFD_E_HIP = 0, -1, -2, -3, -4, -5, -6
 AFD_BF16, AFD_FP8_E4M3 = 0, 1
+AFD_COMBINE_ONCE, AFD_COMBINE_PER_STAGE, AFD_COMBINE_PER_STAGE_FP8 = 0, 1, 2
+COMBINE_MODES = {"once": AFD_COMBINE_ONCE, "per_stage": AFD_COMBINE_PER_STAGE,
+                 "per_stage_fp8": AFD_COMBINE_PER_STAGE_FP8}
 ROUTE_NONE, ROUTE_RANGE, ROUTE_NEG, ROUTE_DUP = 0, 1, 2, 3
 MAX_SOURCES, MAX_PARTITIONS, MAX_EXPERTS, MAX_TOPK = 16, 16, 512, 32
 
@@ -27,7 +30,8 @@ STATUS_NAMES = {0: "AFD_OK", -1: "AFD_E_ARG", -2: "AFD_E_SHAPE", -3: "AFD_E_ORDE
 class Config(ctypes.Structure):
     _fields_ = [("num_sources", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("topk", ctypes.c_int32), ("hidden", ctypes.c_int32),
-                ("expert_alignment", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("expert_alignment", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("combine", ctypes.c_int32)]
 
 
 class Receipt(ctypes.Structure):
@@ -60,6 +64,7 @@ SIGNATURES = {
     "afd_source_collect": ([_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64), _P], _I32),
     "afd_get_error": ([_P, _P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                        ctypes.POINTER(_I32)], _I32),
+    "afd_get_partials": ([_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64)], _I32),
     "afd_status_string": ([_I32], ctypes.c_char_p),
 }
 

@@ -41,17 +41,22 @@ class Buffer:
     """One context over caller-owned (torch) device memory.
 
     num_sources N, num_partitions F, num_experts E, topk K, hidden H,
-    expert_alignment alpha, capacity (largest bucket), dtype "bf16" | "fp8".
+    expert_alignment alpha, capacity (largest bucket), dtype "bf16" | "fp8",
+    combine "once" | "per_stage" | "per_stage_fp8" (how the combine rounds;
+    the per-stage modes need two or more partitions).
     Receive arenas are sized for ``arena_bucket`` (default: capacity)."""
 
     def __init__(self, num_sources, num_partitions, num_experts, topk, hidden, expert_alignment=1,
-                 capacity=2048, dtype="bf16", device=None, arena_bucket=None):
+                 capacity=2048, dtype="bf16", device=None, arena_bucket=None, combine="once"):
         self.lib = nat.load()
         self.device = torch.device(device if device is not None else "cuda", torch.cuda.current_device()) \
             if device is None or isinstance(device, str) and device == "cuda" else torch.device(device)
         self.fp8 = dtype == "fp8"
+        if combine not in nat.COMBINE_MODES:
+            raise ValueError(f"combine must be one of {sorted(nat.COMBINE_MODES)}")
+        self.combine = combine
         self.cfg = nat.Config(num_sources, num_partitions, num_experts, topk, hidden, expert_alignment, capacity,
-                              nat.AFD_FP8_E4M3 if self.fp8 else nat.AFD_BF16)
+                              nat.AFD_FP8_E4M3 if self.fp8 else nat.AFD_BF16, nat.COMBINE_MODES[combine])
         self.N, self.F, self.E, self.K, self.H = num_sources, num_partitions, num_experts, topk, hidden
         self.E_loc = num_experts // num_partitions
         self.alpha, self.capacity = expert_alignment, capacity
@@ -169,6 +174,17 @@ class Buffer:
         if out is not None and res.value == out.data_ptr():
             return out
         return self._ws_view(res.value, T * self.H * 2).view(torch.bfloat16).view(T, self.H)
+
+    def partials(self, s, f) -> torch.Tensor:
+        """Per-stage combine: source s's stage-one rows from partition f, a
+        uint8 view [T, row_bytes] of the workspace (BF16 partials, or E4M3
+        codes followed by the scale bytes).  Rows of tokens without a live
+        choice in f are unspecified."""
+        ptr = ctypes.c_void_p(0)
+        rb = ctypes.c_int64(0)
+        nat.check(self.lib.afd_get_partials(self.ctx, s, f, ctypes.byref(ptr), ctypes.byref(rb)), "get_partials")
+        T = self._T[s]
+        return self._ws_view(ptr.value, max(T, 1) * rb.value).view(-1, rb.value)[:T]
 
     # -- errors / teardown ---------------------------------------------------
     def get_error(self, clear=False):

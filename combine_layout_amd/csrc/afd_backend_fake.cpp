@@ -77,6 +77,19 @@ int be_launch_combine(const RoundPlan &p, void *)
     return g_fail;
 }
 
+int be_launch_partial(const RoundPlan &p, int f, void *)
+{
+    logf("partial f=%d ntok=%d prow=%lld base=%p", f, p.ntok, static_cast<long long>(p.prow),
+         static_cast<void *>(p.partials));
+    return g_fail;
+}
+
+int be_launch_final(const RoundPlan &p, int s, void *)
+{
+    logf("final s=%d T=%d out=%p", s, p.tok_off[s + 1] - p.tok_off[s], p.out[s]);
+    return g_fail;
+}
+
 int be_launch_copy(const void *src, void *dst, int64_t bytes, void *)
 {
     logf("copy %p->%p bytes=%lld", src, dst, static_cast<long long>(bytes));

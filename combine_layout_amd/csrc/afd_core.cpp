@@ -75,6 +75,10 @@ afd_status check_config(const afd_config *c)
     if (c->expert_alignment < 1) return AFD_E_SHAPE;
     if (c->capacity < 1) return AFD_E_SHAPE;
     if (c->dtype != AFD_BF16 && c->dtype != AFD_FP8_E4M3) return AFD_E_SHAPE;
+    if (c->combine != AFD_COMBINE_ONCE && c->combine != AFD_COMBINE_PER_STAGE &&
+        c->combine != AFD_COMBINE_PER_STAGE_FP8)
+        return AFD_E_SHAPE;
+    if (c->combine != AFD_COMBINE_ONCE && c->num_partitions < 2) return AFD_E_SHAPE;
     // index ranges used by the kernels: tokens * K in int32, rows below 2^24
     const int64_t ntok = int64_t(c->num_sources) * c->capacity;
     if (ntok * c->topk >= (int64_t(1) << 31)) return AFD_E_SHAPE;
@@ -113,6 +117,9 @@ WorkspacePlan plan_workspace(const afd_config &c)
     off += a(ntok * c.topk * 8);
     w.inbox = off;
     if (c.num_partitions == 1) off += a(ntok * c.hidden * 2);
+    w.partials = off;
+    if (c.combine != AFD_COMBINE_ONCE)
+        off += a(size_t(c.num_partitions) * ntok * size_t(partial_row_bytes(c.combine, c.hidden)));
     w.total = off;
     return w;
 }
@@ -151,6 +158,8 @@ void build_plan(afd_ctx *c)
     p.alpha = g.expert_alignment;
     p.fp8 = g.dtype == AFD_FP8_E4M3;
     p.capacity = g.capacity;
+    p.combine = g.combine;
+    p.prow = partial_row_bytes(g.combine, g.hidden);
     p.row_bytes = c->row_bytes;
     p.G = g.hidden / 128;
     p.tok_off[0] = 0;
@@ -174,6 +183,7 @@ void build_plan(afd_ctx *c)
     p.blkbase = reinterpret_cast<int32_t *>(c->ws + c->wp.blkbase);
     p.packed = reinterpret_cast<int32_t *>(c->ws + c->wp.packed);
     p.slot = reinterpret_cast<int32_t *>(c->ws + c->wp.slot);
+    p.partials = g.combine != AFD_COMBINE_ONCE ? reinterpret_cast<uint8_t *>(c->ws + c->wp.partials) : nullptr;
 }
 
 }  // namespace
@@ -376,17 +386,20 @@ afd_status afd_worker_reply(afd_ctx *c, int32_t f, const void *reply, int64_t re
     if (receive_rows != c->recv_rows[f]) return AFD_E_SHAPE;
     if (receive_rows > 0 && (!reply || !aligned(reply, 16))) return AFD_E_ARG;
     c->plan.reply[f] = reply;
-    c->replied[f] = true;
-    c->nreplied += 1;
-    if (c->nreplied == c->cfg.num_partitions) {
-        if (c->plan.ntok > 0 && be_launch_combine(c->plan, stream) != 0) {
-            c->replied[f] = false;
-            c->nreplied -= 1;
+    const bool staged = c->cfg.combine != AFD_COMBINE_ONCE;
+    const bool last = c->nreplied + 1 == c->cfg.num_partitions;
+    // per-stage: every reply runs its partition's stage one; once: the last
+    // reply runs the whole combine
+    if (c->plan.ntok > 0 && (staged || last)) {
+        const int rc = staged ? be_launch_partial(c->plan, f, stream) : be_launch_combine(c->plan, stream);
+        if (rc != 0) {
             c->plan.reply[f] = nullptr;
             return AFD_E_HIP;
         }
-        c->phase = kCollecting;
     }
+    c->replied[f] = true;
+    c->nreplied += 1;
+    if (last) c->phase = kCollecting;
     return AFD_OK;
 }
 
@@ -401,6 +414,8 @@ afd_status afd_source_collect(afd_ctx *c, int32_t s, int32_t view, const void **
     if (c->collected[s]) return AFD_E_ORDER;
     const void *res;
     if (g.num_partitions > 1) {
+        if (g.combine != AFD_COMBINE_ONCE && c->T[s] > 0 && be_launch_final(c->plan, s, stream) != 0)
+            return AFD_E_HIP;
         res = c->out_user[s];
     } else if (view) {
         res = inbox_of(c, s);
@@ -416,6 +431,18 @@ afd_status afd_source_collect(afd_ctx *c, int32_t s, int32_t view, const void **
     c->collected[s] = true;
     c->ncollected += 1;
     if (c->ncollected == g.num_sources) c->phase = kIdle;
+    return AFD_OK;
+}
+
+afd_status afd_get_partials(afd_ctx *c, int32_t s, int32_t f, const void **rows, int64_t *row_bytes)
+{
+    if (!c || !rows) return AFD_E_ARG;
+    const afd_config &g = c->cfg;
+    if (g.combine == AFD_COMBINE_ONCE) return AFD_E_ARG;
+    if (s < 0 || s >= g.num_sources || f < 0 || f >= g.num_partitions) return AFD_E_ARG;
+    const int64_t prow = partial_row_bytes(g.combine, g.hidden);
+    *rows = c->ws + c->wp.partials + size_t((int64_t(f) * g.num_sources + s) * g.capacity * prow);
+    if (row_bytes) *row_bytes = prow;
     return AFD_OK;
 }
 

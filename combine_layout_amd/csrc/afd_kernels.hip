@@ -29,6 +29,15 @@
 //             reply rows with 16-byte loads, float32 multiply-then-add in
 //             ascending k, rounds once to bfloat16.
 //   k_copy    inbox -> caller output (single-partition collect without view).
+//   k_partial per-stage combine, stage one (at partition f's reply): one
+//             wavefront per (token, column segment) sums the token's live rows
+//             of partition f like k_combine, rounds to a BF16 partial and
+//             stores it, or its FP8 form (codes plus one power-of-two scale
+//             byte per 128 elements, found with a 16-lane max), into the
+//             source's partial rows in the workspace.
+//   k_final   per-stage combine, stage two (at source s's collect): adds the
+//             token's partials in float32, partitions in ascending order of
+//             their last live top-k lane, and rounds once to BF16.
 //
 // Nothing here uses MFMA: the round is data movement plus one multiply-add
 // per reply element, bound by HBM bandwidth.  Expanded rows are written and
@@ -79,6 +88,18 @@ struct DispatchArgs {
     int32_t *blkbase;
     int32_t *packed;
     int32_t *slot;
+};
+
+// Per-stage combine: partial row of (partition f, source s, token t) at
+// partials + ((f * N + s) * capacity + t) * prow.
+struct StageArgs {
+    const uint16_t *reply;   // stage one: partition f's replies
+    uint16_t *out;           // stage two: source s's output
+    uint8_t *partials;
+    const int32_t *slot;
+    int64_t prow;
+    int tok_off[kMaxSources + 1];
+    int N, ntok, K, H, nvec, nseg, capacity, f, s, T;
 };
 
 struct CombineArgs {
@@ -724,6 +745,234 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     }
 }
 
+// float8_e4m3fn code of x, nearest with ties to the even code; magnitudes
+// at or above 448 (only an infinite input after the exact power-of-two
+// scaling) saturate to 448, NaN keeps its sign.  Normal results round the
+// float32 mantissa to 3 bits with the carry running into the exponent;
+// below 2^-6 the step is 2^-9, so the code is x * 2^9 rounded to even.
+__device__ __forceinline__ uint32_t e4m3_code(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a > 0x7F800000u) code = 0x7Fu;
+    else if (a >= 0x43E00000u) code = 0x7Eu;                                   // >= 448
+    else if (a < 0x3C800000u) code = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));   // < 2^-6
+    else code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    return sign | code;
+}
+
+// Value of an E4M3 code (exact in float32).
+__device__ __forceinline__ float e4m3_value(uint32_t q)
+{
+    const uint32_t mag = q & 0x7Fu;
+    const uint32_t sign = (q & 0x80u) << 24;
+    if (mag == 0x7Fu) return __uint_as_float(0x7FC00000u);
+    const float v = mag < 8u ? float(mag) * 0.001953125f : __uint_as_float((((mag >> 3) + 120u) << 23) | ((mag & 7u) << 20));
+    return __uint_as_float(__float_as_uint(v) | sign);
+}
+
+// Scale exponent of a group from the float32 bits of its amax: the smallest
+// e with amax <= 448 * 2^e = 1.75 * 2^(e + 8), at least -117 (an infinite
+// amax gives 120).
+__device__ __forceinline__ int fp8_group_exponent(uint32_t amax_bits)
+{
+    if (amax_bits < 0x00800000u) return -117;                                   // zero or subnormal
+    const int ex = int(amax_bits >> 23) - 127;
+    const int e = (amax_bits & 0x7FFFFFu) <= 0x600000u ? ex - 8 : ex - 7;
+    return e < -117 ? -117 : e;
+}
+
+// Stage one of the per-stage combine for partition a.f.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_partial(StageArgs a)
+{
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gw = blockIdx.x * 4 + wave_id();
+    const int g = gw / a.nseg;
+    const int seg = gw - g * a.nseg;
+    if (g >= a.ntok) return;
+    int2 sl;
+    sl.x = -1;
+    sl.y = 0;
+    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
+    const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
+    if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
+    const int s = source_of(a, g);
+    const int t = g - a.tok_off[s];
+    const int nvec = a.nvec;
+    const int c = seg * kWave + lane;
+    uint64_t raddr = 0;
+    if (mine) raddr = reinterpret_cast<uint64_t>(a.reply) + uint64_t(sl.x & 0xFFFFFF) * uint64_t(a.H) * 2u;
+    const int rlo = int(uint32_t(raddr)), rhi = int(uint32_t(raddr >> 32));
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int k0 = 0; k0 < a.K; k0 += 8) {
+        u32x4 y[8];
+        uint64_t rk[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            rk[kk] = uint64_t(uint32_t(__builtin_amdgcn_readlane(rlo, k0 + kk))) |
+                     (uint64_t(uint32_t(__builtin_amdgcn_readlane(rhi, k0 + kk))) << 32);
+            const gptr<const u32x4> src = (gptr<const u32x4>)rk[kk];
+            y[kk] = (rk[kk] != 0 && c < nvec) ? __builtin_nontemporal_load(&src[c]) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            if (rk[kk] == 0) continue;
+            const float w = __int_as_float(__builtin_amdgcn_readlane(sl.y, k0 + kk));
+            const uint32_t q[4] = {y[kk].x, y[kk].y, y[kk].z, y[kk].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float plo = w * __uint_as_float(q[j] << 16);
+                const float phi = w * __uint_as_float(q[j] & 0xFFFF0000u);
+                acc[2 * j] = acc[2 * j] + plo;
+                acc[2 * j + 1] = acc[2 * j + 1] + phi;
+            }
+        }
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = bf16_rne_bits(acc[j]);
+    uint8_t *row = a.partials + ((int64_t(a.f) * a.N + s) * a.capacity + t) * a.prow;
+    if (!FP8) {
+        if (c < nvec) {
+            u32x4 r;
+            r.x = b[0] | (b[1] << 16);
+            r.y = b[2] | (b[3] << 16);
+            r.z = b[4] | (b[5] << 16);
+            r.w = b[6] | (b[7] << 16);
+            reinterpret_cast<u32x4 *>(row)[c] = r;
+        }
+        return;
+    }
+    // FP8: a group of 128 elements is 16 lanes; amax over the magnitudes of
+    // its non-NaN elements (integer order equals float order for them)
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t m = (b[j] << 16) & 0x7FFFFFFFu;
+        am = (m <= 0x7F800000u && m > am) ? m : am;
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        const uint32_t o = uint32_t(__shfl_xor(int(am), d, kWave));
+        am = o > am ? o : am;
+    }
+    const int e = fp8_group_exponent(am);
+    const float inv = __uint_as_float(uint32_t(127 - e) << 23);              // 2^-e, a normal float
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        lo |= e4m3_code(__uint_as_float(b[j] << 16) * inv) << (8 * j);
+        hi |= e4m3_code(__uint_as_float(b[4 + j] << 16) * inv) << (8 * j);
+    }
+    const int G = a.H / 128;
+    if (c < nvec) {
+        uint2 v2;
+        v2.x = lo;
+        v2.y = hi;
+        reinterpret_cast<uint2 *>(row)[c] = v2;
+        if ((lane & 15) == 0) row[a.H + c / 16] = uint8_t(127 + e);
+    }
+    const int pad = int(a.prow) - a.H - G;
+    if (seg == 0 && lane < pad) row[a.H + G + lane] = 0;
+}
+
+// Stage two of the per-stage combine for source a.s: one wavefront per
+// (token, column segment).
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_final(StageArgs a)
+{
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gw = blockIdx.x * 4 + wave_id();
+    const int t = gw / a.nseg;
+    const int seg = gw - t * a.nseg;
+    if (t >= a.T) return;
+    const int g = a.tok_off[a.s] + t;
+    int part = -1;
+    if (lane < a.K) {
+        const int sx = a.slot[(int64_t(g) * a.K + lane) * 2];
+        part = sx >= 0 ? (sx >> 24) : -1;
+    }
+    // lane k adds its partition's partial when no later live lane maps there
+    bool last = part >= 0;
+    for (int j = 0; j < a.K; ++j) {
+        const int pj = __builtin_amdgcn_readlane(part, j);
+        last = last && !(j > lane && pj == part);
+    }
+    uint64_t lm = __ballot(last);
+    const int nvec = a.nvec;
+    const int c = seg * kWave + lane;
+    const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
+    const uint8_t *base = a.partials + (int64_t(a.s) * a.capacity + t) * a.prow;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    while (lm != 0) {
+        // up to four partials per batch, all loads issued before the adds
+        const uint8_t *rp[4];
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rp[i] = nullptr;
+            if (lm != 0) {
+                const int k = __builtin_ctzll(lm);
+                lm &= lm - 1;
+                rp[i] = base + int64_t(__builtin_amdgcn_readlane(part, k)) * fstride;
+                n = i + 1;
+            }
+        }
+        if (!FP8) {
+            u32x4 y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                y[i] = (i < n && c < nvec) ? reinterpret_cast<const u32x4 *>(rp[i])[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i >= n) break;
+                const uint32_t q[4] = {y[i].x, y[i].y, y[i].z, y[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] = acc[2 * j] + __uint_as_float(q[j] << 16);
+                    acc[2 * j + 1] = acc[2 * j + 1] + __uint_as_float(q[j] & 0xFFFF0000u);
+                }
+            }
+        } else {
+            uint2 y[4];
+            uint32_t sf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = i < n && c < nvec;
+                y[i] = ok ? reinterpret_cast<const uint2 *>(rp[i])[c] : uint2{0u, 0u};
+                sf[i] = ok ? rp[i][a.H + c / 16] : 127u;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i >= n) break;
+                const float scale = __uint_as_float(sf[i] << 23);                // 2^(byte - 127)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[j] = acc[j] + e4m3_value((y[i].x >> (8 * j)) & 0xFFu) * scale;
+                    acc[4 + j] = acc[4 + j] + e4m3_value((y[i].y >> (8 * j)) & 0xFFu) * scale;
+                }
+            }
+        }
+    }
+    if (c < nvec) {
+        u32x4 r;
+        r.x = bf16_rne_bits(acc[0]) | (bf16_rne_bits(acc[1]) << 16);
+        r.y = bf16_rne_bits(acc[2]) | (bf16_rne_bits(acc[3]) << 16);
+        r.z = bf16_rne_bits(acc[4]) | (bf16_rne_bits(acc[5]) << 16);
+        r.w = bf16_rne_bits(acc[6]) | (bf16_rne_bits(acc[7]) << 16);
+        reinterpret_cast<u32x4 *>(a.out + int64_t(t) * a.H)[c] = r;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_copy(const u32x4 *src, u32x4 *dst, int64_t n)
 {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
@@ -800,6 +1049,24 @@ int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
     const size_t lds = size_t(E) * 12;
     hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), lds, st, a);
     return launched_ok();
+}
+
+StageArgs make_stage_args(const RoundPlan &p)
+{
+    StageArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.partials = p.partials;
+    a.slot = p.slot;
+    a.prow = p.prow;
+    for (int s = 0; s <= p.N; ++s) a.tok_off[s] = p.tok_off[s];
+    a.N = p.N;
+    a.ntok = p.ntok;
+    a.K = p.K;
+    a.H = p.H;
+    a.nvec = p.H / 8;
+    a.nseg = (a.nvec + kWave - 1) / kWave;
+    a.capacity = p.capacity;
+    return a;
 }
 
 }  // namespace
@@ -880,6 +1147,34 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
     hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, st, a);
+    return launched_ok();
+}
+
+int be_launch_partial(const RoundPlan &p, int f, void *stream)
+{
+    StageArgs a = make_stage_args(p);
+    a.f = f;
+    a.reply = static_cast<const uint16_t *>(p.reply[f]);
+    const int64_t waves = int64_t(p.ntok) * a.nseg;
+    dim3 grid(unsigned((waves + 3) / 4));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_partial<true>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_partial<false>, grid, dim3(256), 0, st, a);
+    return launched_ok();
+}
+
+int be_launch_final(const RoundPlan &p, int s, void *stream)
+{
+    StageArgs a = make_stage_args(p);
+    a.s = s;
+    a.T = p.tok_off[s + 1] - p.tok_off[s];
+    a.out = static_cast<uint16_t *>(p.out[s]);
+    const int64_t waves = int64_t(a.T) * a.nseg;
+    if (waves == 0) return 0;
+    dim3 grid(unsigned((waves + 3) / 4));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_final<true>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_final<false>, grid, dim3(256), 0, st, a);
     return launched_ok();
 }
 

@@ -32,6 +32,13 @@ constexpr uint64_t kNoError = ~0ull;
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+// Bytes of one stage-one row of the per-stage combine: BF16 [H], or H E4M3
+// codes followed by H/128 scale bytes, padded to a multiple of 32.
+inline int64_t partial_row_bytes(int combine, int H)
+{
+    return combine == AFD_COMBINE_PER_STAGE_FP8 ? H + align_up(H / 128, 32) : int64_t(H) * 2;
+}
+
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
     size_t err = 0;        // uint64 sticky route-error word
@@ -42,6 +49,7 @@ struct WorkspacePlan {
     size_t packed = 0;     // int32 [N*capacity*K] (expert << 16 | rank in tile), -1 skipped
     size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
+    size_t partials = 0;   // per-stage combine: [F][N][capacity] rows of partial_row_bytes
     size_t total = 0;
     int nblk_max = 0;
 };
@@ -51,6 +59,8 @@ struct WorkspacePlan {
 struct RoundPlan {
     // configuration
     int N = 0, F = 0, E = 0, E_loc = 0, K = 0, H = 0, alpha = 1, fp8 = 0, capacity = 0;
+    int combine = AFD_COMBINE_ONCE;
+    int64_t prow = 0;        // per-stage combine: bytes of one partial row
     int64_t row_bytes = 0;   // H * bytes per activation
     int G = 0;               // H / 128 scale blocks per row
     // tokens, concatenated over sources in order
@@ -79,6 +89,8 @@ struct RoundPlan {
     int32_t *blkbase = nullptr;
     int32_t *packed = nullptr;
     int32_t *slot = nullptr;
+    // per-stage combine: row (f, s, t) at partials + ((f * N + s) * capacity + t) * prow
+    uint8_t *partials = nullptr;
 };
 
 // ---- backend: implemented by the HIP executor or the recording fake ----
@@ -88,6 +100,8 @@ int be_is_capturing(void *stream, int *capturing);
 int be_launch_dispatch(const RoundPlan &p, void *stream);
 int be_read_ends(const RoundPlan &p, void *stream, int32_t *host_ends, uint64_t *err_word);
 int be_launch_combine(const RoundPlan &p, void *stream);
+int be_launch_partial(const RoundPlan &p, int f, void *stream);   // per-stage combine, stage one
+int be_launch_final(const RoundPlan &p, int s, void *stream);     // per-stage combine, stage two
 int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream);
 int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word);
 int be_device_sync();

@@ -56,6 +56,34 @@ typedef enum {
 
 typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
 
+/*
+ * How the combine rounds (afdEP-comm design page; section 6 on rounding per
+ * reduction stage, section 19 on FP8 combine replies).
+ *   AFD_COMBINE_ONCE           one float32 sum over every live choice of a
+ *                              token in ascending k, rounded once to BF16;
+ *                              runs at the round's last worker_reply.
+ *   AFD_COMBINE_PER_STAGE      the shape of a combine spread over FFN GPUs:
+ *                              worker_reply(f) reduces partition f's live
+ *                              rows of every token into one BF16 partial
+ *                              (float32 sum in ascending k, one rounding);
+ *                              source_collect(s) sums source s's partials in
+ *                              float32, partitions ordered by the last live
+ *                              top-k lane that maps to them, and rounds once.
+ *   AFD_COMBINE_PER_STAGE_FP8  as AFD_COMBINE_PER_STAGE, but each partial
+ *                              is carried as E4M3 codes with one
+ *                              power-of-two scale per 128 elements: e is the
+ *                              smallest integer with amax <= 448 * 2^e, at
+ *                              least -117 (an infinite amax gives 120);
+ *                              code = e4m3(v * 2^-e) to nearest even (an
+ *                              infinite value saturates to 448); the row is
+ *                              H codes, then H/128 bytes 127 + e, zero padded
+ *                              to H + align32(H/128) bytes.  Lossy: at most
+ *                              2^-4 of the group's amax per element.
+ * The per-stage modes need num_partitions >= 2 (with one partition the
+ * single partial is the final result).
+ */
+typedef enum { AFD_COMBINE_ONCE = 0, AFD_COMBINE_PER_STAGE = 1, AFD_COMBINE_PER_STAGE_FP8 = 2 } afd_combine_mode;
+
 /* Route error codes (contract page: ids unique per token, in [0, E), or -1). */
 typedef enum { AFD_ROUTE_NONE = 0, AFD_ROUTE_RANGE = 1, AFD_ROUTE_NEG = 2, AFD_ROUTE_DUP = 3 } afd_route_code;
 
@@ -71,6 +99,7 @@ typedef enum { AFD_ROUTE_NONE = 0, AFD_ROUTE_RANGE = 1, AFD_ROUTE_NEG = 2, AFD_R
  *   capacity         the largest bucket (tokens per source) ever used
  *   dtype            activation format: BF16, or float8_e4m3fn with FP32
  *                    block-128 scales [T, H/128]
+ *   combine          afd_combine_mode (fixed for the context's lifetime)
  */
 typedef struct {
     int32_t num_sources;
@@ -80,7 +109,8 @@ typedef struct {
     int32_t hidden;
     int32_t expert_alignment;
     int32_t capacity;
-    int32_t dtype; /* afd_dtype */
+    int32_t dtype;   /* afd_dtype */
+    int32_t combine; /* afd_combine_mode */
 } afd_config;
 
 /* Opaque receipt (contract page: keep it unchanged through the matching
@@ -189,8 +219,10 @@ afd_status afd_worker_receive(afd_ctx *ctx, int32_t f, int32_t bucket, int32_t r
  * is device [receive_rows, H] BF16 covering the entire receive shape, with
  * each live row's expert output in place; replies are unweighted (the
  * combine applies each routing weight exactly once).  Padding rows are never
- * read.  The round's last reply enqueues the combine for every source on
- * `stream`; every reply must be complete in `stream` order by then.
+ * read.  AFD_COMBINE_ONCE: the round's last reply enqueues the combine for
+ * every source on `stream`; every reply must be complete in `stream` order
+ * by then.  Per-stage modes: each reply enqueues partition f's stage one
+ * (its partials, from its own reply only) on `stream`.
  * Errors: AFD_E_ORDER (not received, already replied, or a receipt of
  * another round or partition), AFD_E_ARG.
  */
@@ -201,12 +233,15 @@ afd_status afd_worker_reply(afd_ctx *ctx, int32_t f, const void *reply_bf16, int
  * afd_source_collect (contract page: source_collect(view)).  Needs every
  * partition replied.  *result is device BF16 [T, H] in token order with row
  * stride *row_stride elements.
- *   F > 1: the source's out_bf16 (nothing is enqueued).
+ *   F > 1, AFD_COMBINE_ONCE: the source's out_bf16 (nothing is enqueued).
+ *   F > 1, per-stage modes: stage two for source s is enqueued on `stream`
+ *          into out_bf16 (every partition's stage one must be complete in
+ *          `stream` order); *result is out_bf16.
  *   F = 1, view = 1: a read-only view of the source's combine inbox in the
  *          workspace, valid until the next afd_source_dispatch (design page
  *          section 13); nothing is enqueued.
  *   F = 1, view = 0: the inbox is copied into out_bf16 on `stream`.
- * Errors: AFD_E_ORDER, AFD_E_ARG (view = 0 without out_bf16).
+ * Errors: AFD_E_ORDER, AFD_E_ARG (view = 0 without out_bf16), AFD_E_HIP.
  */
 afd_status afd_source_collect(afd_ctx *ctx, int32_t s, int32_t view, const void **result,
                               int64_t *row_stride, void *stream);
@@ -222,6 +257,18 @@ afd_status afd_source_collect(afd_ctx *ctx, int32_t s, int32_t view, const void 
  */
 afd_status afd_get_error(afd_ctx *ctx, void *stream, int32_t clear, int32_t *code, int32_t *s, int32_t *t,
                          int32_t *k);
+
+/*
+ * afd_get_partials: where the per-stage combine keeps source s's stage-one
+ * rows from partition f (the source's combine inbox region for that FFN on
+ * the design page).  *rows is device memory inside the workspace, T rows of
+ * *row_bytes bytes: BF16 [H] for AFD_COMBINE_PER_STAGE, the FP8 row format
+ * above for AFD_COMBINE_PER_STAGE_FP8.  A token's row is written only when
+ * it has a live choice in f; other rows are unspecified.  Read-only; valid
+ * from partition f's reply until its reply in the next round.  Enqueues
+ * nothing.  Errors: AFD_E_ARG (index, NULL, or AFD_COMBINE_ONCE).
+ */
+afd_status afd_get_partials(afd_ctx *ctx, int32_t s, int32_t f, const void **rows, int64_t *row_bytes);
 
 /* afd_status_string: a static description of a status. */
 const char *afd_status_string(afd_status st);

@@ -112,6 +112,8 @@ def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, k
             r.scales.append(rec.scales.cpu().numpy().copy() if rec.scales is not None else None)
             r.replies.append(replies[f].view(torch.int16).cpu().numpy().view(np.uint16).copy())
     r.out = [o.view(torch.int16).cpu().numpy().view(np.uint16).copy() for o in outs_t]
+    if buf.combine != "once":
+        r.partials = [[buf.partials(s, f).cpu().numpy().copy() for f in range(cfg.F)] for s in range(cfg.N)]
     r.out_tensors = outs_t
     r.buf = buf
     return r

@@ -31,8 +31,8 @@ def log(lib):
     return out
 
 
-def cfg(N=2, F=2, E=8, K=2, H=256, alpha=4, cap=16, dtype=0):
-    return nat.Config(N, F, E, K, H, alpha, cap, dtype)
+def cfg(N=2, F=2, E=8, K=2, H=256, alpha=4, cap=16, dtype=0, combine=0):
+    return nat.Config(N, F, E, K, H, alpha, cap, dtype, combine)
 
 
 def query(lib, c, bucket):
@@ -106,7 +106,7 @@ class Ctx:
 
 def test_library_exports_every_declared_symbol():
     syms = nat.header_symbols()
-    assert len(syms) == 10
+    assert len(syms) == 11
     if not os.path.exists(nat.LIB_PATH):
         pytest.skip("HIP library not built")
     lib = ctypes.CDLL(nat.LIB_PATH)
@@ -126,7 +126,7 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("bad", [
     dict(N=0), dict(N=17), dict(F=0), dict(F=17), dict(E=0), dict(E=513), dict(E=9, F=2),
     dict(K=0), dict(K=33, E=64), dict(K=9, E=8), dict(H=128), dict(H=300), dict(alpha=0), dict(cap=0),
-    dict(dtype=2)])
+    dict(dtype=2), dict(combine=3), dict(combine=-1), dict(combine=1, F=1, E=4), dict(combine=2, F=1, E=4)])
 def test_config_rejected(lib, bad):
     assert query(lib, cfg(**bad), 1)[0] == nat.AFD_E_SHAPE
 
@@ -417,4 +417,73 @@ def test_hip_failure_leaves_state(lib):
     finally:
         lib.afd_fake_set_fail(0)
     assert x.reply(1, r1) == 0
+    x.destroy()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_per_stage_round_launches(lib, mode):
+    """Per-stage combine: each reply runs its partition's stage one, each
+    collect its source's stage two; nothing runs at the last reply."""
+    c = cfg(N=2, F=3, E=6, K=2, H=512, cap=16, combine=mode)
+    _, ws_once, _ = query(lib, cfg(N=2, F=3, E=6, K=2, H=512, cap=16), 16)
+    x = Ctx(lib, c)
+    prow = 512 * 2 if mode == 1 else 512 + 32
+    assert x.ws - ws_once >= 3 * 2 * 16 * prow                  # partial rows in the workspace
+    lib.afd_fake_log_clear()
+    assert x.dispatch(0, 5) == 0 and x.dispatch(1, 4, out=0x7100000) == 0
+    recs = [x.receive(f)[1] for f in range(3)]
+    assert log(lib) == ["dispatch fused=1 ntok=9 nblk=1 T=5,4"]
+    assert x.reply(2, recs[2]) == 0
+    lg = log(lib)
+    assert len(lg) == 1 and lg[0].startswith(f"partial f=2 ntok=9 prow={prow} base=")
+    base = int(lg[0].split("base=")[1], 16)
+    assert FAKE_WS < base < FAKE_WS + x.ws
+    assert x.reply(0, recs[0]) == 0 and log(lib)[0].startswith("partial f=0")
+    assert x.collect(0)[0] == nat.AFD_E_ORDER                    # partition 1 has not replied
+    assert x.reply(1, recs[1]) == 0 and log(lib)[0].startswith("partial f=1")
+    st, res, stride = x.collect(1)
+    assert st == 0 and res == 0x7100000 and stride == 512
+    assert log(lib) == ["final s=1 T=4 out=0x7100000"]
+    assert x.collect(0)[0] == 0 and log(lib) == ["final s=0 T=5 out=0x7000000"]
+    # where source s's rows from partition f live
+    ptr, rb = ctypes.c_void_p(), ctypes.c_int64()
+    for (s_, f_) in [(0, 0), (1, 0), (0, 2), (1, 1)]:
+        assert lib.afd_get_partials(x.ctx, s_, f_, ctypes.byref(ptr), ctypes.byref(rb)) == 0
+        assert rb.value == prow and ptr.value == base + ((f_ * 2 + s_) * 16) * prow
+    assert lib.afd_get_partials(x.ctx, 2, 0, ctypes.byref(ptr), None) == nat.AFD_E_ARG
+    assert lib.afd_get_partials(x.ctx, 0, 3, ctypes.byref(ptr), None) == nat.AFD_E_ARG
+    # an empty source runs no stage two
+    assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 3) == 0
+    recs = [x.receive(f)[1] for f in range(3)]
+    for f in range(3):
+        assert x.reply(f, recs[f]) == 0
+    log(lib)
+    assert x.collect(0)[0] == 0 and log(lib) == []
+    x.destroy()
+
+
+def test_partials_refused_in_once_mode(lib):
+    x = Ctx(lib, cfg())
+    ptr = ctypes.c_void_p()
+    assert lib.afd_get_partials(x.ctx, 0, 0, ctypes.byref(ptr), None) == nat.AFD_E_ARG
+    x.destroy()
+
+
+def test_per_stage_failed_launches_leave_state(lib):
+    x = Ctx(lib, cfg(combine=1))
+    for s in range(2):
+        assert x.dispatch(s, 2) == 0
+    recs = [x.receive(f)[1] for f in range(2)]
+    lib.afd_fake_set_fail(1)
+    try:
+        assert x.reply(0, recs[0]) == nat.AFD_E_HIP               # stage one failed: reply not recorded
+    finally:
+        lib.afd_fake_set_fail(0)
+    assert x.reply(0, recs[0]) == 0 and x.reply(1, recs[1]) == 0
+    lib.afd_fake_set_fail(1)
+    try:
+        assert x.collect(0)[0] == nat.AFD_E_HIP                   # stage two failed: not collected
+    finally:
+        lib.afd_fake_set_fail(0)
+    assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
     x.destroy()
