@@ -99,7 +99,7 @@ struct StageArgs {
     const int32_t *slot;
     int64_t prow;
     int tok_off[kMaxSources + 1];
-    int N, ntok, K, H, nvec, nseg, capacity, f, s, T;
+    int N, F, ntok, K, H, nvec, nseg, capacity, f, s, T;
 };
 
 struct CombineArgs {
@@ -745,32 +745,33 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     }
 }
 
-// float8_e4m3fn code of x, nearest with ties to the even code; magnitudes
-// at or above 448 (only an infinite input after the exact power-of-two
-// scaling) saturate to 448, NaN keeps its sign.  Normal results round the
-// float32 mantissa to 3 bits with the carry running into the exponent;
-// below 2^-6 the step is 2^-9, so the code is x * 2^9 rounded to even.
-__device__ __forceinline__ uint32_t e4m3_code(float x)
-{
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a > 0x7F800000u) code = 0x7Fu;
-    else if (a >= 0x43E00000u) code = 0x7Eu;                                   // >= 448
-    else if (a < 0x3C800000u) code = uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));   // < 2^-6
-    else code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    return sign | code;
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Value of an E4M3 code (exact in float32).
-__device__ __forceinline__ float e4m3_value(uint32_t q)
+// float8_e4m3fn codes of four scaled values (bytes 0..3 of the result):
+// the hardware conversion rounds to the nearest even code.  The inputs are
+// within 448 after the exact power-of-two scaling except for infinities,
+// which are clamped to 448 first (they decode back to infinity at the top
+// scale); NaN elements get the NaN code with their sign.
+__device__ __forceinline__ uint32_t e4m3_codes4(float x0, float x1, float x2, float x3)
 {
-    const uint32_t mag = q & 0x7Fu;
-    const uint32_t sign = (q & 0x80u) << 24;
-    if (mag == 0x7Fu) return __uint_as_float(0x7FC00000u);
-    const float v = mag < 8u ? float(mag) * 0.001953125f : __uint_as_float((((mag >> 3) + 120u) << 23) | ((mag & 7u) << 20));
-    return __uint_as_float(__float_as_uint(v) | sign);
+    const float c0 = __builtin_fminf(__builtin_fmaxf(x0, -448.0f), 448.0f);
+    const float c1 = __builtin_fminf(__builtin_fmaxf(x1, -448.0f), 448.0f);
+    const float c2 = __builtin_fminf(__builtin_fmaxf(x2, -448.0f), 448.0f);
+    const float c3 = __builtin_fminf(__builtin_fmaxf(x3, -448.0f), 448.0f);
+    uint32_t w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false)) & 0xFFFFu;
+    w = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, int(w), true));
+    const float xs[4] = {x0, x1, x2, x3};
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nan |= xs[j] != xs[j];
+    if (__ballot(nan) != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t code = ((__float_as_uint(xs[j]) >> 24) & 0x80u) | 0x7Fu;
+            w = xs[j] != xs[j] ? ((w & ~(0xFFu << (8 * j))) | (code << (8 * j))) : w;
+        }
+    }
+    return w;
 }
 
 // Scale exponent of a group from the float32 bits of its amax: the smallest
@@ -857,19 +858,23 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
         const uint32_t m = (b[j] << 16) & 0x7FFFFFFFu;
         am = (m <= 0x7F800000u && m > am) ? m : am;
     }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-        const uint32_t o = uint32_t(__shfl_xor(int(am), d, kWave));
+    // max over the 16-lane DPP row: rotations by 1, 2, 4 and 8
+    {
+        uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x121, 0xF, 0xF, false));  // row_ror:1
+        am = o > am ? o : am;
+        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x122, 0xF, 0xF, false));           // row_ror:2
+        am = o > am ? o : am;
+        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x124, 0xF, 0xF, false));           // row_ror:4
+        am = o > am ? o : am;
+        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x128, 0xF, 0xF, false));           // row_ror:8
         am = o > am ? o : am;
     }
     const int e = fp8_group_exponent(am);
     const float inv = __uint_as_float(uint32_t(127 - e) << 23);              // 2^-e, a normal float
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        lo |= e4m3_code(__uint_as_float(b[j] << 16) * inv) << (8 * j);
-        hi |= e4m3_code(__uint_as_float(b[4 + j] << 16) * inv) << (8 * j);
-    }
+    const uint32_t lo = e4m3_codes4(__uint_as_float(b[0] << 16) * inv, __uint_as_float(b[1] << 16) * inv,
+                                    __uint_as_float(b[2] << 16) * inv, __uint_as_float(b[3] << 16) * inv);
+    const uint32_t hi = e4m3_codes4(__uint_as_float(b[4] << 16) * inv, __uint_as_float(b[5] << 16) * inv,
+                                    __uint_as_float(b[6] << 16) * inv, __uint_as_float(b[7] << 16) * inv);
     const int G = a.H / 128;
     if (c < nvec) {
         uint2 v2;
@@ -883,7 +888,55 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
 }
 
 // Stage two of the per-stage combine for source a.s: one wavefront per
-// (token, column segment).
+// (token, column segment).  A partition's partial row is added when no later
+// live top-k lane of the token maps to that partition, so partitions are
+// visited in ascending order of their last live lane.  The address of a
+// partial row does not depend on the slot map, so with at most four
+// partitions the rows of every partition are requested together with the
+// token's slots (rows of partitions without a live choice are loaded but
+// never added), and the wavefront waits on memory once.
+template <bool FP8>
+__device__ __forceinline__ void add_partial(float (&acc)[8], const u32x4 &y, uint32_t sf)
+{
+#pragma clang fp contract(off)
+    if (!FP8) {
+        const uint32_t q[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[2 * j] = acc[2 * j] + __uint_as_float(q[j] << 16);
+            acc[2 * j + 1] = acc[2 * j + 1] + __uint_as_float(q[j] & 0xFFFF0000u);
+        }
+    } else {
+        // the hardware conversion decodes E4M3 exactly; the power-of-two
+        // scale keeps every nonzero product a normal float
+        const float scale = __uint_as_float(sf << 23);                         // 2^(byte - 127)
+        const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(int(y.x), false), __builtin_amdgcn_cvt_pk_f32_fp8(int(y.x), true),
+                            __builtin_amdgcn_cvt_pk_f32_fp8(int(y.y), false), __builtin_amdgcn_cvt_pk_f32_fp8(int(y.y), true)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float p0 = v[j].x * scale;
+            const float p1 = v[j].y * scale;
+            acc[2 * j] = acc[2 * j] + p0;
+            acc[2 * j + 1] = acc[2 * j + 1] + p1;
+        }
+    }
+}
+
+// One segment of a partial row: 16 bytes (BF16) or 8 code bytes plus the
+// group's scale byte (FP8).
+template <bool FP8>
+__device__ __forceinline__ void load_partial(const uint8_t *row, int c, int H, u32x4 &y, uint32_t &sf)
+{
+    if (!FP8) {
+        y = reinterpret_cast<const u32x4 *>(row)[c];
+        sf = 0;
+    } else {
+        const uint2 v = reinterpret_cast<const uint2 *>(row)[c];
+        y = u32x4{v.x, v.y, 0u, 0u};
+        sf = row[H + c / 16];
+    }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_final(StageArgs a)
 {
@@ -894,76 +947,73 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     const int seg = gw - t * a.nseg;
     if (t >= a.T) return;
     const int g = a.tok_off[a.s] + t;
+    const int nvec = a.nvec;
+    const int c = seg * kWave + lane;
+    const bool col = c < nvec;
+    const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
+    const uint8_t *base = a.partials + (int64_t(a.s) * a.capacity + t) * a.prow;
     int part = -1;
     if (lane < a.K) {
         const int sx = a.slot[(int64_t(g) * a.K + lane) * 2];
         part = sx >= 0 ? (sx >> 24) : -1;
     }
-    // lane k adds its partition's partial when no later live lane maps there
+    constexpr int SPEC = 4;
+    const bool spec = a.F <= SPEC;
+    u32x4 ys[SPEC];
+    uint32_t sfs[SPEC];
+#pragma unroll
+    for (int i = 0; i < SPEC; ++i) {
+        ys[i] = u32x4{0u, 0u, 0u, 0u};
+        sfs[i] = 127u;
+        if (spec && i < a.F && col) load_partial<FP8>(base + i * fstride, c, a.H, ys[i], sfs[i]);
+    }
     bool last = part >= 0;
     for (int j = 0; j < a.K; ++j) {
         const int pj = __builtin_amdgcn_readlane(part, j);
         last = last && !(j > lane && pj == part);
     }
     uint64_t lm = __ballot(last);
-    const int nvec = a.nvec;
-    const int c = seg * kWave + lane;
-    const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
-    const uint8_t *base = a.partials + (int64_t(a.s) * a.capacity + t) * a.prow;
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-    while (lm != 0) {
-        // up to four partials per batch, all loads issued before the adds
-        const uint8_t *rp[4];
-        int n = 0;
+    if (spec) {
+        while (lm != 0) {
+            const int k = __builtin_ctzll(lm);
+            lm &= lm - 1;
+            const int f = __builtin_amdgcn_readlane(part, k);
+            u32x4 y = ys[0];
+            uint32_t sf = sfs[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rp[i] = nullptr;
-            if (lm != 0) {
-                const int k = __builtin_ctzll(lm);
-                lm &= lm - 1;
-                rp[i] = base + int64_t(__builtin_amdgcn_readlane(part, k)) * fstride;
-                n = i + 1;
+            for (int i = 1; i < SPEC; ++i) {
+                y = f == i ? ys[i] : y;
+                sf = f == i ? sfs[i] : sf;
             }
+            add_partial<FP8>(acc, y, sf);
         }
-        if (!FP8) {
+    } else {
+        while (lm != 0) {
+            // up to four partials per batch, all loads issued before the adds
             u32x4 y[4];
+            uint32_t sf[4];
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                y[i] = u32x4{0u, 0u, 0u, 0u};
+                sf[i] = 127u;
+                if (lm != 0) {
+                    const int k = __builtin_ctzll(lm);
+                    lm &= lm - 1;
+                    if (col) load_partial<FP8>(base + int64_t(__builtin_amdgcn_readlane(part, k)) * fstride, c, a.H,
+                                               y[i], sf[i]);
+                    n = i + 1;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                y[i] = (i < n && c < nvec) ? reinterpret_cast<const u32x4 *>(rp[i])[c] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i >= n) break;
-                const uint32_t q[4] = {y[i].x, y[i].y, y[i].z, y[i].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] = acc[2 * j] + __uint_as_float(q[j] << 16);
-                    acc[2 * j + 1] = acc[2 * j + 1] + __uint_as_float(q[j] & 0xFFFF0000u);
-                }
-            }
-        } else {
-            uint2 y[4];
-            uint32_t sf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = i < n && c < nvec;
-                y[i] = ok ? reinterpret_cast<const uint2 *>(rp[i])[c] : uint2{0u, 0u};
-                sf[i] = ok ? rp[i][a.H + c / 16] : 127u;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i >= n) break;
-                const float scale = __uint_as_float(sf[i] << 23);                // 2^(byte - 127)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[j] = acc[j] + e4m3_value((y[i].x >> (8 * j)) & 0xFFu) * scale;
-                    acc[4 + j] = acc[4 + j] + e4m3_value((y[i].y >> (8 * j)) & 0xFFu) * scale;
-                }
-            }
+                if (i < n) add_partial<FP8>(acc, y[i], sf[i]);
         }
     }
-    if (c < nvec) {
+    if (col) {
         u32x4 r;
         r.x = bf16_rne_bits(acc[0]) | (bf16_rne_bits(acc[1]) << 16);
         r.y = bf16_rne_bits(acc[2]) | (bf16_rne_bits(acc[3]) << 16);
@@ -1060,6 +1110,7 @@ StageArgs make_stage_args(const RoundPlan &p)
     a.prow = p.prow;
     for (int s = 0; s <= p.N; ++s) a.tok_off[s] = p.tok_off[s];
     a.N = p.N;
+    a.F = p.F;
     a.ntok = p.ntok;
     a.K = p.K;
     a.H = p.H;

@@ -119,3 +119,66 @@ def test_staged_graph_replay_with_inputs_changed(mode):
             got = res[s].view(torch.int16).cpu().numpy().view(np.uint16)
             assert np.array_equal(got, ref.out[off:off + T]), f"replay {rep} source {s}"
             off += T
+
+
+def _crafted_rows(rng, n, H):
+    """BF16 rows whose groups hit every E4M3 rounding case after scaling:
+    exact ties between adjacent codes, exact codes, the subnormal range,
+    signed zeros, and (one group each) NaN and an infinity."""
+    import torch
+    pos = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    G = H // 128
+    out = np.zeros((n, H), np.float32)
+    for i in range(n):
+        for b in range(G):
+            k = int(rng.integers(-100, 100))
+            grp = np.concatenate([rng.choice(mids, 60), rng.choice(pos, 40), rng.uniform(-1, 1, 27) * 2.0 ** -8, [448.0]])
+            grp = grp * np.where(rng.random(128) < 0.5, -1.0, 1.0)
+            grp[5] = 0.0
+            grp[6] = -0.0
+            rng.shuffle(grp)
+            out[i, b * 128:(b + 1) * 128] = (grp * 2.0 ** k).astype(np.float32)
+    rows = gen.f32_to_bf16_bits(out)
+    rows[0, 3] = 0x7FC0                      # NaN in one group
+    if n > 1:
+        rows[1, 130] = 0x7F80                # +infinity in another
+    return rows
+
+
+def test_staged_fp8_codes_at_ties_and_specials():
+    """K = 1 (weight 1): each partial is its reply row, so crafted replies put
+    exact ties, subnormals, signed zeros, NaN and an infinity through the
+    kernel's E4M3 encoding, compared byte for byte with the oracle."""
+    h = _gpu()
+    import torch
+    inst = gen.random_small(800, N=2, F=2, E=8, K=1, alpha=4, T=[40, 33], H=512, p_skip=0.0)
+    cfg = inst.cfg
+    assert np.all(np.concatenate([s.weights for s in inst.sources]) == 1.0)
+    buf = h.make_buffer(inst, combine="per_stage_fp8")
+    dev = h.upload(inst)
+    for s, (x, ids, w, sc) in enumerate(dev):
+        buf.source_dispatch(s, x, ids, w, sc, bucket=cfg.bucket)
+    recs = [buf.worker_receive(f, bucket=cfg.bucket) for f in range(cfg.F)]
+    rng = np.random.default_rng(801)
+    replies_np = [_crafted_rows(rng, r.receive_rows, cfg.H) for r in recs]
+    replies = [torch.from_numpy(y.view(np.int16)).cuda().view(torch.bfloat16) for y in replies_np]
+    for f, r in enumerate(recs):
+        buf.worker_reply(f, replies[f], r.receipt)
+    outs = [buf.source_collect(s) for s in range(cfg.N)]
+    torch.cuda.synchronize()
+    ids = np.concatenate([s.ids for s in inst.sources])
+    w = np.concatenate([s.weights for s in inst.sources])
+    lay = oracle.layout(cfg.T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
+    partial, has = oracle.combine_partials(w, lay, cfg.H, cfg.F, replies_np)
+    q = oracle.quantize_partials(partial, has)
+    ref = oracle.combine_stages(lay, cfg.H, None, q)
+    off = 0
+    for s, T in enumerate(cfg.T):
+        for f in range(cfg.F):
+            got = buf.partials(s, f).cpu().numpy()
+            m = has[f][off:off + T].astype(bool)
+            assert np.array_equal(got[m], q[f][off:off + T][m]), f"source {s} partition {f}"
+        o = outs[s].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(o, ref[off:off + T]), f"source {s} output"
+        off += T
