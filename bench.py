@@ -94,7 +94,7 @@ def round_bytes(cfg, L: int, combine: str = "once", n_partial: int = 0) -> dict:
 class RoundSet:
     """One independent set of inputs, outputs, arenas and replies."""
 
-    def __init__(self, inst, view, combine="once"):
+    def __init__(self, inst, view, combine="once", cached=False):
         import torch
         from tests import gpu_harness as h
         self.inst = inst
@@ -113,14 +113,17 @@ class RoundSet:
         for s in range(self.cfg.N):
             self.buf.source_collect(s, view=view)
         torch.cuda.synchronize()
+        self.cached = cached
 
     def dispatch_phase(self):
         """Every source dispatch and worker receive of a round (the receive
-        launches the dispatch kernels); returns the receipts."""
+        launches the dispatch kernels); returns the receipts.  Cached rounds
+        reuse the layout of the set's first round."""
         c = self.cfg
         b = self.buf
         for s, (x, ids, w, scl) in enumerate(self.dev):
-            b.source_dispatch(s, x, ids, w, scl, bucket=c.bucket, out=self.outs[s])
+            b.source_dispatch(s, x, None if self.cached else ids, w, scl, bucket=c.bucket, out=self.outs[s],
+                              cached=self.cached)
         return [b.worker_receive(f, bucket=c.bucket) for f in range(c.F)]
 
     def combine_phase(self, recs):
@@ -348,6 +351,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="2a2f_decode", choices=gen.WORKLOADS)
     ap.add_argument("--combine", default="once", choices=["once", "per_stage", "per_stage_fp8"],
                     help="combine rounding: once (default), or per stage with BF16 or FP8 partials")
+    ap.add_argument("--cached", action="store_true",
+                    help="time rounds that reuse the previous layout (cached dispatch, unchanged routes)")
     ap.add_argument("--graph-rounds", type=int, default=0, help="rounds per captured graph (default by size)")
     ap.add_argument("--cold-bytes", type=float, default=512e6, help="bytes the cold rotation spans")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
@@ -389,11 +394,11 @@ def main(argv=None):
     G = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
     G = max(G, S) if S > 1 else G
     G = int(math.ceil(G / S) * S)
-    sets = [RoundSet(inst, view, args.combine)]
+    sets = [RoundSet(inst, view, args.combine, args.cached)]
     hot_us = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
     print(f"[bench] hot: {hot_us:.3f} us/round", file=sys.stderr, flush=True)
     for _ in range(S - 1):
-        sets.append(RoundSet(inst, view, args.combine))
+        sets.append(RoundSet(inst, view, args.combine, args.cached))
     cold_us = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
     print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round", file=sys.stderr, flush=True)
 
@@ -405,6 +410,10 @@ def main(argv=None):
     fused = sum(cfg.T) <= 512 and sum(cfg.T) * cfg.K <= 4096 and cfg.E <= 256 and row_cols <= 2048
     dom = "dispatch" if fused and nb["dispatch"] >= nb["combine"] else "combine"
     dom_name = {"dispatch": "k_fused", "combine": "k_combine"}[dom]
+    if args.cached:
+        # the cached dispatch is one kernel at every size
+        dom = "dispatch" if nb["dispatch"] >= nb["combine"] else "combine"
+        dom_name = {"dispatch": "k_scatter_cached", "combine": "k_combine"}[dom]
     if args.combine != "once":
         # the per-stage combine is F stage-one and N stage-two launches: the
         # phase as a whole
@@ -435,7 +444,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
                    "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
                    "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
-                   "rounds_per_graph": G, "combine": args.combine},
+                   "rounds_per_graph": G, "combine": args.combine, "cached_layout": bool(args.cached)},
         "us_per_round": round(cold_us, 3),
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_round_hot": round(hot_us, 3),

@@ -59,6 +59,7 @@ SIGNATURES = {
     "afd_bind_partition": ([_P, _I32, _P, _P, _P, _I64], _I32),
     "afd_destroy": ([_P], _I32),
     "afd_source_dispatch": ([_P, _I32, _I32, _P, _P, _P, _P, _I64, _I64, _P, _I32, _I32, _P], _I32),
+    "afd_source_dispatch_cached": ([_P, _I32, _I32, _P, _P, _P, _I64, _I64, _P, _I32, _P], _I32),
     "afd_worker_receive": ([_P, _I32, _I32, _I32, _P, ctypes.POINTER(Receive), _P], _I32),
     "afd_worker_reply": ([_P, _I32, _P, _I64, ctypes.POINTER(Receipt), _P], _I32),
     "afd_source_collect": ([_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64), _P], _I32),

@@ -97,21 +97,29 @@ class Buffer:
         return rb.value
 
     # -- the four role calls ---------------------------------------------------
-    def source_dispatch(self, s, x, ids, weights, x_scale=None, *, bucket, read_host_counts=False, out=None):
-        T = int(ids.shape[0]) if ids is not None else 0
+    def source_dispatch(self, s, x, ids, weights, x_scale=None, *, bucket, read_host_counts=False, out=None,
+                        cached=False):
+        """cached=True reuses the receive layout of the last round (the
+        ElasticBuffer page's cached dispatch): ids are not read (pass None),
+        T must match that round's, and read_host_counts is not available."""
+        if cached:
+            T = int(weights.shape[0]) if weights is not None else 0
+        else:
+            T = int(ids.shape[0]) if ids is not None else 0
         if T > 0:
             if self.fp8:
                 if x.element_size() != 1:
                     raise TypeError("FP8 dispatch takes float8_e4m3fn (or uint8) activations")
             elif x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
                 raise TypeError("BF16 dispatch takes bfloat16 activations")
-            if ids.dtype != topk_idx_dtype:
+            if not cached and ids.dtype != topk_idx_dtype:
                 raise TypeError("ids must be buffer.topk_idx_dtype (int32)")
             if weights.dtype != torch.float32:
                 raise TypeError("weights must be float32")
-            if tuple(x.shape) != (T, self.H) or tuple(ids.shape) != (T, self.K) or tuple(weights.shape) != (T, self.K):
+            if tuple(x.shape) != (T, self.H) or tuple(weights.shape) != (T, self.K) or \
+                    (not cached and tuple(ids.shape) != (T, self.K)):
                 raise ValueError("x must be [T, H]; ids and weights [T, K]")
-            if not (x.is_contiguous() and ids.is_contiguous() and weights.is_contiguous()):
+            if not (x.is_contiguous() and weights.is_contiguous() and (cached or ids.is_contiguous())):
                 raise ValueError("x, ids and weights must be contiguous")
         sst = ssg = 0
         if x_scale is not None:
@@ -120,9 +128,16 @@ class Buffer:
             sst, ssg = x_scale.stride()
         if out is None and T > 0:
             out = torch.empty((T, self.H), dtype=torch.bfloat16, device=self.device)
-        st = self.lib.afd_source_dispatch(self.ctx, s, T, _ptr(x if T else None), _ptr(ids if T else None),
-                                          _ptr(weights if T else None), _ptr(x_scale), sst, ssg, _ptr(out),
-                                          bucket, 1 if read_host_counts else 0, _stream(self.device))
+        if cached:
+            if read_host_counts:
+                raise ValueError("a cached dispatch never reads host counts")
+            st = self.lib.afd_source_dispatch_cached(self.ctx, s, T, _ptr(x if T else None),
+                                                     _ptr(weights if T else None), _ptr(x_scale), sst, ssg,
+                                                     _ptr(out), bucket, _stream(self.device))
+        else:
+            st = self.lib.afd_source_dispatch(self.ctx, s, T, _ptr(x if T else None), _ptr(ids if T else None),
+                                              _ptr(weights if T else None), _ptr(x_scale), sst, ssg, _ptr(out),
+                                              bucket, 1 if read_host_counts else 0, _stream(self.device))
         nat.check(st, "source_dispatch")
         self._round_refs[("src", s)] = (x, ids, weights, x_scale, out)
         self._out[s] = out

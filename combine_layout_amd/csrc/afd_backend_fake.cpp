@@ -53,7 +53,10 @@ int be_launch_dispatch(const RoundPlan &p, void *)
         snprintf(b, sizeof(b), "%s%d", s ? "," : "", p.tok_off[s + 1] - p.tok_off[s]);
         srcs += b;
     }
-    logf("dispatch fused=%d ntok=%d nblk=%d T=%s", p.fused ? 1 : 0, p.ntok, p.nblk, srcs.c_str());
+    if (p.cached)
+        logf("dispatch cached ntok=%d T=%s", p.ntok, srcs.c_str());
+    else
+        logf("dispatch fused=%d ntok=%d nblk=%d T=%s", p.fused ? 1 : 0, p.ntok, p.nblk, srcs.c_str());
     return g_fail;
 }
 

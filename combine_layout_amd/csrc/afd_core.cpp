@@ -58,7 +58,13 @@ struct afd_ctx {
     int64_t recv_rows[kMaxParts] = {};
     int32_t host_ends[kMaxExperts] = {};
     bool route_error = false;
+    bool round_cached = false;     // this round reuses the last layout
     RoundPlan plan;
+
+    // the last layout whose dispatch work was enqueued (for cached rounds)
+    bool layout_valid = false;
+    int layout_bucket = 0;
+    int layout_T[kMaxSources] = {};
 };
 
 namespace {
@@ -135,6 +141,7 @@ void reset_round(afd_ctx *c)
     c->ndispatched = c->nreceived = c->nreplied = c->ncollected = 0;
     c->launched = false;
     c->route_error = false;
+    c->round_cached = false;
     RoundPlan fresh;
     c->plan = fresh;
 }
@@ -269,23 +276,28 @@ afd_status afd_destroy(afd_ctx *c)
     return rc == 0 ? AFD_OK : AFD_E_HIP;
 }
 
-afd_status afd_source_dispatch(afd_ctx *c, int32_t s, int32_t T, const void *x, const int32_t *ids,
-                               const float *weights, const float *x_scale, int64_t sst, int64_t ssg,
-                               void *out_bf16, int32_t bucket, int32_t rhc, void *stream)
+// Checks and records one source's round inputs; ids is NULL for a cached
+// round (the layout of the last enqueued dispatch is reused).
+static afd_status record_dispatch(afd_ctx *c, int32_t s, int32_t T, const void *x, const int32_t *ids,
+                                  const float *weights, const float *x_scale, int64_t sst, int64_t ssg,
+                                  void *out_bf16, int32_t bucket, int32_t rhc, bool cached)
 {
-    (void)stream;
     if (!c) return AFD_E_ARG;
     const afd_config &g = c->cfg;
     if (s < 0 || s >= g.num_sources) return AFD_E_ARG;
     if (c->phase != kIdle && c->phase != kDispatching) return AFD_E_ORDER;
     if (c->phase == kDispatching && c->dispatched[s]) return AFD_E_ORDER;
+    if (c->phase == kDispatching && cached != c->round_cached) return AFD_E_ORDER;
+    if (cached && !c->layout_valid) return AFD_E_ORDER;
     if (bucket < 1 || bucket > g.capacity) return AFD_E_ARG;
     if (rhc != 0 && rhc != 1) return AFD_E_ARG;
     if (c->phase == kDispatching && (bucket != c->bucket || rhc != c->rhc)) return AFD_E_ARG;
+    if (cached && bucket != c->layout_bucket) return AFD_E_ARG;
     if (T < 0 || T > bucket) return AFD_E_SHAPE;
+    if (cached && T != c->layout_T[s]) return AFD_E_SHAPE;
     const bool fp8 = g.dtype == AFD_FP8_E4M3;
     if (T > 0) {
-        if (!x || !ids || !weights) return AFD_E_ARG;
+        if (!x || (!ids && !cached) || !weights) return AFD_E_ARG;
         if (!aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4)) return AFD_E_ARG;
         if (fp8) {
             if (!x_scale || !aligned(x_scale, 4) || sst < 0 || ssg < 0) return AFD_E_ARG;
@@ -300,11 +312,12 @@ afd_status afd_source_dispatch(afd_ctx *c, int32_t s, int32_t T, const void *x, 
         c->round += 1;
         c->bucket = bucket;
         c->rhc = rhc;
+        c->round_cached = cached;
         c->phase = kDispatching;
     }
     RoundPlan &p = c->plan;
     p.x[s] = T > 0 ? x : nullptr;
-    p.ids[s] = T > 0 ? ids : nullptr;
+    p.ids[s] = (T > 0 && !cached) ? ids : nullptr;
     p.w[s] = T > 0 ? weights : nullptr;
     p.scale[s] = (fp8 && T > 0) ? x_scale : nullptr;
     p.sst[s] = sst;
@@ -315,6 +328,22 @@ afd_status afd_source_dispatch(afd_ctx *c, int32_t s, int32_t T, const void *x, 
     c->ndispatched += 1;
     if (c->ndispatched == g.num_sources) c->phase = kExchanging;
     return AFD_OK;
+}
+
+afd_status afd_source_dispatch(afd_ctx *c, int32_t s, int32_t T, const void *x, const int32_t *ids,
+                               const float *weights, const float *x_scale, int64_t sst, int64_t ssg,
+                               void *out_bf16, int32_t bucket, int32_t rhc, void *stream)
+{
+    (void)stream;
+    return record_dispatch(c, s, T, x, ids, weights, x_scale, sst, ssg, out_bf16, bucket, rhc, false);
+}
+
+afd_status afd_source_dispatch_cached(afd_ctx *c, int32_t s, int32_t T, const void *x, const float *weights,
+                                      const float *x_scale, int64_t sst, int64_t ssg, void *out_bf16,
+                                      int32_t bucket, void *stream)
+{
+    (void)stream;
+    return record_dispatch(c, s, T, x, nullptr, weights, x_scale, sst, ssg, out_bf16, bucket, 0, true);
 }
 
 afd_status afd_worker_receive(afd_ctx *c, int32_t f, int32_t bucket, int32_t rhc, int32_t *host_counts,
@@ -338,8 +367,12 @@ afd_status afd_worker_receive(afd_ctx *c, int32_t f, int32_t bucket, int32_t rhc
             if (capturing) return AFD_E_ARG;
         }
         build_plan(c);
+        c->plan.cached = c->round_cached;
         if (be_launch_dispatch(c->plan, stream) != 0) return AFD_E_HIP;
         c->launched = true;
+        c->layout_valid = true;
+        c->layout_bucket = c->bucket;
+        for (int q = 0; q < g.num_sources; ++q) c->layout_T[q] = c->T[q];
         for (int q = 0; q < g.num_partitions; ++q) c->recv_rows[q] = need;
         if (rhc) {
             uint64_t word = kNoError;

@@ -29,6 +29,10 @@
 //             reply rows with 16-byte loads, float32 multiply-then-add in
 //             ascending k, rounds once to bfloat16.
 //   k_copy    inbox -> caller output (single-partition collect without view).
+//   k_scatter_cached  dispatch of a round that reuses the last layout: the
+//             slot map already holds every live choice's partition and row,
+//             so each token's row, scales and new weights go straight to
+//             their slots (64, 128 or 256 lanes per token by row length).
 //   k_partial per-stage combine, stage one (at partition f's reply): one
 //             wavefront per (token, column segment) sums the token's live rows
 //             of partition f like k_combine, rounds to a BF16 partial and
@@ -655,6 +659,110 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     }
 }
 
+// Dispatch of a cached round.  Block = 256 threads = 256 / LPT tokens, LPT
+// (64, 128 or 256) lanes per token, each lane holding VMAX 16-byte columns
+// (column i * LPT + lane of its token); longer rows loop over chunks.  Every
+// wavefront of a token reads the token's K slots itself (no hand-off between
+// wavefronts); the token's first wavefront also writes the new weights into
+// the slot map and the row weights.
+template <int VMAX>
+__global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
+{
+    __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
+    const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
+    const int wpt = lpt / kWave;                          // wavefronts per token
+    const int g = blockIdx.x * (256 / lpt) + wave / wpt;
+    const int tl = (wave % wpt) * kWave + lane;           // lane within the token
+    const bool have = g < a.ntok;
+    const int K = a.K, nvec = a.nvec;
+    const int s = source_of(a, have ? g : 0);
+    const SourceArgs &src = a.src[s];
+    const int t = (have ? g : 0) - int(src.off);
+    u32x4 v[VMAX];
+    int2 sl;
+    sl.x = -1;
+    sl.y = 0;
+    float wk = 0.0f;
+    if (have) {
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i) {
+            const int c = i * lpt + tl;
+            v[i] = xs[c < nvec ? c : 0];
+        }
+        if (lane < K) {
+            sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * K + lane];
+            wk = src.w[int64_t(t) * K + lane];
+        }
+    }
+    if (lane == 0) {
+        if (wave == 0) table_to_lds(s_prow, a.rows);
+        if (wave == 1) table_to_lds(s_pw, a.roww);
+        if (wave == 2) table_to_lds(s_ps, a.scales);
+    }
+    lds_barrier();
+    if (!have) return;
+    uint64_t d = 0, ds = 0;
+    if (lane < K && sl.x >= 0) {
+        const int part = sl.x >> 24;
+        const int row = sl.x & 0xFFFFFF;
+        d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
+        ds = s_ps[part] + uint64_t(row) * uint64_t(a.G) * 4u;
+        if (tl < kWave) {
+            reinterpret_cast<float *>(s_pw[part])[row] = wk;
+            a.slot[(int64_t(g) * K + lane) * 2 + 1] = __float_as_int(wk);
+        }
+    }
+    const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
+    for (int k = 0; k < K; ++k) {
+        const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+        if (dk == 0) continue;
+        const gptr<u32x4> dst = (gptr<u32x4>)dk;
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i) {
+            const int c = i * lpt + tl;
+            if (c < nvec) __builtin_nontemporal_store(v[i], &dst[c]);
+        }
+    }
+    // rows longer than lpt * VMAX columns: the remaining columns, chunk by chunk
+    if (nvec > lpt * VMAX) {
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
+        for (int cb = lpt * VMAX; cb < nvec; cb += lpt * VMAX) {
+            u32x4 r[VMAX];
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = cb + i * lpt + tl;
+                if (c < nvec) r[i] = xs[c];
+            }
+            for (int k = 0; k < K; ++k) {
+                const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+                if (dk == 0) continue;
+                const gptr<u32x4> dst = (gptr<u32x4>)dk;
+#pragma unroll
+                for (int i = 0; i < VMAX; ++i) {
+                    const int c = cb + i * lpt + tl;
+                    if (c < nvec) __builtin_nontemporal_store(r[i], &dst[c]);
+                }
+            }
+        }
+    }
+    if (a.fp8 && tl < kWave) {
+        const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+        const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
+        for (int b = lane; b < a.G; b += kWave) {
+            const float val = sc[int64_t(b) * src.ssg];
+            for (int k = 0; k < K; ++k) {
+                const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                if (sk == 0) continue;
+                ((gptr<float>)sk)[b] = val;
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 {
     uint32_t u = __float_as_uint(f);
@@ -1093,6 +1201,14 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
 }
 
 template <int VMAX>
+int launch_cached_v(const DispatchArgs &a, int lpt, hipStream_t st)
+{
+    const int tpb = 256 / lpt;
+    hipLaunchKernelGGL(k_scatter_cached<VMAX>, dim3((a.ntok + tpb - 1) / tpb), dim3(256), 0, st, a, lpt);
+    return launched_ok();
+}
+
+template <int VMAX>
 int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
@@ -1145,6 +1261,18 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     const DispatchArgs a = make_dispatch_args(p);
     const bool k32 = p.K > 8;
     const int vm = vmax_for(a.nvec);
+    if (p.cached) {
+        if (p.ntok == 0) return 0;
+        // lanes per token: the row's columns rounded up to 64, 128 or 256
+        const int lpt = a.nvec <= 64 ? 64 : a.nvec <= 128 ? 128 : 256;
+        const int per = (a.nvec + lpt - 1) / lpt;
+        switch (per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8) {
+        case 1: return launch_cached_v<1>(a, lpt, st);
+        case 2: return launch_cached_v<2>(a, lpt, st);
+        case 4: return launch_cached_v<4>(a, lpt, st);
+        default: return launch_cached_v<8>(a, lpt, st);
+        }
+    }
     if (p.fused) {
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.nvec + 255) / 256;

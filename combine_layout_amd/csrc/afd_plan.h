@@ -67,6 +67,7 @@ struct RoundPlan {
     int ntok = 0;
     int tok_off[kMaxSources + 1] = {};
     bool fused = false;      // one-kernel dispatch
+    bool cached = false;     // scatter from the slot map of the last layout
     int nblk = 0;            // layout tiles (split path)
     int tile = 0;            // tokens per layout tile
     // per source

@@ -199,6 +199,27 @@ afd_status afd_source_dispatch(afd_ctx *ctx, int32_t s, int32_t T, const void *x
                                int32_t read_host_counts, void *stream);
 
 /*
+ * afd_source_dispatch_cached (ElasticBuffer page, "Cached Dispatch": a
+ * dispatch given the handle of an earlier one reuses its layout, skipping
+ * the layout computation and any host synchronisation).  Records source s's
+ * round inputs like afd_source_dispatch, but without ids: the round reuses
+ * the receive layout of the last round whose dispatch work was enqueued on
+ * this context (every slot, ends[] and the route-error word stay as that
+ * round left them), so its dispatch is the scatter of x, scales and the new
+ * weights alone.  The caller guarantees that the routes are unchanged; the
+ * new weights are applied (row weights and the combine).
+ *   T must equal source s's token count in that layout, and bucket its
+ *   bucket; read_host_counts is not available (the round never syncs).
+ * Every source of a round must dispatch the same way (all cached or none).
+ * Errors: AFD_E_ORDER (no layout yet, or mixed with afd_source_dispatch in
+ * a round, or out of round order), AFD_E_SHAPE (T differs from the layout),
+ * AFD_E_ARG (pointers, alignment, bucket).
+ */
+afd_status afd_source_dispatch_cached(afd_ctx *ctx, int32_t s, int32_t T, const void *x, const float *weights,
+                                      const float *x_scale, int64_t scale_stride_t, int64_t scale_stride_g,
+                                      void *out_bf16, int32_t bucket, void *stream);
+
+/*
  * afd_worker_receive (contract page: worker_receive(bucket,
  * read_host_counts)).  Needs every source dispatched.  The round's first
  * receive enqueues the route check, layout and scatter for ALL partitions on

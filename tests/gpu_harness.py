@@ -84,14 +84,17 @@ class GpuRound:
 
 
 def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, keep_arrays=True, pad_value=NAN_BF16,
-              outs=None):
+              outs=None, cached=False):
+    """One round through the binding; cached=True dispatches without ids,
+    reusing the buffer's last layout."""
     cfg = inst.cfg
     buf = buf or make_buffer(inst)
     dev = dev or upload(inst)
     bucket = bucket or cfg.bucket
     for s, (x, ids, w, sc) in enumerate(dev):
         o = outs[s] if outs is not None else None
-        buf.source_dispatch(s, x, ids, w, sc, bucket=bucket, read_host_counts=rhc, out=o)
+        buf.source_dispatch(s, x, None if cached else ids, w, sc, bucket=bucket, read_host_counts=rhc, out=o,
+                            cached=cached)
     recs = [buf.worker_receive(f, bucket=bucket, read_host_counts=rhc) for f in range(cfg.F)]
     replies = [identity_replies(cfg, rec, f, pad_value) for f, rec in enumerate(recs)]
     for f, rec in enumerate(recs):

@@ -67,6 +67,13 @@ class Ctx:
                                             scale if T else 0, sst, ssg, out,
                                             c.capacity if bucket is None else bucket, rhc, None)
 
+    def dispatch_cached(self, s, T, bucket=None, out=0x7000000, x=0x4000000, w=0x6000000, scale=None, sst=0, ssg=0):
+        c = self.c
+        if scale is None:
+            scale = 0x8000000 if c.dtype == 1 else 0
+        return self.lib.afd_source_dispatch_cached(self.ctx, s, T, x if T else 0, w if T else 0, scale if T else 0,
+                                                   sst, ssg, out, c.capacity if bucket is None else bucket, None)
+
     def receive(self, f, bucket=None, rhc=0, counts=None):
         rec = nat.Receive()
         hc = (ctypes.c_int32 * (self.c.num_experts // self.c.num_partitions))() if counts else None
@@ -106,7 +113,7 @@ class Ctx:
 
 def test_library_exports_every_declared_symbol():
     syms = nat.header_symbols()
-    assert len(syms) == 11
+    assert len(syms) == 12
     if not os.path.exists(nat.LIB_PATH):
         pytest.skip("HIP library not built")
     lib = ctypes.CDLL(nat.LIB_PATH)
@@ -487,3 +494,44 @@ def test_per_stage_failed_launches_leave_state(lib):
         lib.afd_fake_set_fail(0)
     assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
     x.destroy()
+
+
+def test_cached_round(lib):
+    """A cached dispatch reuses the last enqueued layout: its T per source and
+    bucket, no ids, no host counts, and every source of the round alike."""
+    x = Ctx(lib, cfg())
+    assert x.dispatch_cached(0, 4) == nat.AFD_E_ORDER              # no layout yet
+    x.full_round(T=(4, 3))
+    lib.afd_fake_log_clear()
+    assert x.dispatch_cached(0, 5) == nat.AFD_E_SHAPE              # T differs from the layout
+    assert x.dispatch_cached(0, 4, bucket=8) == nat.AFD_E_ARG      # bucket differs
+    assert x.dispatch_cached(0, 4, w=0) == nat.AFD_E_ARG           # weights required
+    assert x.dispatch_cached(0, 4) == 0
+    assert x.dispatch(1, 3) == nat.AFD_E_ORDER                     # mixed in one round
+    assert x.dispatch_cached(1, 3) == 0
+    assert log(lib) == []
+    st, r0, _ = x.receive(0)
+    assert st == 0 and log(lib) == ["dispatch cached ntok=7 T=4,3"]
+    assert x.receive(1, rhc=1)[0] == nat.AFD_E_ARG                 # no host counts in a cached round
+    st, r1, _ = x.receive(1)
+    assert x.reply(0, r0) == 0 and x.reply(1, r1) == 0
+    assert log(lib) == ["combine ntok=7 out=0x7000000,0x7000000"]
+    assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
+    # a new layout (different T) becomes the cached one
+    x.full_round(T=(2, 6))
+    assert x.dispatch_cached(0, 4) == nat.AFD_E_SHAPE
+    assert x.dispatch_cached(0, 2) == 0 and x.dispatch_cached(1, 6) == 0
+    lib.afd_fake_log_clear()
+    assert x.receive(0)[0] == 0 and log(lib) == ["dispatch cached ntok=8 T=2,6"]
+    x.destroy()
+
+
+def test_cached_round_empty_and_fp8(lib):
+    y = Ctx(lib, cfg(dtype=1))
+    y.full_round(T=(0, 5))
+    assert y.dispatch_cached(0, 0, out=0) == 0
+    assert y.dispatch_cached(1, 5, scale=0) == nat.AFD_E_ARG       # FP8 needs scales
+    assert y.dispatch_cached(1, 5, sst=1, ssg=5) == 0
+    lib.afd_fake_log_clear()
+    assert y.receive(0)[0] == 0 and log(lib) == ["dispatch cached ntok=5 T=0,5"]
+    y.destroy()
