@@ -145,6 +145,25 @@ def test_parity_random_split_path(case):
     assert check_round(inst, g, ref) == 0
 
 
+TILED = [(0, [5000, 4000], 256, 4, "bf16"), (1, [600], 8192, 8, "bf16"), (2, [9000], 256, 2, "fp8"),
+         (3, [3000, 3000], 4096, 3, "bf16")]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: f"t{c[0]}")
+def test_parity_tiled_path(case):
+    """Larger tiled rounds: many tiles (more than 8192 tokens, so a tile's
+    expert counts span more than 32 tiles), rows over 8 KB (the scatter loops
+    over row chunks) and 8 KB rows with three ids per token."""
+    h = _gpu()
+    i, T, H, K, dtype = case
+    inst = gen.random_small(400 + i, N=len(T), F=2, E=16, K=K, alpha=8, T=T, H=H, p_skip=0.1, dtype=dtype,
+                            bucket=max(T))
+    print(f"[parity tiled] t{i} T={T} H={H} K={K} {dtype}", flush=True)
+    g = h.run_round(inst, rhc=(i % 2 == 0))
+    ref = _oracle_ref(inst, g.receive_rows)
+    assert check_round(inst, g, ref) == 0
+
+
 @pytest.mark.parametrize("K", [12, 32])
 def test_parity_fused_wide_topk(K):
     h = _gpu()

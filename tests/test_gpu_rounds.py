@@ -112,11 +112,18 @@ def _inject(inst, rng, n_bad=6):
     return inst
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_invalid_routes_sticky_first_offender(seed):
+# (seed, tokens per source, H): the one-kernel dispatch and the tiled path
+# with few and with many tiles
+ROUTE_CASES = [(0, [37, 50], 512), (1, [37, 50], 512), (2, [37, 50], 512), (3, [700, 900], 512),
+               (4, [5000, 4000], 256)]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"s{c[0]}-{sum(c[1])}")
+def test_invalid_routes_sticky_first_offender(case):
     h = _gpu()
+    seed, T, H = case
     rng = np.random.default_rng(seed)
-    inst = _inject(_small(20 + seed, K=4), rng)
+    inst = _inject(_small(20 + seed, K=4, T=T, H=H), rng, n_bad=6 if sum(T) < 1000 else 24)
     cfg = inst.cfg
     ids = np.concatenate([s.ids for s in inst.sources])
     lay = oracle.layout(cfg.T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
@@ -128,7 +135,7 @@ def test_invalid_routes_sticky_first_offender(seed):
     code, s, t, k = buf.get_error(clear=False)
     assert (code, s, t, k) == lay.err
     # sticky across a clean round; cleared on request
-    clean = _small(40 + seed)
+    clean = _small(40 + seed, T=T, H=H)
     h.run_round(clean, buf)
     assert buf.get_error(clear=True) == lay.err
     assert buf.get_error()[0] == 0

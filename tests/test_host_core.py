@@ -403,6 +403,19 @@ def test_split_path_above_fused_limits(lib):
     assert z.receive(0)[0] == 0
     assert log(lib) == ["dispatch fused=0 ntok=600 nblk=3 T=600"]
     z.destroy()
+    # many tiles and 16 KB rows
+    u = Ctx(lib, cfg(N=2, F=2, E=8, K=2, cap=8192))
+    lib.afd_fake_log_clear()
+    assert u.dispatch(0, 5000) == 0 and u.dispatch(1, 4000) == 0
+    assert u.receive(0)[0] == 0
+    assert log(lib) == ["dispatch fused=0 ntok=9000 nblk=36 T=5000,4000"]
+    u.destroy()
+    v = Ctx(lib, cfg(N=1, F=2, E=8, K=2, H=8192, cap=2048))
+    lib.afd_fake_log_clear()
+    assert v.dispatch(0, 600) == 0
+    assert v.receive(0)[0] == 0
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=3 T=600"]
+    v.destroy()
 
 
 def test_hip_failure_leaves_state(lib):
