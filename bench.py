@@ -323,14 +323,18 @@ def kernel_digest():
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
-    """HBM bytes per dispatch of `kernel` on `workload` measured with the
-    rocprofv3 counters FETCH_SIZE and WRITE_SIZE (scaled by a plain-copy
-    calibration), from the summaries under profiles/ -- None when no summary
-    covers it or the kernel source changed since the counters were taken."""
+def load_traffic(kernel, workload, mode="", mult=None):
+    """HBM bytes per dispatch of `kernel` on `workload` (run in `mode`: "" for
+    the default round, "_cached" or "_per_stage..." for the others) measured
+    with the rocprofv3 counters FETCH_SIZE and WRITE_SIZE (scaled by a
+    plain-copy calibration), from the summaries under profiles/ named
+    <kernels>_<workload><mode>.md -- None when no summary covers it or the
+    kernel source changed since the counters were taken.  A kernel "a+b" is
+    the sum of a and b, each times its launches in `mult`."""
     import glob
     digest = kernel_digest()
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
+    parts = kernel.split("+")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}{mode}.md"))):
         text = open(path).read()
         if f"`{digest}`" not in text:
             continue
@@ -338,8 +342,8 @@ def load_traffic(kernel, workload):
             line = line.strip()
             if line.startswith("traffic_bytes_per_dispatch "):
                 table = json.loads(line[len("traffic_bytes_per_dispatch "):])
-                if kernel in table:
-                    return table[kernel]
+                if all(k in table for k in parts):
+                    return sum(table[k] * (mult or {}).get(k, 1) for k in parts)
     return None
 
 
@@ -420,7 +424,10 @@ def main(argv=None):
         dom, dom_name = "combine", "k_partial+k_final"
     dom_bytes = nb[dom]
     dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
-    traffic = load_traffic(dom_name, args.workload)
+    mode = "_cached" if args.cached else ""
+    if args.combine != "once":
+        mode += "_" + args.combine
+    traffic = load_traffic(dom_name, args.workload, mode, {"k_partial": cfg.F, "k_final": cfg.N})
 
     extras = {}
     if not args.no_extras:
@@ -456,6 +463,7 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern[dom], 3)},
     }
     res.update(extras)
+    res["inputs_sha256"] = inst.digests()
     if not args.no_cpu:
         t_cpu, n = cpu_baseline(inst, args.cpu_budget)
         res["cpu_baseline"] = {"value": round(nb["total"] / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
