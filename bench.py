@@ -158,28 +158,37 @@ def capture(sets, order):
     return g
 
 
-def time_graph_rounds(sets, order, steps, warmup):
-    """Replay graphs so that exactly `steps` rounds are timed."""
+def time_graph_rounds(sets, order, steps, warmup, blocks=5):
+    """Replay graphs so that exactly `steps` rounds are timed, in `blocks`
+    consecutive blocks with an event between blocks; returns the median
+    block's µs per round and the per-block values."""
     import torch
     G = len(order)
     g_full = capture(sets, order)
+    reps = steps // G
     rem = steps % G
     g_rem = capture(sets, order[:rem]) if rem else None
-    reps = steps // G
     for _ in range(max(1, math.ceil(warmup / G))):
         g_full.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    blocks = max(1, min(blocks, reps))
+    # graph replays per block (the remainder rounds go to the last block)
+    per = [reps // blocks + (1 if b < reps % blocks else 0) for b in range(blocks)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
     torch.cuda.synchronize()
-    t0.record()
-    for _ in range(reps):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    t1.record()
+    ev[0].record()
+    for b in range(blocks):
+        for _ in range(per[b]):
+            g_full.replay()
+        if b == blocks - 1 and g_rem is not None:
+            g_rem.replay()
+        ev[b + 1].record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / steps  # us per round
+    us = []
+    for b in range(blocks):
+        rounds = per[b] * G + (rem if b == blocks - 1 else 0)
+        us.append(ev[b].elapsed_time(ev[b + 1]) * 1e3 / rounds)
+    return float(np.median(us)), us
 
 
 def capture_phase(sets, order, phase):
@@ -230,6 +239,48 @@ def time_kernels_live(sets, launches=48, reps=8):
         out[phase] = t0.elapsed_time(t1) * 1e3 / (reps * launches)
         del g
     return out
+
+
+def time_identity_experts(rs, reps=20):
+    """Device µs of the identity experts of one round (every partition's
+    replies y = bf16(x * s_e) over its rows up to the last aligned live row,
+    with the per-row s_e prepared beforehand, as eager torch ops): the
+    stand-in for the caller's FFN, outside the round and reported beside
+    it."""
+    import torch
+    from tests import gpu_harness as h
+    cfg = rs.cfg
+    recs = rs.dispatch_phase()
+    rs.combine_phase(recs)
+    torch.cuda.synchronize()
+    work = []
+    for f, r in enumerate(recs):
+        # the rows an FFN computes: up to the partition's last aligned live row
+        ends = r.ends.cpu().numpy()
+        n = int((int(ends[-1]) + cfg.alpha - 1) // cfg.alpha * cfg.alpha) if len(ends) else 0
+        ex = h.expert_of_rows(ends, f, cfg.E // cfg.F, cfg.alpha, n)
+        s_np = np.where(ex >= 0, np.float32(1.0) + ex.astype(np.float32) / np.float32(cfg.E), np.float32(0.0))
+        work.append((r, n, torch.from_numpy(s_np.astype(np.float32)).cuda()))
+
+    def experts():
+        for r, n, sc in work:
+            if cfg.dtype == "fp8":
+                xv = r.rows.view(torch.uint8)[:n].view(torch.float8_e4m3fn).to(torch.float32) * \
+                    torch.repeat_interleave(r.scales[:n], 128, dim=1)
+            else:
+                xv = r.rows[:n].to(torch.float32)
+            (xv * sc[:, None]).to(torch.bfloat16)
+
+    experts()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        experts()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / reps
 
 
 def launch_floor(G=32, steps=3200):
@@ -307,6 +358,17 @@ def cpu_baseline(inst, budget_s=10.0):
 
 
 # ------------------------------------------------------------------ main ----
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
 
 def kernel_digest():
     """First 16 hex digits of the SHA-256 of the kernel source's code: the
@@ -399,12 +461,14 @@ def main(argv=None):
     G = max(G, S) if S > 1 else G
     G = int(math.ceil(G / S) * S)
     sets = [RoundSet(inst, view, args.combine, args.cached)]
-    hot_us = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
+    hot_us, _ = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
     print(f"[bench] hot: {hot_us:.3f} us/round", file=sys.stderr, flush=True)
     for _ in range(S - 1):
         sets.append(RoundSet(inst, view, args.combine, args.cached))
-    cold_us = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
-    print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round", file=sys.stderr, flush=True)
+    cold_us, cold_blocks = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
+    print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round (median of "
+          f"{len(cold_blocks)} blocks: {', '.join(f'{u:.3f}' for u in cold_blocks)})", file=sys.stderr, flush=True)
+    expert_us = time_identity_experts(sets[0])
 
     kern = time_kernels_live(sets)
     # the roofline kernel: the phase with the most algorithmic bytes among
@@ -453,6 +517,7 @@ def main(argv=None):
                    "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
                    "rounds_per_graph": G, "combine": args.combine, "cached_layout": bool(args.cached)},
         "us_per_round": round(cold_us, 3),
+        "us_per_round_blocks": [round(u, 3) for u in cold_blocks],
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_round_hot": round(hot_us, 3),
         "gbps_hot": round(nb["total"] / (hot_us * 1e-6) / 1e9, 2),
@@ -463,6 +528,7 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern[dom], 3)},
     }
     res.update(extras)
+    res["identity_experts_us"] = round(expert_us, 3)
     res["inputs_sha256"] = inst.digests()
     if not args.no_cpu:
         t_cpu, n = cpu_baseline(inst, args.cpu_budget)
@@ -470,7 +536,7 @@ def main(argv=None):
                                "kind": "oracle",
                                "sample": f"{n} full rounds of {args.workload} (layout+dispatch+combine, "
                                          f"{t_cpu * 1e3:.2f} ms/round, single-threaded C oracle, "
-                                         f"{platform.processor() or platform.machine()})"}
+                                         f"{cpu_model()})"}
     print(json.dumps(res), flush=True)
     return 0
 
