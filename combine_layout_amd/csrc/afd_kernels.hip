@@ -283,9 +283,9 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     __shared__ uint32_t s_live;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
-    int *hist = reinterpret_cast<int *>(lds);   // [E + 1] per expert (+ spare): all | before << 16
+    int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (first: 16-byte aligned)
+    int *hist = sids + ntok * K;                // [E + 1] per expert (+ spare): all | before << 16
     int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
-    int *sids = pfx + E;                        // [ntok * K]
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
@@ -313,10 +313,18 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         const int lo = a.tok_off[q] * K;
         const int n = a.tok_off[q + 1] * K - lo;
         const gptr<const int32_t> src = (gptr<const int32_t>)a.src[q].ids;
-        for (int base = wave * kWave; base < n; base += 256)
-            if (base + lane < n)
-                __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4, 0,
-                                                 0);
+        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(a.src[q].ids) & 15u) == 0) {
+            // 16 bytes per lane: a wavefront moves 256 ids per instruction
+            for (int base = wave * 4 * kWave; base < n; base += 16 * kWave)
+                if (base + 4 * lane < n)
+                    __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + 4 * lane), (lptr<void>)(sids + lo + base),
+                                                     16, 0, 0);
+        } else {
+            for (int base = wave * kWave; base < n; base += 256)
+                if (base + lane < n)
+                    __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4,
+                                                     0, 0);
+        }
     }
     // pointer tables, one per wavefront (lane 0)
     if (lane == 0) {
@@ -428,11 +436,25 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
         const LaneSource src = lane_source(a, g);
         s = src.s;
         t = g - src.off;
-        const gptr<const int32_t> idp = (gptr<const int32_t>)src.ids + int64_t(t) * K;
+        // 16-byte loads when the token's ids are 16-byte aligned (fewer
+        // memory instructions on the layout's critical path)
+        const int32_t *idp = src.ids + int64_t(t) * K;
+        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(idp) & 15u) == 0) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int val = idp[k < K ? k : K - 1];
-            ev[k] = k < K ? val : -1;
+            for (int q = 0; q < KMAX / 4; ++q) {
+                int4 v4 = make_int4(-1, -1, -1, -1);
+                if (4 * q < K) v4 = reinterpret_cast<const int4 *>(idp)[q];
+                ev[4 * q] = v4.x;
+                ev[4 * q + 1] = v4.y;
+                ev[4 * q + 2] = v4.z;
+                ev[4 * q + 3] = v4.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int val = idp[k < K ? k : K - 1];
+                ev[k] = k < K ? val : -1;
+            }
         }
     }
     for (int i = tid; i < NW * (E + 1); i += TILE) mask[i] = 0ull;
@@ -463,12 +485,22 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
         const unsigned long long below = (1ull << lane) - 1ull;
         const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
         int32_t *pk = a.packed + int64_t(g) * K;
+        int vals[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             const bool l = (live >> k) & 1u;
             const int e = l ? ev[k] : 0;
-            const int val = l ? ((e << 16) | (pre[wave * E + e] + __popcll(mrow[e] & below))) : -1;
-            if (k < K) pk[k] = val;
+            vals[k] = l ? ((e << 16) | (pre[wave * E + e] + __popcll(mrow[e] & below))) : -1;
+        }
+        if ((K & 3) == 0) {          // packed is 256-byte aligned, so each token's row is 16-byte aligned
+#pragma unroll
+            for (int q = 0; q < KMAX / 4; ++q)
+                if (4 * q < K)
+                    reinterpret_cast<int4 *>(pk)[q] = make_int4(vals[4 * q], vals[4 * q + 1], vals[4 * q + 2], vals[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (k < K) pk[k] = vals[k];
         }
     }
 }
@@ -505,8 +537,20 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     int cv[PRE];
     {
         const gptr<const int32_t> cp = (gptr<const int32_t>)a.blkcnt + int64_t(tid < E ? tid : 0) * nblk;
+        if ((nblk & 3) == 0) {       // an expert's run of counts is then 16-byte aligned
 #pragma unroll
-        for (int b = 0; b < PRE; ++b) cv[b] = b < nblk ? cp[b] : 0;
+            for (int q = 0; q < PRE / 4; ++q) {
+                u32x4 v4 = u32x4{0u, 0u, 0u, 0u};
+                if (4 * q < nblk) v4 = ((gptr<const u32x4>)cp)[q];
+                cv[4 * q] = int(v4.x);
+                cv[4 * q + 1] = int(v4.y);
+                cv[4 * q + 2] = int(v4.z);
+                cv[4 * q + 3] = int(v4.w);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < PRE; ++b) cv[b] = b < nblk ? cp[b] : 0;
+        }
     }
     u32x4 v[W][VMAX];
     int pk[W];
