@@ -117,3 +117,24 @@ def test_cached_graph_replay_with_inputs_changed():
             want = gen.bf16_bits_to_f32(ref.out[off:off + T]).astype(np.float64)
             assert np.array_equal(got, want), f"replay {rep} source {s}"
             off += T
+
+
+def test_cached_round_reuses_sanitised_layout():
+    """A layout built from ids with invalid routes skips them; a cached round
+    reuses that sanitised layout and reports no new offender."""
+    h = _gpu()
+    from tests.test_gpu_rounds import _inject
+    a = _inject(gen.random_small(970, N=2, F=2, E=16, K=4, alpha=8, T=[37, 50], H=512, p_skip=0.1),
+                np.random.default_rng(3))
+    _, b = _pair(a)
+    cfg = a.cfg
+    lay = oracle.layout(cfg.T, np.concatenate([s.ids for s in a.sources]), cfg.E, cfg.F, cfg.K, cfg.alpha)
+    assert lay.err[0] != 0
+    buf = h.make_buffer(a)
+    h.run_round(a, buf, keep_arrays=False)
+    assert buf.get_error(clear=True) == lay.err
+    g = h.run_round(b, buf, cached=True)
+    hyb = _with_ids(b, a)
+    from tests.test_gpu_parity import check_round
+    assert check_round(hyb, g, oracle.run_round(hyb, rows_cap=g.receive_rows)) == 0
+    assert buf.get_error()[0] == 0

@@ -182,3 +182,37 @@ def test_staged_fp8_codes_at_ties_and_specials():
         o = outs[s].view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(o, ref[off:off + T]), f"source {s} output"
         off += T
+
+
+WIDE_F = [(0, 5, 10, 4, [30, 41]), (1, 8, 64, 32, [20, 0, 33]), (2, 16, 32, 12, [70]), (3, 6, 96, 8, [300, 5])]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", WIDE_F, ids=lambda c: f"F{c[1]}K{c[3]}")
+def test_staged_parity_many_partitions(case, mode):
+    """More than four partitions: stage two requests partials in batches of
+    four after reading the slots; top-k up to 32."""
+    h = _gpu()
+    i, F, E, K, T = case
+    inst = gen.random_small(1000 + i, N=len(T), F=F, E=E, K=K, alpha=4, T=T, H=512, p_skip=0.1,
+                            dtype="fp8" if i % 2 else "bf16", bucket=max(T))
+    print(f"[staged F] F={F} E={E} K={K} T={T} {mode}", flush=True)
+    g = h.run_round(inst, h.make_buffer(inst, combine=mode))
+    check_staged(inst, g, mode)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_staged_with_invalid_routes(mode):
+    """Invalid ids are skipped in both stages: partial rows and outputs equal
+    the oracle's sanitised result, and the first offender is reported."""
+    h = _gpu()
+    from tests.test_gpu_rounds import _inject
+    inst = _inject(gen.random_small(1100, N=2, F=3, E=12, K=4, alpha=4, T=[37, 50], H=512, p_skip=0.1),
+                   np.random.default_rng(11))
+    cfg = inst.cfg
+    lay = oracle.layout(cfg.T, np.concatenate([s.ids for s in inst.sources]), cfg.E, cfg.F, cfg.K, cfg.alpha)
+    assert lay.err[0] != 0
+    buf = h.make_buffer(inst, combine=mode)
+    g = h.run_round(inst, buf)
+    check_staged(inst, g, mode)
+    assert buf.get_error(clear=True) == lay.err
