@@ -106,17 +106,15 @@ WorkspacePlan plan_workspace(const afd_config &c)
     WorkspacePlan w;
     auto a = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t ntok = size_t(c.num_sources) * c.capacity;
-    w.nblk_max = int((ntok + kLayoutTile - 1) / kLayoutTile);
+    // every source starts on a tile boundary of the tiled token space
+    w.nblk_max = int(c.num_sources * ((c.capacity + kLayoutTileMin - 1) / kLayoutTileMin));
     size_t off = 0;
     w.err = off;
-    w.counter = off + 8;
     off += 256;
     w.ends = off;
     off += a(size_t(c.num_experts) * 4);
     w.blkcnt = off;
-    off += a(size_t(w.nblk_max) * c.num_experts * 4);
-    w.blkbase = off;
-    off += a(size_t(w.nblk_max) * c.num_experts * 4);
+    off += a(size_t(align_up(w.nblk_max, 4)) * c.num_experts * 4);
     w.packed = off;
     off += a(ntok * c.topk * 4);
     w.slot = off;
@@ -174,8 +172,8 @@ void build_plan(afd_ctx *c)
     p.ntok = p.tok_off[p.N];
     p.fused = p.ntok <= kFusedMaxTokens && int64_t(p.ntok) * p.K <= kFusedMaxIds && p.E <= kFusedMaxExperts &&
               p.row_bytes / 16 <= kFusedMaxCols;
-    p.tile = kLayoutTile;
-    p.nblk = (p.ntok + p.tile - 1) / p.tile;
+    p.tile = place_sources(c->T, p.N, p.voff);
+    p.nblk = p.fused ? 1 : p.voff[p.N] / p.tile;   // the one-kernel dispatch has no tiles
     if (p.nblk < 1) p.nblk = 1;
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];
     for (int f = 0; f < p.F; ++f) {
@@ -184,10 +182,8 @@ void build_plan(afd_ctx *c)
         p.roww[f] = c->part[f].roww;
     }
     p.err = reinterpret_cast<uint64_t *>(c->ws + c->wp.err);
-    p.counter = reinterpret_cast<uint32_t *>(c->ws + c->wp.counter);
     p.ends = reinterpret_cast<int32_t *>(c->ws + c->wp.ends);
     p.blkcnt = reinterpret_cast<int32_t *>(c->ws + c->wp.blkcnt);
-    p.blkbase = reinterpret_cast<int32_t *>(c->ws + c->wp.blkbase);
     p.packed = reinterpret_cast<int32_t *>(c->ws + c->wp.packed);
     p.slot = reinterpret_cast<int32_t *>(c->ws + c->wp.slot);
     p.partials = g.combine != AFD_COMBINE_ONCE ? reinterpret_cast<uint8_t *>(c->ws + c->wp.partials) : nullptr;

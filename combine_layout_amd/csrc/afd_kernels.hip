@@ -62,6 +62,17 @@ constexpr int kWave = 64;
 
 // 16-byte vector as a native clang vector (keeps register arrays in VGPRs).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+
+// Pointers into global memory.  Accesses through generic pointers become
+// flat instructions, which count on both the vector-memory and the LDS
+// counters: the compiler then waits for every outstanding load before any
+// later use of a flat load, and every LDS wait also waits for flat stores.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+template <typename T>
+using lptr = __attribute__((address_space(3))) T *;
 
 // ---------------------------------------------------------------- args ----
 
@@ -73,26 +84,71 @@ struct SourceArgs {
     const int32_t *ids;      // [T, K]
     const float *scale;      // FP8 only: scale of (t, block b) at t * sst + b * ssg
     int64_t sst, ssg;
-    int64_t off;             // first token of the source in the round's token order
-    int64_t pad;
+    int32_t off;             // first token of the source in the round's token order
+    int32_t T;               // tokens of the source
+    int32_t voff;            // first slot of the source in the tiled token space
+    int32_t pad;
+};
+
+// The scalars of a dispatch, 128 bytes that a kernel reads with two
+// 64-byte scalar loads at entry (read field by field, the compiler fetches
+// each field where it is first used, one dependent round trip at a time).
+struct DispatchHdr {
+    int32_t *blkcnt;         // [E][cpitch] tile counts
+    int32_t *packed;         // [ntok][K] (expert << 16 | rank in tile), -1 skipped
+    int32_t *slot;           // [ntok][K] {part << 24 | row, weight bits}
+    int32_t *ends;           // [E]
+    uint64_t *err;           // sticky route-error word
+    int64_t row_bytes;
+    int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
+    int pad[8];
 };
 
 struct DispatchArgs {
+    DispatchHdr h;
+    int voff[kMaxSources];   // first slot of each source in the tiled token space
     SourceArgs src[kMaxSources];
     uint8_t *rows[kMaxParts];
     float *scales[kMaxParts];
     float *roww[kMaxParts];
     int tok_off[kMaxSources + 1];
-    int N, ntok, K, E, E_loc, alpha, nblk, nvec, G, fp8, tile;
-    int64_t row_bytes;
-    uint64_t *err;
-    uint32_t *counter;
-    int32_t *ends;
-    int32_t *blkcnt;
-    int32_t *blkbase;
-    int32_t *packed;
-    int32_t *slot;
 };
+
+// The header as a kernel holds it: the same fields, global pointers.
+struct Hdr {
+    gptr<int32_t> blkcnt, packed, slot, ends;
+    gptr<unsigned long long> err;
+    int64_t row_bytes;
+    int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
+};
+
+__device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a)
+{
+    static_assert(sizeof(DispatchHdr) == 128, "two 64-byte blocks");
+    const u32x16 r0 = reinterpret_cast<const u32x16 *>(&a.h)[0];
+    const u32x16 r1 = reinterpret_cast<const u32x16 *>(&a.h)[1];
+    auto u64 = [&](int i) { return (uint64_t(r0[i + 1]) << 32) | uint64_t(r0[i]); };
+    Hdr h;
+    h.blkcnt = (gptr<int32_t>)u64(0);
+    h.packed = (gptr<int32_t>)u64(2);
+    h.slot = (gptr<int32_t>)u64(4);
+    h.ends = (gptr<int32_t>)u64(6);
+    h.err = (gptr<unsigned long long>)u64(8);
+    h.row_bytes = int64_t(u64(10));
+    h.N = int(r0[12]);
+    h.ntok = int(r0[13]);
+    h.K = int(r0[14]);
+    h.E = int(r0[15]);
+    h.E_loc = int(r1[0]);
+    h.alpha = int(r1[1]);
+    h.nblk = int(r1[2]);
+    h.cpitch = int(r1[3]);
+    h.nvec = int(r1[4]);
+    h.G = int(r1[5]);
+    h.fp8 = int(r1[6]);
+    h.tile = int(r1[7]);
+    return h;
+}
 
 // Per-stage combine: partial row of (partition f, source s, token t) at
 // partials + ((f * N + s) * capacity + t) * prow.
@@ -121,10 +177,6 @@ struct CombineArgs {
 // vector load per lane, so kernels index them only with wave-uniform values
 // (scalar loads); lanes that need per-lane lookups read small LDS copies.
 
-template <typename T>
-using gptr = __attribute__((address_space(1))) T *;
-template <typename T>
-using lptr = __attribute__((address_space(3))) T *;
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int wave_id() { return uni(threadIdx.x / kWave); }
@@ -141,40 +193,63 @@ __device__ __forceinline__ int src_of_lds(const int *tok_off, int N, int g)
 // whose first token is at or before g (empty sources share their
 // successor's offset).  The offsets are read at constant offsets, with the
 // kernel's first scalar loads.
-template <typename Args>
-__device__ __forceinline__ int source_of(const Args &a, int g)
+__device__ __forceinline__ int source_of(const int (&tok_off)[kMaxSources + 1], int N, int g)
 {
     int s = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxSources; ++q) s += (q < a.N && g >= a.tok_off[q]) ? 1 : 0;
+    for (int q = 1; q < kMaxSources; ++q) s += (q < N && g >= tok_off[q]) ? 1 : 0;
     return uni(s);
 }
 
-// Id pointer and first token of the source of a per-lane token g: per-lane
-// selects over records read at constant offsets (a per-lane index into the
-// kernel arguments would become a dependent vector load per lane).
-struct LaneSource {
+// The record of source s (wave-uniform), read as one 64-byte scalar load:
+// field by field, the compiler fetches each field where it is first used,
+// one dependent scalar round trip at a time.
+struct SourceRec {
+    const uint8_t *x;
+    const float *w;
     const int32_t *ids;
-    int s, off;
+    const float *scale;
+    int64_t sst, ssg;
+    int off, T, voff;
 };
 
-__device__ __forceinline__ LaneSource lane_source(const DispatchArgs &a, int g)
+__device__ __forceinline__ SourceRec load_source(const DispatchArgs &a, int s)
 {
-    LaneSource r{a.src[0].ids, 0, 0};
+    static_assert(sizeof(SourceArgs) == 64, "one record per 64 bytes");
+    const u32x16 r = reinterpret_cast<const u32x16 *>(a.src)[s];
+    auto u64 = [&](int i) { return (uint64_t(r[i + 1]) << 32) | uint64_t(r[i]); };
+    SourceRec o;
+    o.x = reinterpret_cast<const uint8_t *>(u64(0));
+    o.w = reinterpret_cast<const float *>(u64(2));
+    o.ids = reinterpret_cast<const int32_t *>(u64(4));
+    o.scale = reinterpret_cast<const float *>(u64(6));
+    o.sst = int64_t(u64(8));
+    o.ssg = int64_t(u64(10));
+    o.off = int(r[12]);
+    o.T = int(r[13]);
+    o.voff = int(r[14]);
+    return o;
+}
+
+// Source whose span of the tiled token space holds the wave-uniform slot v
+// (sources start on tile boundaries; empty sources have empty spans).
+__device__ __forceinline__ int source_of_tiled(const DispatchArgs &a, int N, int v)
+{
+    const u32x16 vo = *reinterpret_cast<const u32x16 *>(a.voff);
+    int s = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxSources; ++q) {
-        const bool in = q < a.N && g >= a.tok_off[q];
-        r.ids = in ? a.src[q].ids : r.ids;
-        r.s = in ? q : r.s;
-        r.off = in ? a.tok_off[q] : r.off;
-    }
-    return r;
+    for (int q = 1; q < kMaxSources; ++q) s += (q < N && v >= int(vo[q])) ? 1 : 0;
+    return uni(s);
 }
 
 __device__ __forceinline__ uint64_t make_err(int s, int t, int k, unsigned code)
 {
     return (uint64_t(s) << 56) | (uint64_t(uint32_t(t)) << 24) | (uint64_t(k) << 16) | uint64_t(code);
 }
+
+// s_waitcnt immediate that waits for the vector memory counter alone to
+// reach zero (expcnt and lgkmcnt fields at their maximum).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ int align_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
@@ -278,11 +353,12 @@ __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int E,
 template <int VMAX, int KMAX>
 __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 {
+    const Hdr h = load_hdr(a);
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ uint32_t s_live;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
-    const int E = a.E, K = a.K, ntok = a.ntok, G = a.G, N = a.N;
+    const int E = h.E, K = h.K, ntok = h.ntok, G = h.G, N = h.N;
     int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (first: 16-byte aligned)
     int *hist = sids + ntok * K;                // [E + 1] per expert (+ spare): all | before << 16
     int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
@@ -290,25 +366,25 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
     const bool mine = g < ntok;
-    const int s = source_of(a, mine ? g : 0);
+    const int s = source_of(a.tok_off, h.N, mine ? g : 0);
     const SourceArgs &src = a.src[s];
     const int t = g - int(src.off);
 
     // 1. request every load: row, weights, scales, all ids
     u32x4 v[VMAX];
     if (mine) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
-            if (c < a.nvec) v[i] = xs[c];
+            if (c < h.nvec) v[i] = xs[c];
         }
     }
     float wk = 0.0f;
-    if (mine && tid < K) wk = src.w[int64_t(t) * K + tid];
+    if (mine && tid < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + tid];
     float scv = 0.0f;
-    const bool myscale = mine && a.fp8 && tid < G;
-    if (myscale) scv = src.scale[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
+    const bool myscale = mine && h.fp8 && tid < G;
+    if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
     for (int q = 0; q < N; ++q) {
         const int lo = a.tok_off[q] * K;
         const int n = a.tok_off[q + 1] * K - lo;
@@ -358,16 +434,16 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
         for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
         if (gg == g) s_live = live;
     }
-    if (blockIdx.x == 0 && err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
+    if (blockIdx.x == 0 && err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
     // partitions); expert e starts at pfx[e] - pfx[first expert of its part]
-    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hist[e] & 0xFFFF, a.alpha);
+    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hist[e] & 0xFFFF, h.alpha);
     lds_barrier();
     block_exclusive_scan(pfx, E);
     if (blockIdx.x == 0)
-        for (int e = tid; e < E; e += 256) a.ends[e] = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] & 0xFFFF);
+        for (int e = tid; e < E; e += 256) h.ends[e] = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] & 0xFFFF);
     if (!mine) return;
 
     // 4. slot of choice k: lane k of every wavefront computes it (those of
@@ -377,18 +453,18 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     int packed = -1;
     if (lane < K && ((s_live >> lane) & 1u)) {
         const int e = sids[g * K + lane];
-        const int row = pfx[e] - pfx[(e / a.E_loc) * a.E_loc] + (hist[e] >> 16);
-        const int part = e / a.E_loc;
+        const int row = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] >> 16);
+        const int part = e / h.E_loc;
         packed = (part << 24) | row;
-        d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
+        d = s_prow[part] + uint64_t(row) * uint64_t(h.row_bytes);
         ds = s_ps[part] + uint64_t(row) * uint64_t(G) * 4u;
-        if (wave == 0) reinterpret_cast<float *>(s_pw[part])[row] = wk;
+        if (wave == 0) ((gptr<float>)s_pw[part])[row] = wk;
     }
     if (wave == 0 && lane < K) {
-        int2 sl;
+        i32x2 sl;
         sl.x = packed;
         sl.y = __float_as_int(wk);
-        reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
+        ((gptr<i32x2>)h.slot)[int64_t(g) * K + lane] = sl;
     }
 
     // 5. stores: the row to every live slot, and the FP8 scales
@@ -402,7 +478,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = tid + i * 256;
-            if (c < a.nvec) __builtin_nontemporal_store(v[i], &dst[c]);
+            if (c < h.nvec) __builtin_nontemporal_store(v[i], &dst[c]);
         }
         if (myscale) {
             const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
@@ -413,41 +489,44 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 }
 
 // Tile histogram of larger rounds.  Block = NW wavefronts = one tile of
-// 64 * NW tokens, lane = token.  blkcnt[e][tile] = live choices of expert e
-// in the tile; packed[g][k] = (expert << 16) | rank of the choice among the
-// tile's choices of that expert (source, token order), or -1.
+// 64 * NW slots of the tiled token space (all of one source), lane = token.
+// blkcnt[e][tile] = live choices of expert e in the tile; packed[g][k] =
+// (expert << 16) | rank of the choice among the tile's choices of that
+// expert (token order), or -1.  Tiles follow (source, token) order, so
+// adding the counts of earlier tiles ranks a choice within its expert.
 template <int KMAX, int NW>
 __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 {
+    const Hdr h = load_hdr(a);
     extern __shared__ __align__(16) unsigned char lds[];
-    const int E = a.E, K = a.K;
+    const int E = h.E, K = h.K;
     constexpr int TILE = NW * kWave;
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
     int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-    const int g = blockIdx.x * TILE + tid;
-    const bool have = g < a.ntok;
+    // the tile lies in one source's span of the tiled token space
+    const int s = source_of_tiled(a, h.N, blockIdx.x * TILE);
+    const SourceRec src = load_source(a, s);
+    const int t = blockIdx.x * TILE - src.voff + tid;      // the lane's token in source s
+    const bool have = t < src.T;
+    const int g = src.off + t;                             // and in the round's order
 
     int ev[KMAX];
-    int s = 0, t = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) ev[k] = -1;
     if (have) {
-        const LaneSource src = lane_source(a, g);
-        s = src.s;
-        t = g - src.off;
         // 16-byte loads when the token's ids are 16-byte aligned (fewer
         // memory instructions on the layout's critical path)
-        const int32_t *idp = src.ids + int64_t(t) * K;
+        const gptr<const int32_t> idp = (gptr<const int32_t>)src.ids + int64_t(t) * K;
         if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(idp) & 15u) == 0) {
 #pragma unroll
             for (int q = 0; q < KMAX / 4; ++q) {
-                int4 v4 = make_int4(-1, -1, -1, -1);
-                if (4 * q < K) v4 = reinterpret_cast<const int4 *>(idp)[q];
-                ev[4 * q] = v4.x;
-                ev[4 * q + 1] = v4.y;
-                ev[4 * q + 2] = v4.z;
-                ev[4 * q + 3] = v4.w;
+                u32x4 v4 = u32x4{~0u, ~0u, ~0u, ~0u};
+                if (4 * q < K) v4 = ((gptr<const u32x4>)idp)[q];
+                ev[4 * q] = int(v4.x);
+                ev[4 * q + 1] = int(v4.y);
+                ev[4 * q + 2] = int(v4.z);
+                ev[4 * q + 3] = int(v4.w);
             }
         } else {
 #pragma unroll
@@ -463,7 +542,7 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     {
         uint64_t err = kNoError;
         live = classify_token<KMAX>(ev, E, s, t, err);
-        if (err != kNoError) atomicMin(reinterpret_cast<unsigned long long *>(a.err), err);
+        if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // mark the token's lane bit per live expert (others into the spare slot E)
         unsigned long long *mrow = mask + size_t(wave) * (E + 1);
         const unsigned long long bit = 1ull << lane;
@@ -478,13 +557,13 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
             pre[w * E + e] = run;
             run += __popcll(mask[w * (E + 1) + e]);
         }
-        a.blkcnt[e * a.nblk + blockIdx.x] = run;
+        h.blkcnt[e * h.cpitch + blockIdx.x] = run;
     }
     lds_barrier();
     if (have) {
         const unsigned long long below = (1ull << lane) - 1ull;
         const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
-        int32_t *pk = a.packed + int64_t(g) * K;
+        const gptr<int32_t> pk = h.packed + int64_t(g) * K;
         int vals[KMAX];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
@@ -496,7 +575,8 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 #pragma unroll
             for (int q = 0; q < KMAX / 4; ++q)
                 if (4 * q < K)
-                    reinterpret_cast<int4 *>(pk)[q] = make_int4(vals[4 * q], vals[4 * q + 1], vals[4 * q + 2], vals[4 * q + 3]);
+                    ((gptr<u32x4>)pk)[q] = u32x4{uint32_t(vals[4 * q]), uint32_t(vals[4 * q + 1]),
+                                                 uint32_t(vals[4 * q + 2]), uint32_t(vals[4 * q + 3])};
         } else {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
@@ -506,8 +586,9 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 }
 
 // Scatter of larger rounds.  Block = 4 wavefronts; wavefront w handles the
-// W = 8 / VMAX consecutive tokens starting at block_first + w * W (a block's
-// tokens lie in one layout tile).  Every block turns the tile counts into
+// W = 8 / VMAX consecutive slots of the tiled token space starting at
+// block_first + w * W (a block's slots lie in one layout tile, so all its
+// tokens come from one source).  Every block turns the tile counts into
 // this tile's first row per expert itself:
 //   base[e] = start_e + sum of counts of e in earlier tiles,
 //   start_e = aligned prefix of the partition's experts before e,
@@ -517,76 +598,67 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 {
+    const Hdr h = load_hdr(a);
     constexpr int W = VMAX >= 8 ? 1 : 8 / VMAX;
     constexpr int TB = 4 * W;
     constexpr int PRE = 32;                     // tile counts of its expert a thread requests at entry
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
-    const int E = a.E, K = a.K, nvec = a.nvec, ntok = a.ntok, nblk = a.nblk;
+    const int E = h.E, K = h.K, nvec = h.nvec, nblk = h.nblk;
     int *base = reinterpret_cast<int *>(lds);   // [E]
     int *A = base + E;                          // [E]
     int *Cs = A + E;                            // [E]
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
-    const int g_first = blockIdx.x * TB;
-    const int tile = g_first / a.tile;
+    const int v_first = blockIdx.x * TB;        // first slot of the tiled token space
+    const int tile = v_first / h.tile;
+    const SourceRec src = load_source(a, source_of_tiled(a, h.N, v_first));
+    const int T_s = src.T;
+    const int t_first = v_first - src.voff + wave * W;    // source token of the wavefront's first slot
+    const int g_src = src.off;
     const bool pre_all = nblk <= PRE;
 
-    // 1. tile counts first (thread e: expert e's run of nblk counts, one
-    // independent load each), then the rows, ranks and weights of this
-    // wavefront's tokens, so the sums below wait for the counts only
-    int cv[PRE];
+    // 1. tile counts first (thread e: expert e's run of counts, 16 bytes
+    // per load, every load unconditional with an in-bounds index), then the
+    // rows, ranks, weights and scales of this wavefront's tokens.  Nothing
+    // loaded is examined before the sums below, which wait for the counts
+    // alone; the rows stay in flight through the scan.
+    u32x4 cv4[PRE / 4];
     {
-        const gptr<const int32_t> cp = (gptr<const int32_t>)a.blkcnt + int64_t(tid < E ? tid : 0) * nblk;
-        if ((nblk & 3) == 0) {       // an expert's run of counts is then 16-byte aligned
+        const gptr<const u32x4> cp = (gptr<const u32x4>)(h.blkcnt + int64_t(tid < E ? tid : 0) * h.cpitch);
+        const int nq = h.cpitch / 4;
 #pragma unroll
-            for (int q = 0; q < PRE / 4; ++q) {
-                u32x4 v4 = u32x4{0u, 0u, 0u, 0u};
-                if (4 * q < nblk) v4 = ((gptr<const u32x4>)cp)[q];
-                cv[4 * q] = int(v4.x);
-                cv[4 * q + 1] = int(v4.y);
-                cv[4 * q + 2] = int(v4.z);
-                cv[4 * q + 3] = int(v4.w);
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < PRE; ++b) cv[b] = b < nblk ? cp[b] : 0;
-        }
+        for (int q = 0; q < PRE / 4; ++q) cv4[q] = cp[q < nq ? q : 0];
     }
+    // keep the count loads ahead of the row loads: the vector memory
+    // counter completes in issue order, so a row load moved before them
+    // would delay the sums by a cold row fetch
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 v[W][VMAX];
     int pk[W];
     float wk[W];
-    // The wavefront's tokens nearly always share a source: then one record
-    // lookup serves all of them (per-token lookups would each wait on a
-    // scalar load).
-    auto load_token = [&](int j, const SourceArgs &src) {
-        const int gj = g_first + wave * W + j;
-        const int g = gj < ntok ? gj : ntok - 1;
-        const int t = g - int(src.off);
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
-#pragma unroll
-        for (int i = 0; i < VMAX; ++i) {
-            const int c = i * kWave + lane;
-            v[j][i] = xs[c < nvec ? c : 0];
-        }
-        const int kl = lane < K ? lane : 0;
-        pk[j] = a.packed[int64_t(g) * K + kl];
-        wk[j] = src.w[int64_t(t) * K + kl];
-        if (lane >= K || gj >= ntok) pk[j] = -1;
-    };
+    float scv[W];                               // FP8: scale of block `lane` of each token
+    // Slots past the source's last token load that token again (T_s >= 1:
+    // a workgroup lies in a non-empty source's span) and store nothing.
+    // BF16 rounds point the scale load at the token's weights, a valid
+    // address whose value is not used.
     {
-        const int g_lo = g_first + wave * W < ntok ? g_first + wave * W : ntok - 1;
-        const int g_hi = g_first + wave * W + W - 1 < ntok ? g_first + wave * W + W - 1 : ntok - 1;
-        const int s_lo = source_of(a, g_lo);
-        if (s_lo == source_of(a, g_hi)) {
-            const SourceArgs &src = a.src[s_lo];
+        const int kl = lane < K ? lane : 0;
+        const bool fp8 = h.fp8 != 0;
+        const float *sbase = fp8 ? src.scale : src.w;
+        const int64_t sst = fp8 ? src.sst : int64_t(K);
+        const int64_t sgl = fp8 ? int64_t(lane < h.G ? lane : 0) * src.ssg : 0;
 #pragma unroll
-            for (int j = 0; j < W; ++j) load_token(j, src);
-        } else {
+        for (int j = 0; j < W; ++j) {
+            const int t = t_first + j < T_s ? t_first + j : T_s - 1;
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
 #pragma unroll
-            for (int j = 0; j < W; ++j) {
-                const int gj = g_first + wave * W + j;
-                load_token(j, a.src[source_of(a, gj < ntok ? gj : ntok - 1)]);
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = i * kWave + lane;
+                v[j][i] = xs[c < nvec ? c : 0];
             }
+            pk[j] = h.packed[int64_t(g_src + t) * K + kl];
+            wk[j] = ((gptr<const float>)src.w)[int64_t(t) * K + kl];
+            scv[j] = ((gptr<const float>)sbase)[int64_t(t) * sst + sgl];
         }
     }
     if (lane == 0) {
@@ -600,52 +672,67 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         int C = 0, before = 0;
         if (e == tid && pre_all) {
 #pragma unroll
-            for (int b = 0; b < PRE; ++b) {
-                C += cv[b];
-                before += b < tile ? cv[b] : 0;
+            for (int q = 0; q < PRE / 4; ++q) {
+                const int c4[4] = {int(cv4[q].x), int(cv4[q].y), int(cv4[q].z), int(cv4[q].w)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 4 * q + i;
+                    const int c = b < nblk ? c4[i] : 0;
+                    C += c;
+                    before += b < tile ? c : 0;
+                }
             }
         } else {
-            const gptr<const int32_t> cp = (gptr<const int32_t>)a.blkcnt + int64_t(e) * nblk;
+            const gptr<const int32_t> cp = (gptr<const int32_t>)h.blkcnt + int64_t(e) * h.cpitch;
             for (int b = 0; b < nblk; ++b) {
                 const int c = cp[b];
                 C += c;
                 before += b < tile ? c : 0;
             }
         }
-        A[e] = align_up_i(C, a.alpha);
+        A[e] = align_up_i(C, h.alpha);
         Cs[e] = C;
         base[e] = before;
     }
     lds_barrier();
     block_exclusive_scan(A, E);
     for (int e = tid; e < E; e += 256) {
-        const int start = A[e] - A[(e / a.E_loc) * a.E_loc];
+        const int start = A[e] - A[(e / h.E_loc) * h.E_loc];
         base[e] += start;
-        if (blockIdx.x == 0) a.ends[e] = start + Cs[e];
+        if (blockIdx.x == 0) h.ends[e] = start + Cs[e];
     }
     lds_barrier();
+    // Every row, rank, weight and scale of the wavefront's tokens was
+    // requested at entry: wait for all of them here, once.  The vector
+    // memory counter also counts stores on this GPU, so a wait for one of
+    // these loads placed after a token's stores (the compiler cannot count
+    // stores issued in a loop) would also wait for those stores to be
+    // acknowledged, serialising the tokens of a wavefront.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // 3. slots and stores, token by token; lane k owns choice k and the
     // address of its row, which the store loop broadcasts
 #pragma unroll
     for (int j = 0; j < W; ++j) {
-        const int g = g_first + wave * W + j;
-        if (g >= ntok) break;
+        const int t = t_first + j;
+        if (t >= T_s) break;                    // the rest of the wavefront's slots are empty
+        const int g = g_src + t;
         int part = -1, row = -1;
         uint64_t d = 0, ds = 0;
-        if (pk[j] >= 0) {
-            const int e = pk[j] >> 16;
-            row = base[e] + (pk[j] & 0xFFFF);
-            part = e / a.E_loc;
-            d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
-            ds = s_ps[part] + uint64_t(row) * uint64_t(a.G) * 4u;
-            reinterpret_cast<float *>(s_pw[part])[row] = wk[j];
+        const int pkj = lane < K ? pk[j] : -1;
+        if (pkj >= 0) {
+            const int e = pkj >> 16;
+            row = base[e] + (pkj & 0xFFFF);
+            part = e / h.E_loc;
+            d = s_prow[part] + uint64_t(row) * uint64_t(h.row_bytes);
+            ds = s_ps[part] + uint64_t(row) * uint64_t(h.G) * 4u;
+            ((gptr<float>)s_pw[part])[row] = wk[j];
         }
         if (lane < K) {
-            int2 sl;
+            i32x2 sl;
             sl.x = part < 0 ? -1 : ((part << 24) | row);
             sl.y = __float_as_int(wk[j]);
-            reinterpret_cast<int2 *>(a.slot)[int64_t(g) * K + lane] = sl;
+            ((gptr<i32x2>)h.slot)[int64_t(g) * K + lane] = sl;
         }
         const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
         for (int k = 0; k < K; ++k) {
@@ -661,8 +748,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
         }
         // rows longer than 64 * VMAX columns: the remaining columns, chunk by chunk
         if (nvec > kWave * VMAX) {
-            const SourceArgs &src = a.src[source_of(a, g)];
-            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + (g - src.off) * a.row_bytes);
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
             for (int cb = kWave * VMAX; cb < nvec; cb += kWave * VMAX) {
                 u32x4 r[VMAX];
 #pragma unroll
@@ -683,21 +769,32 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
                 }
             }
         }
-        if (a.fp8) {
-            const SourceArgs &src = a.src[source_of(a, g)];
-            const int t = g - int(src.off);
-            const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
-            const int64_t ssg = src.ssg;
-            const int G = a.G;
+        if (h.fp8) {
+            const int G = h.G;
             const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
-            for (int b = lane; b < G; b += kWave) {
-                const float val = sc[int64_t(b) * ssg];
+            if (lane < G) {
                 for (int k = 0; k < K; ++k) {
                     const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
                                         (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
                     if (sk == 0) continue;
-                    ((gptr<float>)sk)[b] = val;
+                    ((gptr<float>)sk)[lane] = scv[j];
                 }
+            }
+            if (G > kWave) {
+                // rows of more than 64 scale blocks (H > 8192): the other
+                // blocks are loaded here, and waited for before leaving, so
+                // that no load is left pending into the next token's stores
+                const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+                for (int b = kWave + lane; b < G; b += kWave) {
+                    const float val = sc[int64_t(b) * src.ssg];
+                    for (int k = 0; k < K; ++k) {
+                        const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                        if (sk == 0) continue;
+                        ((gptr<float>)sk)[b] = val;
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         }
     }
@@ -712,32 +809,35 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
 {
+    const Hdr h = load_hdr(a);
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     const int wpt = lpt / kWave;                          // wavefronts per token
     const int g = blockIdx.x * (256 / lpt) + wave / wpt;
     const int tl = (wave % wpt) * kWave + lane;           // lane within the token
-    const bool have = g < a.ntok;
-    const int K = a.K, nvec = a.nvec;
-    const int s = source_of(a, have ? g : 0);
+    const bool have = g < h.ntok;
+    const int K = h.K, nvec = h.nvec;
+    const int s = source_of(a.tok_off, h.N, have ? g : 0);
     const SourceArgs &src = a.src[s];
     const int t = (have ? g : 0) - int(src.off);
     u32x4 v[VMAX];
-    int2 sl;
+    i32x2 sl;
     sl.x = -1;
     sl.y = 0;
     float wk = 0.0f;
+    float scv = 0.0f;                                     // FP8: scale of block `lane` (first wavefront)
     if (have) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = i * lpt + tl;
             v[i] = xs[c < nvec ? c : 0];
         }
         if (lane < K) {
-            sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * K + lane];
-            wk = src.w[int64_t(t) * K + lane];
+            sl = ((gptr<const i32x2>)h.slot)[int64_t(g) * K + lane];
+            wk = ((gptr<const float>)src.w)[int64_t(t) * K + lane];
         }
+        if (h.fp8 && tl < kWave && tl < h.G) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tl) * src.ssg];
     }
     if (lane == 0) {
         if (wave == 0) table_to_lds(s_prow, a.rows);
@@ -750,11 +850,11 @@ __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
     if (lane < K && sl.x >= 0) {
         const int part = sl.x >> 24;
         const int row = sl.x & 0xFFFFFF;
-        d = s_prow[part] + uint64_t(row) * uint64_t(a.row_bytes);
-        ds = s_ps[part] + uint64_t(row) * uint64_t(a.G) * 4u;
+        d = s_prow[part] + uint64_t(row) * uint64_t(h.row_bytes);
+        ds = s_ps[part] + uint64_t(row) * uint64_t(h.G) * 4u;
         if (tl < kWave) {
-            reinterpret_cast<float *>(s_pw[part])[row] = wk;
-            a.slot[(int64_t(g) * K + lane) * 2 + 1] = __float_as_int(wk);
+            ((gptr<float>)s_pw[part])[row] = wk;
+            h.slot[(int64_t(g) * K + lane) * 2 + 1] = __float_as_int(wk);
         }
     }
     const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
@@ -771,7 +871,7 @@ __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
     }
     // rows longer than lpt * VMAX columns: the remaining columns, chunk by chunk
     if (nvec > lpt * VMAX) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * a.row_bytes);
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
         for (int cb = lpt * VMAX; cb < nvec; cb += lpt * VMAX) {
             u32x4 r[VMAX];
 #pragma unroll
@@ -792,10 +892,19 @@ __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
             }
         }
     }
-    if (a.fp8 && tl < kWave) {
-        const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+    if (h.fp8 && tl < kWave) {
         const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
-        for (int b = lane; b < a.G; b += kWave) {
+        if (lane < h.G) {
+            for (int k = 0; k < K; ++k) {
+                const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                if (sk == 0) continue;
+                ((gptr<float>)sk)[lane] = scv;
+            }
+        }
+        // rows of more than 64 scale blocks (H > 8192): the other blocks
+        const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+        for (int b = kWave + lane; b < h.G; b += kWave) {
             const float val = sc[int64_t(b) * src.ssg];
             for (int k = 0; k < K; ++k) {
                 const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
@@ -836,7 +945,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     if (threadIdx.x == 0) table_to_lds(s_rp, a.reply);
     __syncthreads();
     if (!live_wave) return;
-    const int s = source_of(a, g);
+    const int s = source_of(a.tok_off, a.N, g);
     const int t = g - a.tok_off[s];
     const int nvec = a.nvec;
     const int c0 = seg * kWave * VPL + lane;
@@ -953,7 +1062,7 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
     if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
     const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
     if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
-    const int s = source_of(a, g);
+    const int s = source_of(a.tok_off, a.N, g);
     const int t = g - a.tok_off[s];
     const int nvec = a.nvec;
     const int c = seg * kWave + lane;
@@ -1196,6 +1305,8 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
         r.sst = p.sst[s];
         r.ssg = p.ssg[s];
         r.off = p.tok_off[s];
+        r.T = p.tok_off[s + 1] - p.tok_off[s];
+        r.voff = p.voff[s];
     }
     for (int f = 0; f < p.F; ++f) {
         a.rows[f] = static_cast<uint8_t *>(p.rows[f]);
@@ -1203,25 +1314,25 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
         a.roww[f] = p.roww[f];
     }
     for (int s = 0; s <= p.N; ++s) a.tok_off[s] = p.tok_off[s];
-    a.N = p.N;
-    a.ntok = p.ntok;
-    a.K = p.K;
-    a.E = p.E;
-    a.E_loc = p.E_loc;
-    a.alpha = p.alpha;
-    a.nblk = p.nblk;
-    a.tile = p.tile;
-    a.nvec = int(p.row_bytes / 16);
-    a.G = p.G;
-    a.fp8 = p.fp8;
-    a.row_bytes = p.row_bytes;
-    a.err = p.err;
-    a.counter = p.counter;
-    a.ends = p.ends;
-    a.blkcnt = p.blkcnt;
-    a.blkbase = p.blkbase;
-    a.packed = p.packed;
-    a.slot = p.slot;
+    for (int s = 0; s < p.N; ++s) a.voff[s] = p.voff[s];
+    a.h.N = p.N;
+    a.h.ntok = p.ntok;
+    a.h.K = p.K;
+    a.h.E = p.E;
+    a.h.E_loc = p.E_loc;
+    a.h.alpha = p.alpha;
+    a.h.nblk = p.nblk;
+    a.h.cpitch = (p.nblk + 3) / 4 * 4;
+    a.h.tile = p.tile;
+    a.h.nvec = int(p.row_bytes / 16);
+    a.h.G = p.G;
+    a.h.fp8 = p.fp8;
+    a.h.row_bytes = p.row_bytes;
+    a.h.err = p.err;
+    a.h.ends = p.ends;
+    a.h.blkcnt = p.blkcnt;
+    a.h.packed = p.packed;
+    a.h.slot = p.slot;
     return a;
 }
 
@@ -1248,16 +1359,18 @@ template <int VMAX>
 int launch_cached_v(const DispatchArgs &a, int lpt, hipStream_t st)
 {
     const int tpb = 256 / lpt;
-    hipLaunchKernelGGL(k_scatter_cached<VMAX>, dim3((a.ntok + tpb - 1) / tpb), dim3(256), 0, st, a, lpt);
+    hipLaunchKernelGGL(k_scatter_cached<VMAX>, dim3((a.h.ntok + tpb - 1) / tpb), dim3(256), 0, st, a, lpt);
     return launched_ok();
 }
 
+// One workgroup per TB slots of the tiled token space (TB divides every
+// tile size, and the slots are a whole number of tiles).
 template <int VMAX>
-int launch_scatter_v(const DispatchArgs &a, int ntok, int E, hipStream_t st)
+int launch_scatter_v(const DispatchArgs &a, int nslots, int E, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
     const size_t lds = size_t(E) * 12;
-    hipLaunchKernelGGL(k_scatter<VMAX>, dim3((ntok + TB - 1) / TB), dim3(256), lds, st, a);
+    hipLaunchKernelGGL(k_scatter<VMAX>, dim3(nslots / TB), dim3(256), lds, st, a);
     return launched_ok();
 }
 
@@ -1286,7 +1399,7 @@ int be_init_workspace(void *workspace, const WorkspacePlan &wp)
 {
     uint64_t hdr[32];
     std::memset(hdr, 0, sizeof(hdr));
-    hdr[wp.err / 8] = kNoError;  // counter (at byte 8) stays 0
+    hdr[wp.err / 8] = kNoError;
     if (hipMemcpy(workspace, hdr, sizeof(hdr), hipMemcpyHostToDevice) != hipSuccess) return 1;
     return 0;
 }
@@ -1304,12 +1417,12 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     hipStream_t st = static_cast<hipStream_t>(stream);
     const DispatchArgs a = make_dispatch_args(p);
     const bool k32 = p.K > 8;
-    const int vm = vmax_for(a.nvec);
+    const int vm = vmax_for(a.h.nvec);
     if (p.cached) {
         if (p.ntok == 0) return 0;
         // lanes per token: the row's columns rounded up to 64, 128 or 256
-        const int lpt = a.nvec <= 64 ? 64 : a.nvec <= 128 ? 128 : 256;
-        const int per = (a.nvec + lpt - 1) / lpt;
+        const int lpt = a.h.nvec <= 64 ? 64 : a.h.nvec <= 128 ? 128 : 256;
+        const int per = (a.h.nvec + lpt - 1) / lpt;
         switch (per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8) {
         case 1: return launch_cached_v<1>(a, lpt, st);
         case 2: return launch_cached_v<2>(a, lpt, st);
@@ -1319,7 +1432,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     }
     if (p.fused) {
         // one block per token; 256 threads hold the row, VMAX columns each
-        const int per = (a.nvec + 255) / 256;
+        const int per = (a.h.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
         const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4;
         dim3 grid(p.ntok > 0 ? p.ntok : 1);
@@ -1331,16 +1444,27 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         }
     }
     {
-        const size_t lds = size_t(4) * (p.E + 1) * 8 + size_t(4) * p.E * 4;
-        if (k32) hipLaunchKernelGGL((k_layout<32, 4>), dim3(p.nblk), dim3(256), lds, st, a);
-        else hipLaunchKernelGGL((k_layout<8, 4>), dim3(p.nblk), dim3(256), lds, st, a);
+        // one workgroup per tile of 64, 128 or 256 tokens, one lane per token
+        const int nw = p.tile / kWave;
+        const size_t lds = size_t(nw) * (p.E + 1) * 8 + size_t(nw) * p.E * 4;
+        const dim3 grid(p.nblk), blk(p.tile);
+        if (nw == 1) {
+            if (k32) hipLaunchKernelGGL((k_layout<32, 1>), grid, blk, lds, st, a);
+            else hipLaunchKernelGGL((k_layout<8, 1>), grid, blk, lds, st, a);
+        } else if (nw == 2) {
+            if (k32) hipLaunchKernelGGL((k_layout<32, 2>), grid, blk, lds, st, a);
+            else hipLaunchKernelGGL((k_layout<8, 2>), grid, blk, lds, st, a);
+        } else {
+            if (k32) hipLaunchKernelGGL((k_layout<32, 4>), grid, blk, lds, st, a);
+            else hipLaunchKernelGGL((k_layout<8, 4>), grid, blk, lds, st, a);
+        }
     }
     if (launched_ok()) return 1;
     switch (vm) {
-    case 1: return launch_scatter_v<1>(a, p.ntok, p.E, st);
-    case 2: return launch_scatter_v<2>(a, p.ntok, p.E, st);
-    case 4: return launch_scatter_v<4>(a, p.ntok, p.E, st);
-    default: return launch_scatter_v<8>(a, p.ntok, p.E, st);
+    case 1: return launch_scatter_v<1>(a, p.voff[p.N], p.E, st);
+    case 2: return launch_scatter_v<2>(a, p.voff[p.N], p.E, st);
+    case 4: return launch_scatter_v<4>(a, p.voff[p.N], p.E, st);
+    default: return launch_scatter_v<8>(a, p.voff[p.N], p.E, st);
     }
 }
 

@@ -15,9 +15,14 @@ constexpr int kMaxParts = AFD_MAX_PARTITIONS;
 constexpr int kMaxExperts = AFD_MAX_EXPERTS;
 constexpr int kMaxTopk = AFD_MAX_TOPK;
 
-// Tokens handled by one workgroup of the layout kernel (4 wavefronts of 64
-// lanes, one token per lane; a wavefront's 64 tokens form one chunk).
+// Tokens handled by one workgroup of the layout kernel: 1, 2 or 4
+// wavefronts of 64 lanes, one token per lane (a wavefront's 64 tokens form
+// one chunk).
+constexpr int kLayoutTileMin = 64;
 constexpr int kLayoutTile = 256;
+// Tile counts of an expert the scatter requests at entry (beyond this many
+// tiles it sums them in a loop).
+constexpr int kLayoutMaxTiles = 32;
 // Small rounds rebuild the layout inside every scatter workgroup (one kernel
 // for the whole dispatch): at most this many tokens, ids (staged in LDS) and
 // experts, and rows of at most this many 16-byte columns.
@@ -32,6 +37,22 @@ constexpr uint64_t kNoError = ~0ull;
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+// Larger rounds place every source on a tile boundary of a "tiled" token
+// space: source s occupies slots [voff[s], voff[s] + T[s]), and the slots up
+// to the next boundary are empty.  Every layout tile, and every scatter
+// workgroup inside it, then holds the tokens of a single source, whose
+// record a kernel reads once.  The tile is the smallest of 64, 128 and 256
+// tokens that keeps the round within kLayoutMaxTiles tiles, so mid-size
+// rounds spread their layout over more workgroups.  Returns the tile.
+inline int place_sources(const int *T, int N, int *voff)
+{
+    for (int tile = kLayoutTileMin;; tile *= 2) {
+        voff[0] = 0;
+        for (int s = 0; s < N; ++s) voff[s + 1] = voff[s] + int(align_up(T[s], tile));
+        if (tile == kLayoutTile || voff[N] / tile <= kLayoutMaxTiles) return tile;
+    }
+}
+
 // Bytes of one stage-one row of the per-stage combine: BF16 [H], or H E4M3
 // codes followed by H/128 scale bytes, padded to a multiple of 32.
 inline int64_t partial_row_bytes(int combine, int H)
@@ -42,10 +63,9 @@ inline int64_t partial_row_bytes(int combine, int H)
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
     size_t err = 0;        // uint64 sticky route-error word
-    size_t counter = 0;    // uint32 arrival counter of the layout kernel
     size_t ends = 0;       // int32 [E]
-    size_t blkcnt = 0;     // int32 [E][nblk] live choices per layout tile (expert-major)
-    size_t blkbase = 0;    // int32 [nblk_max][E] first row of each tile's run
+    size_t blkcnt = 0;     // int32 [E][pitch] live choices per layout tile (expert-major;
+                           // pitch = tiles rounded up to 4)
     size_t packed = 0;     // int32 [N*capacity*K] (expert << 16 | rank in tile), -1 skipped
     size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
@@ -70,6 +90,7 @@ struct RoundPlan {
     bool cached = false;     // scatter from the slot map of the last layout
     int nblk = 0;            // layout tiles (split path)
     int tile = 0;            // tokens per layout tile
+    int voff[kMaxSources + 1] = {};   // first tiled slot of each source (voff[N]: slots)
     // per source
     const void *x[kMaxSources] = {};
     const int32_t *ids[kMaxSources] = {};
@@ -84,10 +105,8 @@ struct RoundPlan {
     const void *reply[kMaxParts] = {};
     // workspace
     uint64_t *err = nullptr;
-    uint32_t *counter = nullptr;
     int32_t *ends = nullptr;
     int32_t *blkcnt = nullptr;
-    int32_t *blkbase = nullptr;
     int32_t *packed = nullptr;
     int32_t *slot = nullptr;
     // per-stage combine: row (f, s, t) at partials + ((f * N + s) * capacity + t) * prow

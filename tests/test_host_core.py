@@ -381,27 +381,28 @@ def test_single_partition_view_and_copy(lib):
 
 
 def test_split_path_above_fused_limits(lib):
-    # above 512 tokens: tiled layout (256-token tiles)
+    # above 512 tokens: tiled layout (the smallest of 64/128/256-token tiles
+    # that keeps a round within 32 tiles)
     c = cfg(N=2, F=2, E=8, K=2, cap=2048)
     x = Ctx(lib, c)
     lib.afd_fake_log_clear()
     assert x.dispatch(0, 300) == 0 and x.dispatch(1, 1000) == 0
     assert x.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=1300 nblk=6 T=300,1000"]
+    assert log(lib) == ["dispatch fused=0 ntok=1300 nblk=21 T=300,1000"]
     x.destroy()
     # more than 4096 ids
     y = Ctx(lib, cfg(N=1, F=2, E=32, K=16, cap=2048))
     lib.afd_fake_log_clear()
     assert y.dispatch(0, 300) == 0
     assert y.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=2 T=300"]
+    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=5 T=300"]
     y.destroy()
     # more than 256 experts
     z = Ctx(lib, cfg(N=1, F=2, E=512, K=4, cap=2048))
     lib.afd_fake_log_clear()
     assert z.dispatch(0, 600) == 0
     assert z.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=3 T=600"]
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600"]
     z.destroy()
     # many tiles and 16 KB rows
     u = Ctx(lib, cfg(N=2, F=2, E=8, K=2, cap=8192))
@@ -414,7 +415,7 @@ def test_split_path_above_fused_limits(lib):
     lib.afd_fake_log_clear()
     assert v.dispatch(0, 600) == 0
     assert v.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=3 T=600"]
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600"]
     v.destroy()
 
 
