@@ -313,25 +313,37 @@ __device__ __forceinline__ void table_to_lds(uint64_t *dst, T *const (&arr)[M])
 // Route rule of the contract page for one token's ids ev[0..KMAX), where
 // entries past K hold -1: -1 skips; other negatives, ids >= E and repeats of
 // an earlier valid id are errors and are skipped too.  Returns the bit set
-// of live choices and records the first error (lowest k) of the token in
-// `err`.  Branch-free: repeats are found by comparing with the earlier ids in
-// registers, and every decision is a select.
+// of live choices; a token that breaks the rule also records its first error
+// (lowest k) in `err`.  Repeats are found by comparing with the earlier ids
+// in registers.  The common case (every id valid or -1) is compares and
+// selects only; the error word is built only for a lane that needs it.
 template <int KMAX>
 __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int E, int s, int t, uint64_t &err)
 {
     uint32_t live = 0;
+    bool bad = false;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int e = ev[k];
-        const bool valid = e >= 0 && e < E;
         bool dup = false;
 #pragma unroll
         for (int j = 0; j < k; ++j) dup |= ev[j] == e;
-        const unsigned code =
-            e < -1 ? unsigned(AFD_ROUTE_NEG) : e >= E ? unsigned(AFD_ROUTE_RANGE) : (valid && dup) ? unsigned(AFD_ROUTE_DUP) : 0u;
-        live |= (valid && !dup) ? (1u << k) : 0u;
-        const uint64_t cand = make_err(s, t, k, code);
-        err = (code != 0 && err == kNoError) ? cand : err;
+        const bool ok = uint32_t(e) < uint32_t(E) && !dup;
+        live |= ok ? (1u << k) : 0u;
+        bad |= !ok && e != -1;
+    }
+    if (bad) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int e = ev[k];
+            bool dup = false;
+#pragma unroll
+            for (int j = 0; j < k; ++j) dup |= ev[j] == e;
+            const unsigned code = e < -1 ? unsigned(AFD_ROUTE_NEG)
+                                  : e >= E ? unsigned(AFD_ROUTE_RANGE)
+                                  : (e >= 0 && dup) ? unsigned(AFD_ROUTE_DUP) : 0u;
+            if (code != 0 && err == kNoError) err = make_err(s, t, k, code);
+        }
     }
     return live;
 }
@@ -418,10 +430,22 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     uint64_t err = kNoError;
     for (int gg = tid; gg < ntok; gg += 256) {
         int ev[KMAX];
+        if ((K & 3) == 0) {         // a token's ids are then 16-byte aligned in LDS
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const int val = sids[gg * K + (k < K ? k : K - 1)];
-            ev[k] = k < K ? val : -1;
+            for (int q = 0; q < KMAX / 4; ++q) {
+                u32x4 v4 = u32x4{~0u, ~0u, ~0u, ~0u};
+                if (4 * q < K) v4 = reinterpret_cast<const u32x4 *>(sids + gg * K)[q];
+                ev[4 * q] = int(v4.x);
+                ev[4 * q + 1] = int(v4.y);
+                ev[4 * q + 2] = int(v4.z);
+                ev[4 * q + 3] = int(v4.w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int val = sids[gg * K + (k < K ? k : K - 1)];
+                ev[k] = k < K ? val : -1;
+            }
         }
         int ss = 0, tt = 0;
         if (blockIdx.x == 0) {
