@@ -610,10 +610,11 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 }
 
 // Scatter of larger rounds.  Block = 4 wavefronts; wavefront w handles the
-// W = 8 / VMAX consecutive slots of the tiled token space starting at
-// block_first + w * W (a block's slots lie in one layout tile, so all its
-// tokens come from one source).  Every block turns the tile counts into
-// this tile's first row per expert itself:
+// W = 4 / VMAX (at least 1) consecutive slots of the tiled token space
+// starting at block_first + w * W (a block's slots lie in one layout tile,
+// so all its tokens come from one source).  Small blocks put several on
+// each CU, which keeps more stores in flight per CU.  Every block turns the
+// tile counts into this tile's first row per expert itself:
 //   base[e] = start_e + sum of counts of e in earlier tiles,
 //   start_e = aligned prefix of the partition's experts before e,
 // which needs no communication between blocks.  The tile counts are
@@ -623,7 +624,7 @@ template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 {
     const Hdr h = load_hdr(a);
-    constexpr int W = VMAX >= 8 ? 1 : 8 / VMAX;
+    constexpr int W = VMAX >= 4 ? 1 : 4 / VMAX;     // tokens per wavefront (1 KB .. 4 KB of row per lane set)
     constexpr int TB = 4 * W;
     constexpr int PRE = 32;                     // tile counts of its expert a thread requests at entry
     extern __shared__ __align__(16) unsigned char lds[];
@@ -1392,7 +1393,7 @@ int launch_cached_v(const DispatchArgs &a, int lpt, hipStream_t st)
 template <int VMAX>
 int launch_scatter_v(const DispatchArgs &a, int nslots, int E, hipStream_t st)
 {
-    constexpr int TB = 4 * (VMAX >= 8 ? 1 : 8 / VMAX);
+    constexpr int TB = 4 * (VMAX >= 4 ? 1 : 4 / VMAX);
     const size_t lds = size_t(E) * 12;
     hipLaunchKernelGGL(k_scatter<VMAX>, dim3(nslots / TB), dim3(256), lds, st, a);
     return launched_ok();
