@@ -379,8 +379,8 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const int g = blockIdx.x;
     const bool mine = g < ntok;
     const int s = source_of(a.tok_off, h.N, mine ? g : 0);
-    const SourceArgs &src = a.src[s];
-    const int t = g - int(src.off);
+    const SourceRec src = load_source(a, s);
+    const int t = g - src.off;
 
     // 1. request every load: row, weights, scales, all ids
     u32x4 v[VMAX];
@@ -398,10 +398,11 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const bool myscale = mine && h.fp8 && tid < G;
     if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
     for (int q = 0; q < N; ++q) {
-        const int lo = a.tok_off[q] * K;
-        const int n = a.tok_off[q + 1] * K - lo;
-        const gptr<const int32_t> src = (gptr<const int32_t>)a.src[q].ids;
-        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(a.src[q].ids) & 15u) == 0) {
+        const SourceRec rq = load_source(a, q);
+        const int lo = rq.off * K;
+        const int n = rq.T * K;
+        const gptr<const int32_t> src = (gptr<const int32_t>)rq.ids;
+        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(rq.ids) & 15u) == 0) {
             // 16 bytes per lane: a wavefront moves 256 ids per instruction
             for (int base = wave * 4 * kWave; base < n; base += 16 * kWave)
                 if (base + 4 * lane < n)
@@ -462,10 +463,27 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     lds_barrier();
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
-    // partitions); expert e starts at pfx[e] - pfx[first expert of its part]
-    for (int e = tid; e < E; e += 256) pfx[e] = align_up_i(hist[e] & 0xFFFF, h.alpha);
+    // partitions); expert e starts at pfx[e] - pfx[first expert of its part].
+    // Wavefront 0 aligns and scans in one pass (E <= 256: at most 4 experts
+    // per lane), then one barrier.
+    if (tid < kWave) {
+        const int per = (E + kWave - 1) / kWave;
+        const int lo = lane * per;
+        int c[4];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = i < per && lo + i < E ? align_up_i(hist[lo + i] & 0xFFFF, h.alpha) : 0;
+            sum += c[i];
+        }
+        int run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < per && lo + i < E) pfx[lo + i] = run;
+            run += c[i];
+        }
+    }
     lds_barrier();
-    block_exclusive_scan(pfx, E);
     if (blockIdx.x == 0)
         for (int e = tid; e < E; e += 256) h.ends[e] = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] & 0xFFFF);
     if (!mine) return;
