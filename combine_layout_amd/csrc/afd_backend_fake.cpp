@@ -53,10 +53,19 @@ int be_launch_dispatch(const RoundPlan &p, void *)
         snprintf(b, sizeof(b), "%s%d", s ? "," : "", p.tok_off[s + 1] - p.tok_off[s]);
         srcs += b;
     }
-    if (p.cached)
+    if (p.cached) {
         logf("dispatch cached ntok=%d T=%s", p.ntok, srcs.c_str());
-    else
-        logf("dispatch fused=%d ntok=%d nblk=%d T=%s", p.fused ? 1 : 0, p.ntok, p.nblk, srcs.c_str());
+    } else if (p.fused) {
+        logf("dispatch fused=1 ntok=%d nblk=%d T=%s", p.ntok, p.nblk, srcs.c_str());
+    } else {
+        std::string vo;
+        for (int s = 0; s <= p.N; ++s) {
+            char b[32];
+            snprintf(b, sizeof(b), "%s%d", s ? "," : "", p.voff[s]);
+            vo += b;
+        }
+        logf("dispatch fused=0 ntok=%d nblk=%d T=%s tile=%d voff=%s", p.ntok, p.nblk, srcs.c_str(), p.tile, vo.c_str());
+    }
     return g_fail;
 }
 

@@ -388,35 +388,54 @@ def test_split_path_above_fused_limits(lib):
     lib.afd_fake_log_clear()
     assert x.dispatch(0, 300) == 0 and x.dispatch(1, 1000) == 0
     assert x.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=1300 nblk=21 T=300,1000"]
+    assert log(lib) == ["dispatch fused=0 ntok=1300 nblk=21 T=300,1000 tile=64 voff=0,320,1344"]
     x.destroy()
     # more than 4096 ids
     y = Ctx(lib, cfg(N=1, F=2, E=32, K=16, cap=2048))
     lib.afd_fake_log_clear()
     assert y.dispatch(0, 300) == 0
     assert y.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=5 T=300"]
+    assert log(lib) == ["dispatch fused=0 ntok=300 nblk=5 T=300 tile=64 voff=0,320"]
     y.destroy()
     # more than 256 experts
     z = Ctx(lib, cfg(N=1, F=2, E=512, K=4, cap=2048))
     lib.afd_fake_log_clear()
     assert z.dispatch(0, 600) == 0
     assert z.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600"]
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600 tile=64 voff=0,640"]
     z.destroy()
     # many tiles and 16 KB rows
     u = Ctx(lib, cfg(N=2, F=2, E=8, K=2, cap=8192))
     lib.afd_fake_log_clear()
     assert u.dispatch(0, 5000) == 0 and u.dispatch(1, 4000) == 0
     assert u.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=9000 nblk=36 T=5000,4000"]
+    assert log(lib) == ["dispatch fused=0 ntok=9000 nblk=36 T=5000,4000 tile=256 voff=0,5120,9216"]
     u.destroy()
     v = Ctx(lib, cfg(N=1, F=2, E=8, K=2, H=8192, cap=2048))
     lib.afd_fake_log_clear()
     assert v.dispatch(0, 600) == 0
     assert v.receive(0)[0] == 0
-    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600"]
+    assert log(lib) == ["dispatch fused=0 ntok=600 nblk=10 T=600 tile=64 voff=0,640"]
     v.destroy()
+
+
+def test_split_path_sources_start_on_tile_boundaries(lib):
+    # every source starts on a tile boundary of the tiled token space, empty
+    # sources take no space, and the tile grows until the round fits 32 tiles
+    x = Ctx(lib, cfg(N=3, F=2, E=8, K=2, cap=4096))
+    lib.afd_fake_log_clear()
+    assert x.dispatch(0, 65) == 0 and x.dispatch(1, 0) == 0 and x.dispatch(2, 500) == 0
+    assert x.receive(0)[0] == 0
+    # 65 -> two 64-slot tiles, 0 -> none, 500 -> eight: 10 tiles (9 without the padding)
+    assert log(lib) == ["dispatch fused=0 ntok=565 nblk=10 T=65,0,500 tile=64 voff=0,128,128,640"]
+    x.destroy()
+    y = Ctx(lib, cfg(N=3, F=2, E=8, K=2, cap=4096))
+    lib.afd_fake_log_clear()
+    assert y.dispatch(0, 1) == 0 and y.dispatch(1, 2100) == 0 and y.dispatch(2, 1) == 0
+    assert y.receive(0)[0] == 0
+    # 64-slot tiles would need 1 + 33 + 1 = 35 tiles; 128-slot tiles: 1 + 17 + 1 = 19
+    assert log(lib) == ["dispatch fused=0 ntok=2102 nblk=19 T=1,2100,1 tile=128 voff=0,128,2304,2432"]
+    y.destroy()
 
 
 def test_hip_failure_leaves_state(lib):
