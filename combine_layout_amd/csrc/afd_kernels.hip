@@ -16,15 +16,17 @@
 // Kernels
 //   k_fused   dispatch for small rounds (<= kFusedMaxTokens tokens): every
 //             workgroup rebuilds the whole layout in LDS from the ids, then
-//             scatters its own four tokens.  One launch for the dispatch.
-//   k_layout  dispatch, larger rounds, step 1: 256-token tiles; per 64-token
-//             chunk an LDS bit mask per expert gives each choice its rank
-//             (popcount of the lanes below it); writes each tile's count per
-//             expert and every choice's rank inside its tile.
+//             scatters its own token.  One launch for the dispatch.
+//   k_layout  dispatch, larger rounds, step 1: tiles of 64, 128 or 256
+//             slots of a tiled token space in which every source starts on
+//             a tile boundary; per 64-token chunk an LDS bit mask per expert
+//             gives each choice its rank (popcount of the lanes below it);
+//             writes each tile's count per expert and every choice's rank
+//             inside its tile.
 //   k_scatter dispatch, step 2: every workgroup sums the tile counts into
-//             its tile's first row per expert (and ends[]), then one
-//             wavefront per token copies the row once from HBM into
-//             registers and stores it to each live slot.
+//             its tile's first row per expert (and ends[]), then each
+//             wavefront copies its tokens' rows once from HBM into registers
+//             and stores them to each live slot.
 //   k_combine one wavefront per (token, column segment): gathers the live
 //             reply rows with 16-byte loads, float32 multiply-then-add in
 //             ascending k, rounds once to bfloat16.
