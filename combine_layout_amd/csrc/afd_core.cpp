@@ -118,7 +118,7 @@ WorkspacePlan plan_workspace(const afd_config &c)
     w.packed = off;
     off += a(ntok * c.topk * 4);
     w.slot = off;
-    off += a(ntok * c.topk * 8);
+    off += a(ntok * c.topk * 8 + 64);   // + slack for the combine's 64-byte slot reads
     w.inbox = off;
     if (c.num_partitions == 1) off += a(ntok * c.hidden * 2);
     w.partials = off;

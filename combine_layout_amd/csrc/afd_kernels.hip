@@ -27,9 +27,10 @@
 //             its tile's first row per expert (and ends[]), then each
 //             wavefront copies its tokens' rows once from HBM into registers
 //             and stores them to each live slot.
-//   k_combine one wavefront per (token, column segment): gathers the live
-//             reply rows with 16-byte loads, float32 multiply-then-add in
-//             ascending k, rounds once to bfloat16.
+//   k_combine one wavefront per (token, column segment): reads the token's
+//             slots with scalar loads, gathers the live reply rows with
+//             16-byte loads, float32 multiply-then-add in ascending k,
+//             rounds once to bfloat16.
 //   k_copy    inbox -> caller output (single-partition collect without view).
 //   k_scatter_cached  dispatch of a round that reuses the last layout: the
 //             slot map already holds every live choice's partition and row,
@@ -164,12 +165,15 @@ struct StageArgs {
     int N, F, ntok, K, H, nvec, nseg, capacity, f, s, T;
 };
 
+// The combine's scalars fill the first 64 bytes and the token offsets start
+// at byte 64, so a wavefront reads each with one 64-byte scalar load.
 struct CombineArgs {
+    const int32_t *slot;     // [ntok][K] {part << 24 | row, weight bits}, 64 bytes of slack at the end
+    int N, ntok, K, H, nvec, nseg;
+    int pad[8];
+    int tok_off[kMaxSources + 1];
     const uint16_t *reply[kMaxParts];
     uint16_t *out[kMaxSources];
-    int tok_off[kMaxSources + 1];
-    int N, ntok, K, H, nvec, nseg;
-    const int32_t *slot;
 };
 
 // ------------------------------------------------------------- helpers ----
@@ -970,46 +974,63 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 }
 
 // Combine: one wavefront per (token, segment of 64*VPL 16-byte columns).
-// Lane k < K loads the token's slot k and forms the address of its reply
-// row; the wavefront then issues every live row's loads before it
+// The token's slots arrive as wave-uniform values, one 64-byte scalar load
+// per eight choices (the slot map does not change during the kernel); the
+// partition bases are looked up in the kernel arguments with the choices'
+// partition numbers, all eight requested before one wait.  The chain
+// before the row loads is three scalar round trips: arguments, slots,
+// bases.  The wavefront then issues every live row's loads before it
 // accumulates, in ascending k, with a float32 multiply and a separate add.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
 #pragma clang fp contract(off)
-    __shared__ uint64_t s_rp[kMaxParts];
+    static_assert(offsetof(CombineArgs, pad) + sizeof(int) * 8 == 64, "scalars in the first 64 bytes");
+    static_assert(offsetof(CombineArgs, tok_off) == 64, "offsets at byte 64");
+    const u32x16 hv = *reinterpret_cast<const u32x16 *>(&a);
+    const int32_t *slot = reinterpret_cast<const int32_t *>((uint64_t(hv[1]) << 32) | uint64_t(hv[0]));
+    const int N = int(hv[2]), ntok = int(hv[3]), K = int(hv[4]), H = int(hv[5]), nvec = int(hv[6]), nseg = int(hv[7]);
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / a.nseg;
-    const int seg = gw - g * a.nseg;
-    const bool live_wave = g < a.ntok;
-    int2 sl;
-    sl.x = -1;
-    sl.y = 0;
-    if (live_wave && lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
-    if (threadIdx.x == 0) table_to_lds(s_rp, a.reply);
-    __syncthreads();
-    if (!live_wave) return;
-    const int s = source_of(a.tok_off, a.N, g);
-    const int t = g - a.tok_off[s];
-    const int nvec = a.nvec;
+    const int g = gw / nseg;
+    const int seg = gw - g * nseg;
+    if (g >= ntok) return;
+    // source of g and its first token (offsets are nondecreasing; empty
+    // sources share their successor's offset)
+    const u32x16 to = *reinterpret_cast<const u32x16 *>(a.tok_off);
+    int s = 0, t0 = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxSources; ++q)
+        if (q < N && g >= int(to[q])) { s = q; t0 = int(to[q]); }
+    const int t = g - t0;
     const int c0 = seg * kWave * VPL + lane;
-    uint64_t raddr = 0;
-    if (sl.x >= 0) raddr = s_rp[sl.x >> 24] + uint64_t(sl.x & 0xFFFFFF) * uint64_t(a.H) * 2u;
-    const int rlo = int(uint32_t(raddr)), rhi = int(uint32_t(raddr >> 32));
+    const uint64_t rowb = uint64_t(H) * 2u;
     float acc[VPL][8];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
 
-    for (int k0 = 0; k0 < a.K; k0 += 8) {
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        // slots k0 .. k0 + 7 (entries past K belong to the next token, or
+        // to the region's slack, and are not used)
+        const u32x16 sv = *(__attribute__((address_space(4))) const u32x16 *)(slot + (int64_t(g) * K + k0) * 2);
         u32x4 y[8][VPL];
-        uint64_t rk[8];
+        uint64_t rk[8], b[8];
+        // partition numbers are masked into the table, so even the unused
+        // entries index inside it
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) b[kk] = reinterpret_cast<uint64_t>(a.reply[(int(sv[2 * kk]) >> 24) & (kMaxParts - 1)]);
+        // keeps the eight loads ahead of their first use (otherwise each is
+        // sunk into its choice's branch with a wait of its own)
+        asm volatile("" ::"s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(b[3]), "s"(b[4]), "s"(b[5]), "s"(b[6]), "s"(b[7]));
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            rk[kk] = uint64_t(uint32_t(__builtin_amdgcn_readlane(rlo, k0 + kk))) |
-                     (uint64_t(uint32_t(__builtin_amdgcn_readlane(rhi, k0 + kk))) << 32);
+            const int sl = int(sv[2 * kk]);
+            rk[kk] = (k0 + kk < K && sl >= 0) ? b[kk] + uint64_t(sl & 0xFFFFFF) * rowb : 0;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
             const gptr<const u32x4> src = (gptr<const u32x4>)rk[kk];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
@@ -1020,7 +1041,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             if (rk[kk] == 0) continue;
-            const float w = __int_as_float(__builtin_amdgcn_readlane(sl.y, k0 + kk));
+            const float w = __uint_as_float(sv[2 * kk + 1]);
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const uint32_t q[4] = {y[kk][i].x, y[kk][i].y, y[kk][i].z, y[kk][i].w};
@@ -1036,7 +1057,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
             }
         }
     }
-    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(t) * a.H);
+    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(t) * H);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = c0 + i * kWave;

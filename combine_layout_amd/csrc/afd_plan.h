@@ -67,7 +67,8 @@ struct WorkspacePlan {
     size_t blkcnt = 0;     // int32 [E][pitch] live choices per layout tile (expert-major;
                            // pitch = tiles rounded up to 4)
     size_t packed = 0;     // int32 [N*capacity*K] (expert << 16 | rank in tile), -1 skipped
-    size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}
+    size_t slot = 0;       // int32x2 [N*capacity*K] {part << 24 | row, weight bits}, then 64
+                           // bytes of slack (the combine reads slots 64 bytes at a time)
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
     size_t partials = 0;   // per-stage combine: [F][N][capacity] rows of partial_row_bytes
     size_t total = 0;
