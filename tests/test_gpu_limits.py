@@ -4,8 +4,10 @@ C ABI), against the CPU oracle on the same seeded inputs.
 Limits (include/afd.h): 16 sources, 16 partitions, 512 experts, top-32.
 Degenerate rounds: every expert chosen by every token (K = E), an
 alignment larger than any expert's count, every choice skipped, a single
-token.  Both dispatch paths, both activation formats, and the per-stage
-and cached modes are covered."""
+token.  Wide rows: FP8 rows with more scale blocks than a wavefront has
+lanes, and BF16 rows at and past the widest the one-kernel dispatch takes.
+Both dispatch paths, both activation formats, and the per-stage and cached
+modes are covered."""
 import dataclasses
 
 import numpy as np
@@ -100,3 +102,34 @@ def test_every_choice_skipped(F):
 def test_single_token():
     inst = gen.random_small(1207, N=1, F=2, E=4, K=2, alpha=2, T=[1], H=256, p_skip=0.0)
     _run(inst)
+
+
+WIDE = [("fp8", 16384, [20, 13]),    # one-kernel dispatch, 128 scale blocks per row
+        ("fp8", 16384, [600]),       # tiled path: scale blocks past the first 64 take the long-row branch
+        ("bf16", 16384, [9, 4]),     # 32 KiB rows: the widest the one-kernel dispatch takes
+        ("bf16", 16640, [9, 4])]     # one 16-byte column wider: tiled path even for 13 tokens
+
+
+@pytest.mark.parametrize("dtype,H,T", WIDE, ids=lambda v: str(v))
+def test_wide_rows(dtype, H, T):
+    """Rows of 16 K elements and more: FP8 rows carry more scale blocks than a
+    wavefront has lanes, and BF16 rows reach and pass the one-kernel limit."""
+    inst = gen.random_small(1208, N=len(T), F=2, E=8, K=4, alpha=4, T=T, H=H, p_skip=0.1, dtype=dtype)
+    print(f"[limits wide] {dtype} H={H} T={T}", flush=True)
+    _run(inst, rhc=dtype == "fp8")
+
+
+@pytest.mark.parametrize("combine", ["once", "per_stage_fp8"])
+def test_wide_fp8_rows_cached(combine):
+    """A cached round over FP8 rows with 128 scale blocks (the cached scatter's
+    long-row scale branch), and the per-stage FP8 combine over 16 K columns."""
+    h = _gpu()
+    from tests.test_gpu_parity import check_round
+    a = gen.random_small(1209, N=1, F=2, E=8, K=4, alpha=4, T=[600], H=16384, p_skip=0.1, dtype="fp8")
+    b = gen.generate(dataclasses.replace(a.cfg, seed=a.cfg.seed + 1000))
+    buf = h.make_buffer(a, combine=combine)
+    print(f"[limits wide cached] {combine}", flush=True)
+    h.run_round(a, buf, keep_arrays=False)
+    g = h.run_round(b, buf, cached=True)
+    hyb = gen.Instance(b.cfg, [dataclasses.replace(y, ids=x.ids) for x, y in zip(a.sources, b.sources)])
+    assert check_round(hyb, g, oracle.run_round(hyb, rows_cap=g.receive_rows, combine_mode=combine)) == 0
