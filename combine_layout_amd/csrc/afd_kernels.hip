@@ -107,6 +107,18 @@ struct DispatchHdr {
     int pad[8];
 };
 
+// Layout tile record, 16 bytes, for rounds of at most kLayoutMaxTiles tiles:
+// a layout workgroup reads its tile's record at an address known at entry
+// (from its block index alone), in the same batch of scalar loads as the
+// header, instead of finding its source first.  Every tile of the tiled
+// token space holds at least one token, so n = 0 marks a round without the
+// table (more tiles, or the one-kernel dispatch).
+struct TileArgs {
+    const int32_t *ids;      // ids of the tile's first token
+    int32_t g0;              // the tile's first token in the round's order
+    int32_t ns;              // tokens of the tile | source << 16
+};
+
 struct DispatchArgs {
     DispatchHdr h;
     int voff[kMaxSources];   // first slot of each source in the tiled token space
@@ -115,6 +127,7 @@ struct DispatchArgs {
     float *scales[kMaxParts];
     float *roww[kMaxParts];
     int tok_off[kMaxSources + 1];
+    TileArgs tiles[kLayoutMaxTiles];
 };
 
 // The header as a kernel holds it: the same fields, global pointers.
@@ -545,19 +558,37 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
 template <int KMAX, int NW>
 __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 {
+    static_assert(sizeof(TileArgs) == 16, "one tile record per 16 bytes");
+    const u32x4 tr = reinterpret_cast<const u32x4 *>(a.tiles)[blockIdx.x < kLayoutMaxTiles ? blockIdx.x : 0];
     const Hdr h = load_hdr(a);
+    // the header's second half with the first batch of scalar loads, not
+    // after the ids arrive (where its first uses are)
+    asm volatile("" ::"s"(h.cpitch));
     extern __shared__ __align__(16) unsigned char lds[];
     const int E = h.E, K = h.K;
     constexpr int TILE = NW * kWave;
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
     int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
-    // the tile lies in one source's span of the tiled token space
-    const int s = source_of_tiled(a, h.N, blockIdx.x * TILE);
-    const SourceRec src = load_source(a, s);
-    const int t = blockIdx.x * TILE - src.voff + tid;      // the lane's token in source s
-    const bool have = t < src.T;
-    const int g = src.off + t;                             // and in the round's order
+    // the tile lies in one source's span of the tiled token space: its
+    // first token's ids, its token count and its first token in the round
+    int s, n_tile, g_first;
+    const int32_t *ids_first;
+    if ((tr.w & 0xFFFFu) != 0) {
+        ids_first = reinterpret_cast<const int32_t *>((uint64_t(tr.y) << 32) | uint64_t(tr.x));
+        g_first = int(tr.z);
+        n_tile = int(tr.w & 0xFFFFu);
+        s = int(tr.w >> 16);
+    } else {
+        s = source_of_tiled(a, h.N, blockIdx.x * TILE);
+        const SourceRec src = load_source(a, s);
+        const int t_first = blockIdx.x * TILE - src.voff;
+        ids_first = src.ids + int64_t(t_first) * K;
+        g_first = src.off + t_first;
+        n_tile = src.T - t_first;
+    }
+    const bool have = tid < n_tile;
+    const int g = g_first + tid;                           // the lane's token in the round's order
 
     int ev[KMAX];
 #pragma unroll
@@ -565,7 +596,7 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     if (have) {
         // 16-byte loads when the token's ids are 16-byte aligned (fewer
         // memory instructions on the layout's critical path)
-        const gptr<const int32_t> idp = (gptr<const int32_t>)src.ids + int64_t(t) * K;
+        const gptr<const int32_t> idp = (gptr<const int32_t>)ids_first + int64_t(tid) * K;
         if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(idp) & 15u) == 0) {
 #pragma unroll
             for (int q = 0; q < KMAX / 4; ++q) {
@@ -589,7 +620,7 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     uint32_t live = 0;
     {
         uint64_t err = kNoError;
-        live = classify_token<KMAX>(ev, E, s, t, err);
+        live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);   // token index used only for an error
         if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // mark the token's lane bit per live expert (others into the spare slot E)
         unsigned long long *mrow = mask + size_t(wave) * (E + 1);
@@ -1399,6 +1430,17 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.h.blkcnt = p.blkcnt;
     a.h.packed = p.packed;
     a.h.slot = p.slot;
+    if (!p.fused && p.nblk <= kLayoutMaxTiles)
+        for (int b = 0; b < p.nblk; ++b) {
+            int src = 0;
+            while (src + 1 < p.N && b * p.tile >= p.voff[src + 1]) ++src;
+            const int t0 = b * p.tile - p.voff[src];
+            const int T = p.tok_off[src + 1] - p.tok_off[src];
+            const int n = T - t0 < p.tile ? T - t0 : p.tile;
+            a.tiles[b].ids = p.ids[src] + int64_t(t0) * p.K;
+            a.tiles[b].g0 = p.tok_off[src] + t0;
+            a.tiles[b].ns = n | (src << 16);
+        }
     return a;
 }
 
