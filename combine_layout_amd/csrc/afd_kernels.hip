@@ -138,11 +138,11 @@ struct Hdr {
     int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
 };
 
-__device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a)
+__device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a, u32x16 &r0, u32x16 &r1)
 {
     static_assert(sizeof(DispatchHdr) == 128, "two 64-byte blocks");
-    const u32x16 r0 = reinterpret_cast<const u32x16 *>(&a.h)[0];
-    const u32x16 r1 = reinterpret_cast<const u32x16 *>(&a.h)[1];
+    r0 = reinterpret_cast<const u32x16 *>(&a.h)[0];
+    r1 = reinterpret_cast<const u32x16 *>(&a.h)[1];
     auto u64 = [&](int i) { return (uint64_t(r0[i + 1]) << 32) | uint64_t(r0[i]); };
     Hdr h;
     h.blkcnt = (gptr<int32_t>)u64(0);
@@ -164,6 +164,12 @@ __device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a)
     h.fp8 = int(r1[6]);
     h.tile = int(r1[7]);
     return h;
+}
+
+__device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a)
+{
+    u32x16 r0, r1;
+    return load_hdr(a, r0, r1);
 }
 
 // Per-stage combine: partial row of (partition f, source s, token t) at
@@ -208,15 +214,26 @@ __device__ __forceinline__ int src_of_lds(const int *tok_off, int N, int g)
     return s;
 }
 
-// Source of global token g for a wave-uniform g: the number of sources q >= 1
-// whose first token is at or before g (empty sources share their
-// successor's offset).  The offsets are read at constant offsets, with the
-// kernel's first scalar loads.
-__device__ __forceinline__ int source_of(const int (&tok_off)[kMaxSources + 1], int N, int g)
+// The first tokens of sources 0..15 as one 64-byte scalar load.
+__device__ __forceinline__ u32x16 load_offsets(const int (&tok_off)[kMaxSources + 1])
 {
-    int s = 0;
+    static_assert(kMaxSources == 16, "offsets of every source in one 64-byte load");
+    return *reinterpret_cast<const u32x16 *>(tok_off);
+}
+
+// Source of global token g for a wave-uniform g, and the source's first
+// token: the last source q whose first token is at or before g (offsets are
+// nondecreasing; empty sources share their successor's offset).
+__device__ __forceinline__ int source_of(const u32x16 &to, int N, int g, int &first)
+{
+    int s = 0, t0 = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxSources; ++q) s += (q < N && g >= tok_off[q]) ? 1 : 0;
+    for (int q = 1; q < kMaxSources; ++q)
+        if (q < N && g >= int(to[q])) {
+            s = q;
+            t0 = int(to[q]);
+        }
+    first = uni(t0);
     return uni(s);
 }
 
@@ -397,9 +414,10 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
     const bool mine = g < ntok;
-    const int s = source_of(a.tok_off, h.N, mine ? g : 0);
+    int t0;
+    const int s = source_of(load_offsets(a.tok_off), h.N, mine ? g : 0, t0);
     const SourceRec src = load_source(a, s);
-    const int t = g - src.off;
+    const int t = g - t0;
 
     // 1. request every load: row, weights, scales, all ids
     u32x4 v[VMAX];
@@ -889,7 +907,13 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 template <int VMAX>
 __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
 {
-    const Hdr h = load_hdr(a);
+    u32x16 r0, r1;
+    const Hdr h = load_hdr(a, r0, r1);
+    const u32x16 to = load_offsets(a.tok_off);
+    // both header halves, the offsets and lpt in one batch of scalar loads
+    // (left alone, the compiler requests each where it is first used and
+    // waits for it there: three dependent round trips before the record)
+    asm volatile("" ::"s"(r0), "s"(r1), "s"(to), "s"(lpt));
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     const int wpt = lpt / kWave;                          // wavefronts per token
@@ -897,9 +921,10 @@ __global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
     const int tl = (wave % wpt) * kWave + lane;           // lane within the token
     const bool have = g < h.ntok;
     const int K = h.K, nvec = h.nvec;
-    const int s = source_of(a.tok_off, h.N, have ? g : 0);
-    const SourceArgs &src = a.src[s];
-    const int t = (have ? g : 0) - int(src.off);
+    int t0;
+    const int s = source_of(to, h.N, have ? g : 0, t0);
+    const SourceRec src = load_source(a, s);
+    const int t = (have ? g : 0) - t0;
     u32x4 v[VMAX];
     i32x2 sl;
     sl.x = -1;
@@ -1010,7 +1035,7 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 // partition bases are looked up in the kernel arguments with the choices'
 // partition numbers, all eight requested before one wait.  The chain
 // before the row loads is three scalar round trips: arguments, slots,
-// bases.  The wavefront then issues every live row's loads before it
+// bases (the token offsets are read only for the output address).  The wavefront then issues every live row's loads before it
 // accumulates, in ascending k, with a float32 multiply and a separate add.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
@@ -1026,14 +1051,6 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     const int g = gw / nseg;
     const int seg = gw - g * nseg;
     if (g >= ntok) return;
-    // source of g and its first token (offsets are nondecreasing; empty
-    // sources share their successor's offset)
-    const u32x16 to = *reinterpret_cast<const u32x16 *>(a.tok_off);
-    int s = 0, t0 = 0;
-#pragma unroll
-    for (int q = 1; q < kMaxSources; ++q)
-        if (q < N && g >= int(to[q])) { s = q; t0 = int(to[q]); }
-    const int t = g - t0;
     const int c0 = seg * kWave * VPL + lane;
     const uint64_t rowb = uint64_t(H) * 2u;
     float acc[VPL][8];
@@ -1088,7 +1105,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
             }
         }
     }
-    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(t) * H);
+    // the token's source and place in it, needed only for the output address
+    int t0;
+    const int s = source_of(load_offsets(a.tok_off), N, g, t0);
+    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(g - t0) * H);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = c0 + i * kWave;
@@ -1159,8 +1179,9 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
     if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
     const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
     if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
-    const int s = source_of(a.tok_off, a.N, g);
-    const int t = g - a.tok_off[s];
+    int t0;
+    const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
+    const int t = g - t0;
     const int nvec = a.nvec;
     const int c = seg * kWave + lane;
     uint64_t raddr = 0;
