@@ -1033,10 +1033,11 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 // The token's slots arrive as wave-uniform values, one 64-byte scalar load
 // per eight choices (the slot map does not change during the kernel); the
 // partition bases are looked up in the kernel arguments with the choices'
-// partition numbers, all eight requested before one wait.  The chain
-// before the row loads is three scalar round trips: arguments, slots,
-// bases (the token offsets are read only for the output address).  The wavefront then issues every live row's loads before it
-// accumulates, in ascending k, with a float32 multiply and a separate add.
+// partition numbers, all eight requested before one wait.  The chain before
+// the row loads is three scalar round trips: arguments, slots, bases (the
+// token offsets are read only for the output address).  The wavefront then
+// issues every live row's loads before it accumulates, in ascending k, with
+// a float32 multiply and a separate add.
 template <int VPL>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {

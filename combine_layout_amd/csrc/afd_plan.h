@@ -21,7 +21,9 @@ constexpr int kMaxTopk = AFD_MAX_TOPK;
 constexpr int kLayoutTileMin = 64;
 constexpr int kLayoutTile = 256;
 // Tile counts of an expert the scatter requests at entry (beyond this many
-// tiles it sums them in a loop).
+// tiles it sums them in a loop), and the number of tile records the layout
+// kernel's arguments carry (rounds with more tiles find each tile's source
+// from the source offsets instead).
 constexpr int kLayoutMaxTiles = 32;
 // Small rounds rebuild the layout inside every scatter workgroup (one kernel
 // for the whole dispatch): at most this many tokens, ids (staged in LDS) and
