@@ -1452,7 +1452,7 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.h.blkcnt = p.blkcnt;
     a.h.packed = p.packed;
     a.h.slot = p.slot;
-    if (!p.fused && p.nblk <= kLayoutMaxTiles)
+    if (!p.fused && !p.cached && p.nblk <= kLayoutMaxTiles)   // the layout kernel runs
         for (int b = 0; b < p.nblk; ++b) {
             int src = 0;
             while (src + 1 < p.N && b * p.tile >= p.voff[src + 1]) ++src;
