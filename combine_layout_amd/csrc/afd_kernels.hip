@@ -184,12 +184,13 @@ struct StageArgs {
     int N, F, ntok, K, H, nvec, nseg, capacity, f, s, T;
 };
 
-// The combine's scalars fill the first 64 bytes and the token offsets start
-// at byte 64, so a wavefront reads each with one 64-byte scalar load.
+// The combine's scalars and the first four partitions' reply bases fill the
+// first 64 bytes, and the token offsets start at byte 64, so a wavefront
+// reads each with one 64-byte scalar load.
 struct CombineArgs {
     const int32_t *slot;     // [ntok][K] {part << 24 | row, weight bits}, 64 bytes of slack at the end
     int N, ntok, K, H, nvec, nseg;
-    int pad[8];
+    const uint16_t *reply4[4];   // reply[0..3] again (rounds of at most four partitions select from these)
     int tok_off[kMaxSources + 1];
     const uint16_t *reply[kMaxParts];
     uint16_t *out[kMaxSources];
@@ -1031,22 +1032,27 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 
 // Combine: one wavefront per (token, segment of 64*VPL 16-byte columns).
 // The token's slots arrive as wave-uniform values, one 64-byte scalar load
-// per eight choices (the slot map does not change during the kernel); the
-// partition bases are looked up in the kernel arguments with the choices'
-// partition numbers, all eight requested before one wait.  The chain before
-// the row loads is three scalar round trips: arguments, slots, bases (the
-// token offsets are read only for the output address).  The wavefront then
-// issues every live row's loads before it accumulates, in ascending k, with
-// a float32 multiply and a separate add.
-template <int VPL>
+// per eight choices (the slot map does not change during the kernel).  With
+// at most NB = 2 or 4 partitions each choice's reply base is selected from
+// the ones that came with the scalars, so the chain before the row loads is
+// two scalar round trips: arguments, slots (the two-way select is the
+// cheaper one, which shows at decode).  With more partitions (NB = 0) the
+// bases are looked up in the kernel arguments by partition number, all
+// eight requested before one wait (a third round trip).  The token offsets are read only for
+// the output address.  The wavefront then issues every live row's loads
+// before it accumulates, in ascending k, with a float32 multiply and a
+// separate add.
+template <int VPL, int NB>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
 #pragma clang fp contract(off)
-    static_assert(offsetof(CombineArgs, pad) + sizeof(int) * 8 == 64, "scalars in the first 64 bytes");
-    static_assert(offsetof(CombineArgs, tok_off) == 64, "offsets at byte 64");
+    static_assert(offsetof(CombineArgs, reply4) == 32 && offsetof(CombineArgs, tok_off) == 64,
+                  "scalars and four bases in the first 64 bytes, offsets at byte 64");
     const u32x16 hv = *reinterpret_cast<const u32x16 *>(&a);
     const int32_t *slot = reinterpret_cast<const int32_t *>((uint64_t(hv[1]) << 32) | uint64_t(hv[0]));
     const int N = int(hv[2]), ntok = int(hv[3]), K = int(hv[4]), H = int(hv[5]), nvec = int(hv[6]), nseg = int(hv[7]);
+    auto base4 = [&](uint32_t q) { return (uint64_t(hv[9 + 2 * q]) << 32) | uint64_t(hv[8 + 2 * q]); };
+    const uint64_t rb0 = base4(0), rb1 = base4(1), rb2 = base4(2), rb3 = base4(3);
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
     const int g = gw / nseg;
@@ -1066,13 +1072,25 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         const u32x16 sv = *(__attribute__((address_space(4))) const u32x16 *)(slot + (int64_t(g) * K + k0) * 2);
         u32x4 y[8][VPL];
         uint64_t rk[8], b[8];
-        // partition numbers are masked into the table, so even the unused
-        // entries index inside it
+        // partition numbers are masked into the tables, so even the unused
+        // entries select inside them
+        if (NB == 2) {
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) b[kk] = reinterpret_cast<uint64_t>(a.reply[(int(sv[2 * kk]) >> 24) & (kMaxParts - 1)]);
-        // keeps the eight loads ahead of their first use (otherwise each is
-        // sunk into its choice's branch with a wait of its own)
-        asm volatile("" ::"s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(b[3]), "s"(b[4]), "s"(b[5]), "s"(b[6]), "s"(b[7]));
+            for (int kk = 0; kk < 8; ++kk) b[kk] = (sv[2 * kk] >> 24) & 1u ? rb1 : rb0;
+        } else if (NB == 4) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const uint32_t q = (sv[2 * kk] >> 24) & 3u;
+                b[kk] = q & 2u ? (q & 1u ? rb3 : rb2) : (q & 1u ? rb1 : rb0);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                b[kk] = reinterpret_cast<uint64_t>(a.reply[(int(sv[2 * kk]) >> 24) & (kMaxParts - 1)]);
+            // keeps the eight loads ahead of their first use (otherwise each
+            // is sunk into its choice's branch with a wait of its own)
+            asm volatile("" ::"s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(b[3]), "s"(b[4]), "s"(b[5]), "s"(b[6]), "s"(b[7]));
+        }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             const int sl = int(sv[2 * kk]);
@@ -1612,6 +1630,7 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     CombineArgs a;
     std::memset(&a, 0, sizeof(a));
     for (int f = 0; f < p.F; ++f) a.reply[f] = static_cast<const uint16_t *>(p.reply[f]);
+    for (int f = 0; f < 4 && f < p.F; ++f) a.reply4[f] = a.reply[f];
     for (int s = 0; s < p.N; ++s) a.out[s] = static_cast<uint16_t *>(p.out[s]);
     for (int s = 0; s <= p.N; ++s) a.tok_off[s] = p.tok_off[s];
     a.N = p.N;
@@ -1623,7 +1642,9 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     a.nseg = (a.nvec + kWave - 1) / kWave;
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
-    hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, st, a);
+    if (p.F <= 2) hipLaunchKernelGGL((k_combine<1, 2>), grid, dim3(256), 0, st, a);
+    else if (p.F <= 4) hipLaunchKernelGGL((k_combine<1, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_combine<1, 0>), grid, dim3(256), 0, st, a);
     return launched_ok();
 }
 
