@@ -103,6 +103,7 @@ def load_fake():
     lib = _bind(ctypes.CDLL(FAKE_LIB_PATH))
     lib.afd_fake_log_get.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_int]
     lib.afd_fake_set_ends.argtypes = [_P, ctypes.c_int, ctypes.c_uint64]
+    lib.afd_fake_tiles.argtypes = [_P, ctypes.c_int]
     return lib
 
 

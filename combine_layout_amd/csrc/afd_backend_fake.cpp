@@ -15,6 +15,7 @@
 namespace {
 std::vector<std::string> g_log;
 std::vector<int32_t> g_ends;
+std::vector<afd::TileRec> g_tiles;   // the last dispatch's layout tile records
 uint64_t g_err = afd::kNoError;
 int g_capturing = 0;
 int g_fail = 0;
@@ -47,6 +48,8 @@ int be_is_capturing(void *, int *capturing)
 
 int be_launch_dispatch(const RoundPlan &p, void *)
 {
+    TileRec tr[kLayoutMaxTiles];
+    g_tiles.assign(tr, tr + layout_tiles(p, tr));
     std::string srcs;
     for (int s = 0; s < p.N; ++s) {
         char b[64];
@@ -140,4 +143,17 @@ void afd_fake_set_ends(const int32_t *ends, int n, uint64_t err)
 }
 void afd_fake_set_capturing(int c) { g_capturing = c; }
 void afd_fake_set_fail(int f) { g_fail = f; }
+// The last dispatch's layout tile records as (src, t0, n, g0) quadruples;
+// returns their number (0: no table).
+int afd_fake_tiles(int32_t *out, int max)
+{
+    const int n = int(g_tiles.size());
+    for (int b = 0; b < n && b < max; ++b) {
+        out[4 * b] = g_tiles[size_t(b)].src;
+        out[4 * b + 1] = g_tiles[size_t(b)].t0;
+        out[4 * b + 2] = g_tiles[size_t(b)].n;
+        out[4 * b + 3] = g_tiles[size_t(b)].g0;
+    }
+    return n;
+}
 }

@@ -1470,17 +1470,13 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.h.blkcnt = p.blkcnt;
     a.h.packed = p.packed;
     a.h.slot = p.slot;
-    if (!p.fused && !p.cached && p.nblk <= kLayoutMaxTiles)   // the layout kernel runs
-        for (int b = 0; b < p.nblk; ++b) {
-            int src = 0;
-            while (src + 1 < p.N && b * p.tile >= p.voff[src + 1]) ++src;
-            const int t0 = b * p.tile - p.voff[src];
-            const int T = p.tok_off[src + 1] - p.tok_off[src];
-            const int n = T - t0 < p.tile ? T - t0 : p.tile;
-            a.tiles[b].ids = p.ids[src] + int64_t(t0) * p.K;
-            a.tiles[b].g0 = p.tok_off[src] + t0;
-            a.tiles[b].ns = n | (src << 16);
-        }
+    TileRec tr[kLayoutMaxTiles];
+    const int ntr = layout_tiles(p, tr);
+    for (int b = 0; b < ntr; ++b) {
+        a.tiles[b].ids = p.ids[tr[b].src] + int64_t(tr[b].t0) * p.K;
+        a.tiles[b].g0 = tr[b].g0;
+        a.tiles[b].ns = tr[b].n | (tr[b].src << 16);
+    }
     return a;
 }
 

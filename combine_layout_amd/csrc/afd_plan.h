@@ -116,6 +116,28 @@ struct RoundPlan {
     uint8_t *partials = nullptr;
 };
 
+// Layout tile records of a round of at most kLayoutMaxTiles tiles: tile b
+// holds tokens t0 .. t0 + n - 1 of source src, the first of them token g0 of
+// the round.  The layout kernel reads its tile's record instead of finding
+// its source.  Returns the number of records; 0 when no layout kernel runs
+// (one-kernel or cached dispatch) or the round has more tiles.
+struct TileRec {
+    int src, t0, n, g0;
+};
+
+inline int layout_tiles(const RoundPlan &p, TileRec *out)
+{
+    if (p.fused || p.cached || p.nblk > kLayoutMaxTiles) return 0;
+    for (int b = 0; b < p.nblk; ++b) {
+        int s = 0;   // the last source whose span starts at or before the tile (empty spans are skipped)
+        while (s + 1 < p.N && b * p.tile >= p.voff[s + 1]) ++s;
+        const int t0 = b * p.tile - p.voff[s];
+        const int T = p.tok_off[s + 1] - p.tok_off[s];
+        out[b] = TileRec{s, t0, T - t0 < p.tile ? T - t0 : p.tile, p.tok_off[s] + t0};
+    }
+    return p.nblk;
+}
+
 // ---- backend: implemented by the HIP executor or the recording fake ----
 // Each returns 0 on success, nonzero on a runtime failure.
 int be_init_workspace(void *workspace, const WorkspacePlan &wp);

@@ -438,6 +438,48 @@ def test_split_path_sources_start_on_tile_boundaries(lib):
     y.destroy()
 
 
+def tiles(lib):
+    buf = (ctypes.c_int32 * (4 * 32))()
+    n = lib.afd_fake_tiles(ctypes.cast(buf, ctypes.c_void_p), 32)
+    return [tuple(buf[4 * b:4 * b + 4]) for b in range(n)]
+
+
+def test_layout_tile_records(lib):
+    # each layout tile's record: (source, first token in the source, tokens,
+    # first token in the round); empty sources own no tile, a source's last
+    # tile is partial, and rounds above 32 tiles, one-kernel rounds and
+    # cached rounds carry no records
+    x = Ctx(lib, cfg(N=3, F=2, E=8, K=2, cap=4096))
+    assert x.dispatch(0, 65) == 0 and x.dispatch(1, 0) == 0 and x.dispatch(2, 500) == 0
+    assert x.receive(0)[0] == 0
+    assert tiles(lib) == [(0, 0, 64, 0), (0, 64, 1, 64)] + [(2, 64 * i, 64, 65 + 64 * i) for i in range(7)] + \
+        [(2, 448, 52, 513)]
+    x.destroy()
+    y = Ctx(lib, cfg(N=3, F=2, E=8, K=2, cap=4096))
+    assert y.dispatch(0, 1) == 0 and y.dispatch(1, 2100) == 0 and y.dispatch(2, 1) == 0
+    assert y.receive(0)[0] == 0
+    t = tiles(lib)
+    assert len(t) == 19 and t[0] == (0, 0, 1, 0) and t[-1] == (2, 0, 1, 2101)
+    assert t[1:18] == [(1, 128 * i, 128 if i < 16 else 2100 - 2048, 1 + 128 * i) for i in range(17)]
+    y.destroy()
+    z = Ctx(lib, cfg(N=2, F=2, E=8, K=2, cap=8192))
+    assert z.dispatch(0, 5000) == 0 and z.dispatch(1, 4000) == 0
+    assert z.receive(0)[0] == 0
+    assert tiles(lib) == []                  # 36 tiles of 256
+    z.destroy()
+    w = Ctx(lib, cfg(N=2, F=2, E=8, K=2, cap=64))
+    assert w.dispatch(0, 30) == 0 and w.dispatch(1, 20) == 0
+    assert w.receive(0)[0] == 0
+    assert tiles(lib) == []                  # one-kernel dispatch
+    w.destroy()
+    v = Ctx(lib, cfg(N=1, F=2, E=8, K=2, cap=1024))
+    v.full_round(T=(600,))
+    assert tiles(lib) == [(0, 64 * i, 64 if i < 9 else 24, 64 * i) for i in range(10)]
+    assert v.dispatch_cached(0, 600) == 0 and v.receive(0)[0] == 0
+    assert tiles(lib) == []                  # cached dispatch: no layout kernel
+    v.destroy()
+
+
 def test_hip_failure_leaves_state(lib):
     x = Ctx(lib, cfg())
     for s in range(2):
