@@ -78,7 +78,7 @@ typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
  *                              infinite value saturates to 448); the row is
  *                              H codes, then H/128 bytes 127 + e, zero padded
  *                              to H + align32(H/128) bytes.  Lossy: at most
- *                              2^-4 of the group's amax per element.
+ *                              amax/16 of its group per element.
  * The per-stage modes need num_partitions >= 2 (with one partition the
  * single partial is the final result).
  */

@@ -66,8 +66,11 @@ class Layout:
         self.err = err                  # (code, s, t, k)
 
 
-def check_config(N, E, F, K, H, alpha) -> bool:
-    return lib().orc_check_config(N, E, F, K, H, alpha) == 0
+def check_config(T: Sequence[int], bucket: int, capacity: int, E: int, F: int, K: int, H: int, alpha: int) -> bool:
+    """Step one of a round (API contract page, "Roles and tensors"): is the
+    configuration with per-source token counts T valid?"""
+    T_arr = np.ascontiguousarray(T, dtype=np.int32)
+    return lib().orc_check_config(len(T_arr), _p(T_arr), bucket, capacity, E, F, K, H, alpha) == 0
 
 
 def layout(T: Sequence[int], ids: np.ndarray, E: int, F: int, K: int, alpha: int) -> Layout:
@@ -245,6 +248,8 @@ def run_round(inst, rows_cap: Optional[Sequence[int]] = None, combine_mode: str 
     fp8 = cfg.dtype == "fp8"
     T = [len(s.ids) for s in inst.sources]
     K, H, E, F = cfg.K, cfg.H, cfg.E, cfg.F
+    if not check_config(T, cfg.bucket, cfg.capacity, E, F, K, H, cfg.alpha):
+        raise ValueError("invalid configuration or shapes")
     ids = np.concatenate([s.ids for s in inst.sources]) if sum(T) else np.zeros((0, K), np.int32)
     w = np.concatenate([s.weights for s in inst.sources]) if sum(T) else np.zeros((0, K), np.float32)
     dt = np.uint8 if fp8 else np.uint16

@@ -90,16 +90,26 @@ static float e4m3_to_f32(uint8_t q)
     return sign ? -v : v;
 }
 
-/* ---- configuration (API contract page, "Roles and tensors") ------------- */
+/* ---- configuration and shapes (API contract page, "Roles and tensors") -- */
 
-/* H a multiple of 256, 1 <= K <= min(32, E), experts divide evenly over the
- * FFN partitions, alignment >= 1. */
-int orc_check_config(int N, int E, int F, int K, int H, int alpha)
+/* A round is valid when the hidden size is a positive multiple of 256, the
+ * top-k satisfies 1 <= K <= min(32, E), the experts split evenly over the F
+ * FFN partitions, the alignment is at least 1, and every source's token
+ * count fits the bucket, which fits the capacity: 0 <= T[s] <= bucket <=
+ * capacity.  There is at least one source and one partition, and a bucket
+ * holds at least one token (reading: a bucket is the token count a capture
+ * is specialised for, so an empty one specialises nothing).  Returns ORC_OK
+ * or ORC_BAD_CONFIG. */
+int orc_check_config(int N, const int32_t *T, int bucket, int capacity, int E, int F, int K, int H, int alpha)
 {
+    int s;
     if (N < 1 || E < 1 || F < 1 || K < 1 || alpha < 1 || H < 256) return ORC_BAD_CONFIG;
     if (H % 256 != 0) return ORC_BAD_CONFIG;
     if (K > 32 || K > E) return ORC_BAD_CONFIG;
     if (E % F != 0) return ORC_BAD_CONFIG;
+    if (bucket < 1 || bucket > capacity) return ORC_BAD_CONFIG;
+    for (s = 0; s < N; ++s)
+        if (T[s] < 0 || T[s] > bucket) return ORC_BAD_CONFIG;
     return ORC_OK;
 }
 

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_combine as tc
+from tests import test_oracle_config as tcfg
 from tests import test_oracle_layout as tl
 from tests import test_oracle_staged as ts
 
@@ -49,6 +50,12 @@ MUTANTS = {
     "fp8_dequant_bias": ("(int)row[H + h / 128] - 127);", "(int)row[H + h / 128] - 126);"),
     "fp8_ties_up": ("((c + 1) & 1) == 0)) c = c + 1;", "1)) c = c + 1;"),
     "fp8_nan_in_amax": ("if (v == v && v > amax) amax = v;", "if (v > amax || v != v) amax = v;"),
+    # configuration and shape check
+    "config_hidden_multiple_of_128": ("if (H % 256 != 0) return ORC_BAD_CONFIG;", "if (H % 128 != 0) return ORC_BAD_CONFIG;"),
+    "config_topk_limit_dropped": ("if (K > 32 || K > E) return ORC_BAD_CONFIG;", "if (K > E) return ORC_BAD_CONFIG;"),
+    "config_uneven_split_accepted": ("    if (E % F != 0) return ORC_BAD_CONFIG;\n", "\n"),
+    "config_bucket_past_capacity": ("if (bucket < 1 || bucket > capacity)", "if (bucket < 1)"),
+    "config_tokens_past_bucket": ("if (T[s] < 0 || T[s] > bucket)", "if (T[s] < 0)"),
 }
 
 
@@ -69,6 +76,7 @@ def _pins():
             ts.test_stage_two_order_is_last_lane, ts.test_fp8_partials_exact_for_short_integers,
             ts.test_single_partition_reduces_to_single_rounding,
             lambda: ts.test_quantized_rows_match_torch_and_closed_form(256)]
+    out.insert(0, tcfg.test_config_pins_all)   # fast, so first
     for i in (0, 3, 4):
         out.append(lambda i=i: ts.test_partials_equal_masked_single_rounding_combine(i))
         out.append(lambda i=i: ts.test_stage_two_equals_single_rounding_combine_of_partials(i, False))

@@ -15,7 +15,7 @@ What pins it, independently of the oracle's own mechanism:
     frexp, and the page's special values (clamp at -117, 2^120 for an
     infinite amax);
   * quantised rows against torch's cast of the exactly scaled values, and
-    the page's error bound (at most 2^-4 of the group's amax);
+    the section 19 error bound (|decoded - v| <= amax_group / 16);
   * stage one against the pinned single-rounding combine run on the layout
     with other partitions' choices skipped;
   * stage two against the pinned single-rounding combine of the partials
@@ -148,8 +148,8 @@ def test_quantized_rows_match_torch_and_closed_form(H):
 
 
 def test_quantization_error_bound():
-    """Design page, section 19: per element the error is at most 2^-4 of its
-    group's amax; a value that is already representable round-trips."""
+    """Design page, section 19 error bound: |decoded - v| <= amax_group / 16
+    for every element; a value that is already representable round-trips."""
     rng = np.random.default_rng(23)
     H = 1024
     v = (rng.standard_normal((64, H)) * 2.0 ** rng.integers(-40, 40, (64, 1))).astype(np.float32)
