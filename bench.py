@@ -1,4 +1,4 @@
-"""Benchmark of one AFD dispatch+combine round on one MI355X.
+"""Benchmark of the AFD dispatch+combine round on one MI355X.
 
 A step is one round of the whole hot path for every role: N source
 dispatches, F worker receives (layout + scatter), F worker replies (the last
@@ -7,10 +7,16 @@ resident in HBM.  Replies come from identity experts computed once before
 timing (expert compute is outside the library and outside the round, as in
 the afdEP-comm measurements, which time communication only).
 
-Rounds are captured in HIP graphs and replayed.  "cold" rounds rotate over
-enough independent input/arena/reply sets to push every round's bytes through
-HBM past the on-package cache; "hot" rounds reuse one set.  `value` is the
-cold whole-round algorithmic throughput:
+Every workload (the six seeded shapes) is measured by default; the top-level
+value is the E128/K8/H2048 decode round the metric names, and a block per
+workload carries the same figures.  Rounds are captured in HIP graphs and
+replayed.  "cold" rounds rotate over enough independent input/arena/reply
+sets to push every round's bytes through HBM past the on-package cache
+(round i on set i mod S, so a block's rounds use distinct sets); "hot"
+rounds reuse one set.  The timed rounds are split into five blocks; a
+workload's figure is the median block, and the median of that over fresh
+processes (three by default).  `value` is the cold whole-round algorithmic
+throughput:
 
   per token       : H*b_x (+4*H/128 FP8 scales) read x, 2*H write the output,
                     8*K read ids+weights, 8*K write + 8*K read the slot map
@@ -96,7 +102,7 @@ class RoundSet:
 
     def __init__(self, inst, view, combine="once", cached=False):
         import torch
-        from tests import gpu_harness as h
+        import harness as h
         self.inst = inst
         self.cfg = inst.cfg
         self.view = view
@@ -158,36 +164,52 @@ def capture(sets, order):
     return g
 
 
-def time_graph_rounds(sets, order, steps, warmup, blocks=5):
-    """Replay graphs so that exactly `steps` rounds are timed, in `blocks`
-    consecutive blocks with an event between blocks; returns the median
-    block's µs per round and the per-block values."""
+def time_rounds(sets, S, steps, warmup, blocks=5, gmax=32):
+    """Time exactly `steps` rounds in `blocks` consecutive blocks.
+
+    Rounds are numbered from 0 with the `warmup` untimed rounds first; round
+    i runs on set i mod S, so consecutive rounds use different sets and the
+    rounds of a block rotate through distinct ones.  Each block is replayed
+    as graphs of at most `gmax` rounds (cached by starting set and length).
+    The warmup replays stay queued ahead of the first block, so the GPU is
+    busy while the blocks are enqueued, and HIP events between the blocks
+    bracket device work.  Returns the median block's µs per round and every
+    block's value."""
     import torch
-    G = len(order)
-    g_full = capture(sets, order)
-    reps = steps // G
-    rem = steps % G
-    g_rem = capture(sets, order[:rem]) if rem else None
-    for _ in range(max(1, math.ceil(warmup / G))):
-        g_full.replay()
+    graphs = {}
+
+    def chunks(start, n):
+        out = []
+        while n > 0:
+            m = min(n, gmax)
+            key = (start % S, m)
+            if key not in graphs:
+                graphs[key] = capture(sets, [(start + j) % S for j in range(m)])
+            out.append(graphs[key])
+            start += m
+            n -= m
+        return out
+
+    blocks = max(1, min(blocks, steps))
+    per = [steps // blocks + (1 if b < steps % blocks else 0) for b in range(blocks)]
+    warm = chunks(0, warmup)
+    plan = []
+    i = warmup
+    for b in range(blocks):
+        plan.append(chunks(i, per[b]))
+        i += per[b]
     torch.cuda.synchronize()
-    blocks = max(1, min(blocks, reps))
-    # graph replays per block (the remainder rounds go to the last block)
-    per = [reps // blocks + (1 if b < reps % blocks else 0) for b in range(blocks)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
-    torch.cuda.synchronize()
+    for g in warm:
+        g.replay()
     ev[0].record()
     for b in range(blocks):
-        for _ in range(per[b]):
-            g_full.replay()
-        if b == blocks - 1 and g_rem is not None:
-            g_rem.replay()
+        for g in plan[b]:
+            g.replay()
         ev[b + 1].record()
     torch.cuda.synchronize()
-    us = []
-    for b in range(blocks):
-        rounds = per[b] * G + (rem if b == blocks - 1 else 0)
-        us.append(ev[b].elapsed_time(ev[b + 1]) * 1e3 / rounds)
+    us = [ev[b].elapsed_time(ev[b + 1]) * 1e3 / per[b] for b in range(blocks)]
+    del graphs
     return float(np.median(us)), us
 
 
@@ -248,7 +270,7 @@ def time_identity_experts(rs, reps=20):
     stand-in for the caller's FFN, outside the round and reported beside
     it."""
     import torch
-    from tests import gpu_harness as h
+    import harness as h
     cfg = rs.cfg
     recs = rs.dispatch_phase()
     rs.combine_phase(recs)
@@ -328,10 +350,14 @@ def copy_bandwidth(nbytes=1 << 30, reps=20):
 
 # ---------------------------------------------------------- CPU baseline ----
 
-def cpu_baseline(inst, budget_s=10.0):
-    """The oracle as it stands (single-threaded C), timed on this host:
-    layout + row/scale/weight dispatch + combine per round, identity-expert
-    replies computed once outside the timing (as on the GPU)."""
+def cpu_baseline(inst, budget_s, parallel=False, ref=None):
+    """The oracle as it stands, timed on this host's cores: layout + row,
+    scale and weight dispatch + combine per round, the identity-expert
+    replies computed once outside the timing (as on the GPU) and every
+    output array allocated once before it.  parallel=True runs the oracle's
+    OpenMP timing build (row copy and combine on every thread; counting,
+    aligned prefix and slots serial).  Returns (seconds per round, rounds,
+    threads)."""
     import oracle
     cfg = inst.cfg
     T = cfg.T
@@ -339,28 +365,45 @@ def cpu_baseline(inst, budget_s=10.0):
     w = np.concatenate([s.weights for s in inst.sources])
     x = np.concatenate([s.x for s in inst.sources])
     G = cfg.H // 128
-    ref = oracle.run_round(inst)
+    ref = ref or oracle.run_round(inst)
     caps = ref.rows_cap
-    rounds = 0
-    t_total = 0.0
-    while True:
-        t0 = time.perf_counter()
+    threads = oracle.set_parallel(parallel)
+    try:
         lay = oracle.layout(T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
-        oracle.dispatch(x, w, lay, cfg.F, caps)
-        if cfg.dtype == "fp8":
-            oracle.dispatch_scales(T, [s.scale for s in inst.sources], [(G, 1)] * cfg.N, G, lay, cfg.F, caps)
-        oracle.combine(w, lay, cfg.H, ref.replies)
-        t_total += time.perf_counter() - t0
-        rounds += 1
-        if t_total >= budget_s:
-            break
-    return t_total / rounds, rounds
+        rows = oracle.dispatch(x, w, lay, cfg.F, caps)
+        scales = oracle.dispatch_scales(T, [s.scale for s in inst.sources], [(G, 1)] * cfg.N, G, lay, cfg.F,
+                                        caps) if cfg.dtype == "fp8" else None
+        out = oracle.combine(w, lay, cfg.H, ref.replies)
+        rounds = 0
+        t_total = 0.0
+        while True:
+            t0 = time.perf_counter()
+            lay = oracle.layout(T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
+            oracle.dispatch(x, w, lay, cfg.F, caps, out=rows)
+            if scales is not None:
+                oracle.dispatch_scales(T, [s.scale for s in inst.sources], [(G, 1)] * cfg.N, G, lay, cfg.F, caps,
+                                       out=scales)
+            oracle.combine(w, lay, cfg.H, ref.replies, out=out)
+            t_total += time.perf_counter() - t0
+            rounds += 1
+            if t_total >= budget_s:
+                break
+    finally:
+        oracle.set_parallel(False)
+    return t_total / rounds, rounds, threads
 
-
-# ------------------------------------------------------------------ main ----
 
 def cpu_model() -> str:
-    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    """The host CPU's model string as lscpu prints it, else /proc/cpuinfo's,
+    else the machine type."""
+    import subprocess
+    try:
+        txt = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in txt.splitlines():
+            if line.strip().lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.lower().startswith("model name"):
@@ -409,19 +452,192 @@ def load_traffic(kernel, workload, mode="", mult=None):
     return None
 
 
+# ------------------------------------------------------ GPU measurement ----
+
+# E128 / top-8 / H2048 workloads: the ones the 60%-of-peak target applies to
+GATED = ("2a2f_decode", "2a2f_fp8_prefill")
+GATE_FRAC = 0.60
+MAX_COLD_SETS = 64
+
+
+def dominant_kernel(info, nb, cached, combine):
+    """The single-kernel phase with the most algorithmic bytes, from the
+    kernels the library reports for the round: the dispatch when it is one
+    kernel (the one-kernel or cached scatter), else the combine; the
+    per-stage combine is timed as its whole phase."""
+    if combine != "once":
+        return "combine", "k_partial+k_final"
+    path = info["dispatch_path"]
+    single = {"one_kernel": "k_fused", "cached": "k_scatter_cached"}.get(path)
+    if single is not None and nb["dispatch"] >= nb["combine"]:
+        return "dispatch", single
+    return "combine", "k_combine"
+
+
+def measure_workload(name, args):
+    """Every GPU figure of one workload, measured in this process."""
+    import torch
+    inst = gen.instance_by_name(name)
+    cfg = inst.cfg
+    L = live_choices(inst)
+    nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else 0)
+    view = cfg.F == 1
+    S = min(MAX_COLD_SETS, max(1, math.ceil(args.cold_bytes / nb["total"])))
+    gmax = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
+    print(f"[bench] {name}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} alpha={cfg.alpha} "
+          f"dtype={cfg.dtype} L={L} bytes/round={nb['total']} cold sets={S}", file=sys.stderr, flush=True)
+    sets = [RoundSet(inst, view, args.combine, args.cached)]
+    info = sets[0].buf.round_info()
+    hot_us, hot_blocks = time_rounds(sets, 1, args.steps, args.warmup, gmax=gmax)
+    for _ in range(S - 1):
+        sets.append(RoundSet(inst, view, args.combine, args.cached))
+    cold_us, cold_blocks = time_rounds(sets, S, args.steps, args.warmup, gmax=gmax)
+    print(f"[bench] {name}: cold {cold_us:.3f} us/round (blocks {', '.join(f'{u:.3f}' for u in cold_blocks)}), "
+          f"hot {hot_us:.3f}", file=sys.stderr, flush=True)
+    kern = time_kernels_live(sets)
+    expert_us = time_identity_experts(sets[0])
+    dom, dom_name = dominant_kernel(info, nb, args.cached, args.combine)
+    mode = ("_cached" if args.cached else "") + ("" if args.combine == "once" else "_" + args.combine)
+    traffic = load_traffic(dom_name, name, mode, {"k_partial": cfg.F, "k_final": cfg.N})
+    dom_gbps = nb[dom] / (kern[dom] * 1e-6) / 1e9
+    gbps = nb["total"] / (cold_us * 1e-6) / 1e9
+    res = {
+        "us_per_round": cold_us,
+        "us_per_round_blocks": cold_blocks,
+        "us_per_round_hot": hot_us,
+        "us_per_round_hot_blocks": hot_blocks,
+        "gbps": gbps,
+        "pct_peak": 100 * gbps / PEAK_HBM_GBPS,
+        "bytes_per_round": nb["total"],
+        "bytes_dispatch": nb["dispatch"],
+        "bytes_combine": nb["combine"],
+        "kernels_us": kern,
+        "identity_experts_us": expert_us,
+        "dispatch_path": info["dispatch_path"],
+        "layout_tiles": info["layout_tiles"],
+        "cold_sets": S,
+        "rounds_per_graph_max": gmax,
+        "live_choices": L,
+        "config": {"workload": name, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
+                   "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
+                   "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
+                   "combine": args.combine, "cached_layout": bool(args.cached)},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": dom_gbps / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": kern[dom]},
+        "inputs_sha256": inst.digests(),
+    }
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure(names, args):
+    """Every selected workload, then the launch floor and the copy rate, in
+    this process (which initialises the GPU)."""
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    out = {"workloads": {}}
+    for name in names:
+        out["workloads"][name] = measure_workload(name, args)
+    if not args.no_extras:
+        out["launch_floor_us_per_round"] = launch_floor()
+        out["copy_gbps"] = copy_bandwidth()
+    return out
+
+
+# ------------------------------------------------------------------ main ----
+
+def _median(vals):
+    return float(np.median(np.asarray(vals, dtype=np.float64)))
+
+
+def aggregate(runs, names, args):
+    """Per workload, the median over fresh processes of each timing, with
+    every process's value kept beside it."""
+    out = {}
+    for name in names:
+        rs = [r["workloads"][name] for r in runs]
+        first = rs[0]
+        nb = first["bytes_per_round"]
+        cold = _median([r["us_per_round"] for r in rs])
+        hot = _median([r["us_per_round_hot"] for r in rs])
+        kern = {k: _median([r["kernels_us"][k] for r in rs]) for k in first["kernels_us"]}
+        roof = dict(first["roofline"])
+        dom = "dispatch" if roof["kernel"] in ("k_fused", "k_scatter_cached") else "combine"
+        roof["avg_launch_us"] = kern[dom]
+        roof["achieved"] = roof["algorithmic_bytes_per_launch"] / (kern[dom] * 1e-6) / 1e9
+        roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
+        gbps = nb / (cold * 1e-6) / 1e9
+        w = {
+            "us_per_round": round(cold, 3),
+            "us_per_round_per_process": [round(r["us_per_round"], 3) for r in rs],
+            "us_per_round_blocks": [[round(u, 3) for u in r["us_per_round_blocks"]] for r in rs],
+            "gbps": round(gbps, 2),
+            "pct_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+            "us_per_round_hot": round(hot, 3),
+            "gbps_hot": round(nb / (hot * 1e-6) / 1e9, 2),
+            "pct_peak_hot": round(100 * nb / (hot * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+            "bytes_per_round": nb,
+            "kernels_us": {k: round(v, 3) for k, v in kern.items()},
+            "identity_experts_us": round(_median([r["identity_experts_us"] for r in rs]), 3),
+            "dispatch_path": first["dispatch_path"],
+            "cold_sets": first["cold_sets"],
+            "config": first["config"],
+            "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+            "inputs_sha256": first["inputs_sha256"],
+        }
+        if name in GATED and args.combine == "once" and not args.cached:
+            budget = nb / (GATE_FRAC * PEAK_HBM_GBPS * 1e9) * 1e6
+            w["gate_60pct"] = {"budget_us": round(budget, 3), "pass": bool(cold <= budget)}
+        out[name] = w
+    return out
+
+
+def run_children(args, argv):
+    """Measure in `args.processes` fresh processes, one after another; each
+    prints its results as one JSON line.  Returns them, or exits with the
+    first failing child's status."""
+    import subprocess
+    runs = []
+    child_argv = [a for a in argv if not a.startswith("--processes")]
+    for p in range(args.processes):
+        print(f"[bench] process {p + 1} of {args.processes}", file=sys.stderr, flush=True)
+        proc = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), *child_argv, "--processes", "0",
+                               "--child"], stdout=subprocess.PIPE, text=True)
+        if proc.returncode != 0:
+            print(f"[bench] measuring process {p + 1} failed with status {proc.returncode}", file=sys.stderr)
+            sys.exit(proc.returncode if proc.returncode > 0 else 1)
+        runs.append(json.loads(proc.stdout.strip().splitlines()[-1]))
+    return runs
+
+
 def main(argv=None):
+    argv = list(sys.argv[1:] if argv is None else argv)
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3200)
-    ap.add_argument("--warmup", type=int, default=320)
-    ap.add_argument("--workload", default="2a2f_decode", choices=gen.WORKLOADS)
+    ap.add_argument("--steps", type=int, default=20, help="timed rounds per workload and process")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed rounds before them")
+    ap.add_argument("--workload", default="all",
+                    help="comma-separated workload names, or 'all' (" + ", ".join(gen.WORKLOADS) + ")")
+    ap.add_argument("--headline", default="2a2f_decode", choices=gen.WORKLOADS,
+                    help="the workload of the top-level value (the metric's E128/K8/H2048 decode round)")
+    ap.add_argument("--processes", type=int, default=3,
+                    help="fresh processes to take the median over (0: measure in this process)")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--combine", default="once", choices=["once", "per_stage", "per_stage_fp8"],
                     help="combine rounding: once (default), or per stage with BF16 or FP8 partials")
     ap.add_argument("--cached", action="store_true",
                     help="time rounds that reuse the previous layout (cached dispatch, unchanged routes)")
-    ap.add_argument("--graph-rounds", type=int, default=0, help="rounds per captured graph (default by size)")
+    ap.add_argument("--graph-rounds", type=int, default=0, help="most rounds per captured graph (default by size)")
     ap.add_argument("--cold-bytes", type=float, default=512e6, help="bytes the cold rotation spans")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work per setting for the headline workload's CPU baseline")
+    ap.add_argument("--cpu-budget-other", type=float, default=1.0,
+                    help="seconds per setting for the other workloads' CPU figures")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip launch-floor and copy probes")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
@@ -433,111 +649,85 @@ def main(argv=None):
         print("bench.py measures one GPU only: the dispatch/combine path runs every role on a single "
               "device, so there is no multi-GPU configuration to launch (use --gpus 1).", file=sys.stderr)
         return 2
-
-    import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    torch.cuda.set_device(0)
+    names = gen.WORKLOADS if args.workload == "all" else args.workload.split(",")
+    for n in names:
+        if n not in gen.WORKLOADS:
+            ap.error(f"unknown workload {n}")
+    if args.combine != "once":
+        names = [n for n in names if gen.instance_by_name(n).cfg.F >= 2]   # per stage needs two partitions
+        if not names:
+            ap.error("the per-stage combine needs a workload with two or more partitions")
+    headline = args.headline if args.headline in names else names[0]
 
     if args.copy_only:
+        import torch
+        torch.cuda.set_device(0)
         gbps = copy_bandwidth(args.copy_only << 20, reps=10)
         print(json.dumps({"copy_mib": args.copy_only, "copy_gbps": round(gbps, 1)}), flush=True)
         return 0
+    if args.child or args.processes == 0:
+        res = measure(names, args)
+        if args.child:
+            print(json.dumps(res), flush=True)
+            return 0
+        runs = [res]
+    else:
+        runs = run_children(args, argv)     # this process never touches the GPU
 
-    inst = gen.instance_by_name(args.workload)
-    cfg = inst.cfg
-    L = live_choices(inst)
-    if args.combine != "once" and cfg.F < 2:
-        print("the per-stage combine needs two or more partitions", file=sys.stderr)
-        return 2
-    nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else 0)
-    view = cfg.F == 1
-    print(f"[bench] {args.workload}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} "
-          f"alpha={cfg.alpha} dtype={cfg.dtype} L={L} bytes/round={nb['total']}", file=sys.stderr, flush=True)
-
-    S = max(1, math.ceil(args.cold_bytes / nb["total"]))
-    G = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
-    G = max(G, S) if S > 1 else G
-    G = int(math.ceil(G / S) * S)
-    sets = [RoundSet(inst, view, args.combine, args.cached)]
-    hot_us, _ = time_graph_rounds(sets, [0] * G, args.steps, args.warmup)
-    print(f"[bench] hot: {hot_us:.3f} us/round", file=sys.stderr, flush=True)
-    for _ in range(S - 1):
-        sets.append(RoundSet(inst, view, args.combine, args.cached))
-    cold_us, cold_blocks = time_graph_rounds(sets, [i % S for i in range(G)], args.steps, args.warmup)
-    print(f"[bench] cold ({S} sets, {G} rounds/graph): {cold_us:.3f} us/round (median of "
-          f"{len(cold_blocks)} blocks: {', '.join(f'{u:.3f}' for u in cold_blocks)})", file=sys.stderr, flush=True)
-    expert_us = time_identity_experts(sets[0])
-
-    kern = time_kernels_live(sets)
-    # the roofline kernel: the phase with the most algorithmic bytes among
-    # those that are one kernel (the combine always; the dispatch when the
-    # one-kernel path runs it)
-    row_cols = cfg.H * (1 if cfg.dtype == "fp8" else 2) // 16
-    fused = sum(cfg.T) <= 512 and sum(cfg.T) * cfg.K <= 4096 and cfg.E <= 256 and row_cols <= 2048
-    dom = "dispatch" if fused and nb["dispatch"] >= nb["combine"] else "combine"
-    dom_name = {"dispatch": "k_fused", "combine": "k_combine"}[dom]
-    if args.cached:
-        # the cached dispatch is one kernel at every size
-        dom = "dispatch" if nb["dispatch"] >= nb["combine"] else "combine"
-        dom_name = {"dispatch": "k_scatter_cached", "combine": "k_combine"}[dom]
-    if args.combine != "once":
-        # the per-stage combine is F stage-one and N stage-two launches: the
-        # phase as a whole
-        dom, dom_name = "combine", "k_partial+k_final"
-    dom_bytes = nb[dom]
-    dom_gbps = dom_bytes / (kern[dom] * 1e-6) / 1e9
-    mode = "_cached" if args.cached else ""
-    if args.combine != "once":
-        mode += "_" + args.combine
-    traffic = load_traffic(dom_name, args.workload, mode, {"k_partial": cfg.F, "k_final": cfg.N})
-
-    extras = {}
-    if not args.no_extras:
-        extras["launch_floor_us_per_round"] = round(launch_floor(), 3)
-        extras["copy_gbps"] = round(copy_bandwidth(), 1)
-
-    value = nb["total"] / (cold_us * 1e-6) / 1e9
-    res = {
+    per = aggregate(runs, names, args)
+    top = per[headline]
+    value = top["gbps"]
+    line = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(cold_us / 1e3, 6),
+        "ms_per_step": round(top["us_per_round"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
-                   "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
-                   "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
-                   "rounds_per_graph": G, "combine": args.combine, "cached_layout": bool(args.cached)},
-        "us_per_round": round(cold_us, 3),
-        "us_per_round_blocks": [round(u, 3) for u in cold_blocks],
-        "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
-        "us_per_round_hot": round(hot_us, 3),
-        "gbps_hot": round(nb["total"] / (hot_us * 1e-6) / 1e9, 2),
-        "bytes_per_round": nb["total"],
-        "kernels_us": {k: round(v, 3) for k, v in kern.items()},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbps, 2), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(dom_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(kern[dom], 3)},
+        "config": top["config"],
+        "us_per_round": top["us_per_round"],
+        "pct_peak": top["pct_peak"],
+        "us_per_round_hot": top["us_per_round_hot"],
+        "processes": len(runs),
+        "roofline": top["roofline"],
     }
-    res.update(extras)
-    res["identity_experts_us"] = round(expert_us, 3)
-    res["inputs_sha256"] = inst.digests()
+    if "gate_60pct" in top:
+        line["gate_60pct"] = top["gate_60pct"]
+    for k in ("launch_floor_us_per_round", "copy_gbps"):
+        if k in runs[0]:
+            line[k] = round(_median([r[k] for r in runs]), 3)
+    line["workloads"] = per
     if not args.no_cpu:
-        t_cpu, n = cpu_baseline(inst, args.cpu_budget)
-        res["cpu_baseline"] = {"value": round(nb["total"] / t_cpu / 1e9, 4), "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"{n} full rounds of {args.workload} (layout+dispatch+combine, "
-                                         f"{t_cpu * 1e3:.2f} ms/round, single-threaded C oracle, "
-                                         f"{cpu_model()})"}
-    print(json.dumps(res), flush=True)
+        import oracle
+        model = cpu_model()
+        for name in names:
+            inst = gen.instance_by_name(name)
+            ref = oracle.run_round(inst)
+            budget = args.cpu_budget if name == headline else args.cpu_budget_other
+            figs = {}
+            for par in (False, True):
+                t_cpu, n, threads = cpu_baseline(inst, budget, par, ref)
+                figs["all_cores" if par else "one_thread"] = (t_cpu, n, threads)
+            nb = per[name]["bytes_per_round"]
+            per[name]["cpu_oracle"] = {
+                k: {"gbps": round(nb / t / 1e9, 4), "ms_per_round": round(t * 1e3, 3), "rounds": n,
+                    "threads": th} for k, (t, n, th) in figs.items()}
+            if name == headline:
+                t, n, th = figs["all_cores"]
+                t1, n1, _ = figs["one_thread"]
+                line["cpu_baseline"] = {
+                    "value": round(nb / t / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+                    "sample": f"{n} full rounds of {name} (layout + dispatch + combine, {t * 1e3:.3f} ms/round; "
+                              f"row copy and combine on {th} OpenMP threads, counting and slots serial) on {model}; "
+                              f"single-threaded: {n1} rounds, {t1 * 1e3:.3f} ms/round, "
+                              f"{nb / t1 / 1e9:.4f} GB/s"}
+    print(json.dumps(line), flush=True)
     return 0
 
 

@@ -43,6 +43,15 @@ class Receive(ctypes.Structure):
                 ("ends", ctypes.c_void_p), ("receive_rows", ctypes.c_int64), ("receipt", Receipt)]
 
 
+class RoundInfo(ctypes.Structure):
+    _fields_ = [("round", ctypes.c_uint64), ("dispatch_path", ctypes.c_int32),
+                ("dispatch_kernels", ctypes.c_int32), ("combine_kernels", ctypes.c_int32),
+                ("tokens", ctypes.c_int32), ("layout_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32)]
+
+
+DISPATCH_PATHS = {0: "none", 1: "one_kernel", 2: "tiled", 3: "cached", 4: "empty"}
+
+
 class AfdError(RuntimeError):
     def __init__(self, status, what=""):
         self.status = status
@@ -66,6 +75,7 @@ SIGNATURES = {
     "afd_get_error": ([_P, _P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                        ctypes.POINTER(_I32)], _I32),
     "afd_get_partials": ([_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64)], _I32),
+    "afd_get_round_info": ([_P, ctypes.POINTER(RoundInfo)], _I32),
     "afd_status_string": ([_I32], ctypes.c_char_p),
 }
 

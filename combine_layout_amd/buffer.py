@@ -78,12 +78,34 @@ class Buffer:
         nat.check(self.lib.afd_create(ctypes.byref(self.cfg), _ptr(self.workspace), ws.value, ctypes.byref(ctx)),
                   "afd_create")
         self.ctx = ctx
-        for f, (rows, scales, roww) in enumerate(self.arenas):
-            nat.check(self.lib.afd_bind_partition(self.ctx, f, _ptr(rows), _ptr(scales), _ptr(roww),
-                                                  self.rows_cap), "afd_bind_partition")
+        self._bind()
         self._round_refs = {}
         self._out = [None] * num_sources
         self._T = [0] * num_sources
+
+    def _bind(self):
+        for f, (rows, scales, roww) in enumerate(self.arenas):
+            nat.check(self.lib.afd_bind_partition(self.ctx, f, _ptr(rows), _ptr(scales), _ptr(roww),
+                                                  self.rows_cap), "afd_bind_partition")
+
+    def bind_arenas(self, bucket):
+        """Allocate and bind receive arenas sized for `bucket` tokens per
+        source.  Allowed between rounds, or after a worker_receive refused
+        the round for a smaller arena (then receive again)."""
+        rb = self.rows_bound(bucket)
+        arenas = []
+        for _ in range(self.F):
+            rows = torch.empty((rb, self.H), dtype=torch.uint8 if self.fp8 else torch.bfloat16, device=self.device)
+            scales = torch.empty((rb, self.H // 128), dtype=torch.float32, device=self.device) if self.fp8 else None
+            arenas.append((rows, scales, torch.empty(rb, dtype=torch.float32, device=self.device)))
+        old = self.arenas, self.rows_cap
+        self.arenas, self.rows_cap = arenas, rb
+        try:
+            self._bind()
+        except nat.AfdError:
+            self.arenas, self.rows_cap = old
+            self._bind()
+            raise
 
     # -- helpers -------------------------------------------------------------
     def _ws_view(self, ptr: int, nbytes: int) -> torch.Tensor:
@@ -200,6 +222,16 @@ class Buffer:
         nat.check(self.lib.afd_get_partials(self.ctx, s, f, ctypes.byref(ptr), ctypes.byref(rb)), "get_partials")
         T = self._T[s]
         return self._ws_view(ptr.value, max(T, 1) * rb.value).view(-1, rb.value)[:T]
+
+    def round_info(self) -> dict:
+        """Which kernels the last enqueued round runs: dispatch path
+        ("one_kernel", "tiled", "cached", "empty"), kernel counts, tokens and
+        layout tiles."""
+        ri = nat.RoundInfo()
+        nat.check(self.lib.afd_get_round_info(self.ctx, ctypes.byref(ri)), "get_round_info")
+        return {"round": ri.round, "dispatch_path": nat.DISPATCH_PATHS.get(ri.dispatch_path, ri.dispatch_path),
+                "dispatch_kernels": ri.dispatch_kernels, "combine_kernels": ri.combine_kernels,
+                "tokens": ri.tokens, "layout_tiles": ri.layout_tiles, "tile_tokens": ri.tile_tokens}
 
     # -- errors / teardown ---------------------------------------------------
     def get_error(self, clear=False):

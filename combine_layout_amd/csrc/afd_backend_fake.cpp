@@ -58,6 +58,8 @@ int be_launch_dispatch(const RoundPlan &p, void *)
     }
     if (p.cached) {
         logf("dispatch cached ntok=%d T=%s", p.ntok, srcs.c_str());
+    } else if (p.empty) {
+        logf("dispatch empty E=%d T=%s", p.E, srcs.c_str());
     } else if (p.fused) {
         logf("dispatch fused=1 ntok=%d nblk=%d T=%s", p.ntok, p.nblk, srcs.c_str());
     } else {

@@ -61,6 +61,9 @@ struct afd_ctx {
     bool round_cached = false;     // this round reuses the last layout
     RoundPlan plan;
 
+    // how the last round whose dispatch work was enqueued runs
+    afd_round_info info{};
+
     // the last layout whose dispatch work was enqueued (for cached rounds)
     bool layout_valid = false;
     int layout_bucket = 0;
@@ -170,11 +173,13 @@ void build_plan(afd_ctx *c)
     p.tok_off[0] = 0;
     for (int s = 0; s < p.N; ++s) p.tok_off[s + 1] = p.tok_off[s] + c->T[s];
     p.ntok = p.tok_off[p.N];
-    p.fused = p.ntok <= kFusedMaxTokens && int64_t(p.ntok) * p.K <= kFusedMaxIds && p.E <= kFusedMaxExperts &&
-              p.row_bytes / 16 <= kFusedMaxCols;
+    // a round without tokens has empty expert ranges at any E and H: its
+    // dispatch only clears ends[]
+    p.empty = p.ntok == 0;
+    p.fused = !p.empty && p.ntok <= kFusedMaxTokens && int64_t(p.ntok) * p.K <= kFusedMaxIds &&
+              p.E <= kFusedMaxExperts && p.row_bytes / 16 <= kFusedMaxCols;
     p.tile = place_sources(c->T, p.N, p.voff);
-    p.nblk = p.fused ? 1 : p.voff[p.N] / p.tile;   // the one-kernel dispatch has no tiles
-    if (p.nblk < 1) p.nblk = 1;
+    p.nblk = p.fused || p.empty ? 1 : p.voff[p.N] / p.tile;   // the one-kernel dispatch has no tiles
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];
     for (int f = 0; f < p.F; ++f) {
         p.rows[f] = c->part[f].rows;
@@ -189,9 +194,50 @@ void build_plan(afd_ctx *c)
     p.partials = g.combine != AFD_COMBINE_ONCE ? reinterpret_cast<uint8_t *>(c->ws + c->wp.partials) : nullptr;
 }
 
+// Which kernels the round just enqueued runs (mirrors the executor's choice
+// in be_launch_dispatch and the reply/collect launches).
+void record_info(afd_ctx *c)
+{
+    const RoundPlan &p = c->plan;
+    afd_round_info &i = c->info;
+    i = afd_round_info{};
+    i.round = c->round;
+    i.tokens = p.ntok;
+    if (p.cached) {
+        i.dispatch_path = AFD_PATH_CACHED;
+        i.dispatch_kernels = p.ntok > 0 ? 1 : 0;
+    } else if (p.empty) {
+        i.dispatch_path = AFD_PATH_EMPTY;
+        i.dispatch_kernels = 1;
+    } else if (p.fused) {
+        i.dispatch_path = AFD_PATH_ONE_KERNEL;
+        i.dispatch_kernels = 1;
+    } else {
+        i.dispatch_path = AFD_PATH_TILED;
+        i.dispatch_kernels = 2;
+        i.layout_tiles = p.nblk;
+        i.tile_tokens = p.tile;
+    }
+    if (p.ntok > 0) {
+        if (p.combine == AFD_COMBINE_ONCE) {
+            i.combine_kernels = 1;
+        } else {
+            i.combine_kernels = p.F;
+            for (int s = 0; s < p.N; ++s) i.combine_kernels += p.tok_off[s + 1] > p.tok_off[s] ? 1 : 0;
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+afd_status afd_get_round_info(const afd_ctx *c, afd_round_info *info)
+{
+    if (!c || !info) return AFD_E_ARG;
+    *info = c->info;
+    return AFD_OK;
+}
 
 const char *afd_status_string(afd_status st)
 {
@@ -217,6 +263,17 @@ afd_status afd_query(const afd_config *cfg, int32_t bucket, size_t *workspace_by
     return AFD_OK;
 }
 
+static void init_ctx(afd_ctx *c, const afd_config *cfg, void *workspace, size_t workspace_bytes,
+                     const WorkspacePlan &wp)
+{
+    c->cfg = *cfg;
+    c->E_loc = cfg->num_experts / cfg->num_partitions;
+    c->row_bytes = int64_t(cfg->hidden) * (cfg->dtype == AFD_FP8_E4M3 ? 1 : 2);
+    c->ws = static_cast<char *>(workspace);
+    c->ws_bytes = workspace_bytes;
+    c->wp = wp;
+}
+
 afd_status afd_create(const afd_config *cfg, void *workspace, size_t workspace_bytes, afd_ctx **out)
 {
     if (!out) return AFD_E_ARG;
@@ -228,12 +285,7 @@ afd_status afd_create(const afd_config *cfg, void *workspace, size_t workspace_b
     if (workspace_bytes < wp.total) return AFD_E_CAPACITY;
     afd_ctx *c = new (std::nothrow) afd_ctx;
     if (!c) return AFD_E_ARG;
-    c->cfg = *cfg;
-    c->E_loc = cfg->num_experts / cfg->num_partitions;
-    c->row_bytes = int64_t(cfg->hidden) * (cfg->dtype == AFD_FP8_E4M3 ? 1 : 2);
-    c->ws = static_cast<char *>(workspace);
-    c->ws_bytes = workspace_bytes;
-    c->wp = wp;
+    init_ctx(c, cfg, workspace, workspace_bytes, wp);
     if (be_init_workspace(workspace, wp) != 0) {
         delete c;
         return AFD_E_HIP;
@@ -247,7 +299,9 @@ afd_status afd_bind_partition(afd_ctx *c, int32_t f, void *rows, float *scales, 
 {
     if (!c) return AFD_E_ARG;
     if (f < 0 || f >= c->cfg.num_partitions) return AFD_E_ARG;
-    if (c->phase != kIdle) return AFD_E_ORDER;
+    // allowed until a round's dispatch work is enqueued, so a receive that
+    // failed (a smaller arena than the bucket needs) can be retried
+    if (c->phase != kIdle && c->launched) return AFD_E_ORDER;
     if (rows_cap < 0) return AFD_E_ARG;
     if (rows_cap > 0) {
         if (!rows || !row_weights || !aligned(rows, 16) || !aligned(row_weights, 4)) return AFD_E_ARG;
@@ -366,6 +420,7 @@ afd_status afd_worker_receive(afd_ctx *c, int32_t f, int32_t bucket, int32_t rhc
         c->plan.cached = c->round_cached;
         if (be_launch_dispatch(c->plan, stream) != 0) return AFD_E_HIP;
         c->launched = true;
+        record_info(c);
         c->layout_valid = true;
         c->layout_bucket = c->bucket;
         for (int q = 0; q < g.num_sources; ++q) c->layout_T[q] = c->T[q];

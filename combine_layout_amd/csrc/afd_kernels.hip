@@ -1421,6 +1421,12 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     }
 }
 
+// Dispatch of a round without tokens: every expert's range is empty.
+__global__ __launch_bounds__(256) void k_zero_ends(int32_t *ends, int E)
+{
+    for (int e = threadIdx.x; e < E; e += 256) ends[e] = 0;
+}
+
 __global__ __launch_bounds__(256) void k_copy(const u32x4 *src, u32x4 *dst, int64_t n)
 {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
@@ -1574,12 +1580,16 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         default: return launch_cached_v<8>(a, lpt, st);
         }
     }
+    if (p.empty) {
+        hipLaunchKernelGGL(k_zero_ends, dim3(1), dim3(256), 0, st, p.ends, p.E);
+        return launched_ok();
+    }
     if (p.fused) {
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.h.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
         const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4;
-        dim3 grid(p.ntok > 0 ? p.ntok : 1);
+        dim3 grid(p.ntok);
         switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);
         case 2: return launch_fused_v<2>(a, k32, grid, lds, st);

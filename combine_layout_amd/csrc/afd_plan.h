@@ -90,6 +90,7 @@ struct RoundPlan {
     int ntok = 0;
     int tok_off[kMaxSources + 1] = {};
     bool fused = false;      // one-kernel dispatch
+    bool empty = false;      // no tokens: the dispatch only clears ends[]
     bool cached = false;     // scatter from the slot map of the last layout
     int nblk = 0;            // layout tiles (split path)
     int tile = 0;            // tokens per layout tile
@@ -127,7 +128,7 @@ struct TileRec {
 
 inline int layout_tiles(const RoundPlan &p, TileRec *out)
 {
-    if (p.fused || p.cached || p.nblk > kLayoutMaxTiles) return 0;
+    if (p.fused || p.cached || p.empty || p.nblk > kLayoutMaxTiles) return 0;
     for (int b = 0; b < p.nblk; ++b) {
         int s = 0;   // the last source whose span starts at or before the tile (empty spans are skipped)
         while (s + 1 < p.N && b * p.tile >= p.voff[s + 1]) ++s;

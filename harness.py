@@ -1,8 +1,10 @@
-"""GPU-side test harness: uploads a generated instance, runs one round through
-the library's Python binding (the C ABI), and plays the FFN with identity
-experts written in torch (expert e scales its rows by s_e = 1 + e/E and rounds
-to bfloat16) -- the stand-in for the caller's expert computation, which is
-not part of the library."""
+"""GPU-side harness shared by the tests, the smoke check and the benchmark:
+uploads a generated instance, runs one round through the library's Python
+binding (the C ABI), and plays the FFN with identity experts written in
+torch (expert e scales its rows by s_e = 1 + e/E and rounds to bfloat16) --
+the stand-in for the caller's expert computation, which is not part of the
+library.  It holds none of the exchange's arithmetic and never touches the
+CPU oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -101,6 +103,17 @@ def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, k
         buf.worker_reply(f, replies[f], rec.receipt)
     outs_t = [buf.source_collect(s, view=view) for s in range(cfg.N)]
     torch.cuda.synchronize()
+    r = read_round(cfg, recs, replies, outs_t, keep_arrays)
+    if buf.combine != "once":
+        r.partials = [[buf.partials(s, f).cpu().numpy().copy() for f in range(cfg.F)] for s in range(cfg.N)]
+    r.out_tensors = outs_t
+    r.buf = buf
+    return r
+
+
+def read_round(cfg, recs, replies, outs, keep_arrays=True):
+    """Copy a completed round's receive views, replies and outputs to the
+    host (the stream must be synchronised)."""
     r = GpuRound()
     for f, rec in enumerate(recs):
         r.ends.append(rec.ends.cpu().numpy().copy())
@@ -114,9 +127,5 @@ def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, k
             r.row_weights.append(rec.weights.cpu().numpy().copy())
             r.scales.append(rec.scales.cpu().numpy().copy() if rec.scales is not None else None)
             r.replies.append(replies[f].view(torch.int16).cpu().numpy().view(np.uint16).copy())
-    r.out = [o.view(torch.int16).cpu().numpy().view(np.uint16).copy() for o in outs_t]
-    if buf.combine != "once":
-        r.partials = [[buf.partials(s, f).cpu().numpy().copy() for f in range(cfg.F)] for s in range(cfg.N)]
-    r.out_tensors = outs_t
-    r.buf = buf
+    r.out = [o.view(torch.int16).cpu().numpy().view(np.uint16).copy() for o in outs]
     return r

@@ -147,30 +147,40 @@ typedef struct {
 afd_status afd_query(const afd_config *cfg, int32_t bucket, size_t *workspace_bytes, int64_t *rows_bound);
 
 /*
- * afd_create: make a context over a caller-owned device workspace of at
- * least afd_query bytes (256-byte aligned).  Initialises the workspace's
- * error word and counters with a synchronous device write.  The workspace
- * must stay allocated until afd_destroy.
+ * afd_create (contract page: the Buffer, which owns the exchange's state and
+ * storage; "Initialization and close() are ... outside CUDA capture"): make a
+ * context over a caller-owned device workspace of at least afd_query bytes
+ * (256-byte aligned).  Initialises the workspace's error word and counters
+ * with a synchronous device write, so it is not for a capturing stream.  The
+ * workspace must stay allocated until afd_destroy.
  * Errors: AFD_E_SHAPE (config), AFD_E_ARG (NULL or misaligned pointer),
  * AFD_E_CAPACITY (workspace too small), AFD_E_HIP.
  */
 afd_status afd_create(const afd_config *cfg, void *workspace, size_t workspace_bytes, afd_ctx **out);
 
 /*
- * afd_bind_partition: bind partition f's receive arena (device, caller-owned):
+ * afd_bind_partition (contract page, "Graphs, streams and lifetime": receive
+ * tensors are distinct from the registered transport buffers, and FFN
+ * bounds count the Attention sources): bind partition f's receive arena
+ * (device, caller-owned), sized for the conservative receive bound:
  *   rows        [rows_cap, H] BF16 or E4M3 (16-byte aligned)
  *   scales      [rows_cap, H/128] FP32, FP8 only (NULL for BF16)
  *   row_weights [rows_cap] FP32
- * Call between rounds, never while a stream is being captured.  Every round
- * needs rows_cap >= R_max(bucket).
- * Errors: AFD_E_ARG (index, NULL or misaligned pointer), AFD_E_ORDER (inside
- * a round).
+ * Call between rounds, or inside a round until its first afd_worker_receive
+ * has enqueued the dispatch work (so a receive that failed with
+ * AFD_E_CAPACITY can be retried after binding a larger arena); never while a
+ * stream is being captured.  Every round needs rows_cap >= R_max(bucket).
+ * Errors: AFD_E_ARG (index, NULL or misaligned pointer), AFD_E_ORDER (the
+ * round's dispatch work is already enqueued).
  */
 afd_status afd_bind_partition(afd_ctx *ctx, int32_t f, void *rows, float *scales, float *row_weights,
                               int64_t rows_cap);
 
-/* afd_destroy: synchronise the device and free the host context.  Frees no
- * device memory (the caller owns it).  NULL is accepted. */
+/* afd_destroy (contract page: close() synchronises outstanding work and
+ * frees the Buffer's storage; graphs are destroyed before it): synchronise
+ * the device and free the host context.  Frees no device memory (the caller
+ * owns it).  Replaying a graph that captured calls on the context after
+ * this is undefined.  NULL is accepted. */
 afd_status afd_destroy(afd_ctx *ctx);
 
 /*
@@ -290,6 +300,35 @@ afd_status afd_get_error(afd_ctx *ctx, void *stream, int32_t clear, int32_t *cod
  * nothing.  Errors: AFD_E_ARG (index, NULL, or AFD_COMBINE_ONCE).
  */
 afd_status afd_get_partials(afd_ctx *ctx, int32_t s, int32_t f, const void **rows, int64_t *row_bytes);
+
+/* How a round's dispatch ran (afd_round_info.dispatch_path). */
+typedef enum {
+    AFD_PATH_NONE = 0,        /* no dispatch enqueued yet */
+    AFD_PATH_ONE_KERNEL = 1,  /* small rounds: layout and scatter in one kernel */
+    AFD_PATH_TILED = 2,       /* layout kernel over token tiles, then the scatter */
+    AFD_PATH_CACHED = 3,      /* afd_source_dispatch_cached: the scatter alone */
+    AFD_PATH_EMPTY = 4        /* no tokens: ends[] cleared */
+} afd_dispatch_path;
+
+typedef struct {
+    uint64_t round;            /* the round described (0: none yet) */
+    int32_t dispatch_path;     /* afd_dispatch_path */
+    int32_t dispatch_kernels;  /* kernels the round's dispatch launched */
+    int32_t combine_kernels;   /* kernels its combine launches: 1 (AFD_COMBINE_ONCE
+                                  with tokens), F + sources with tokens (per stage), 0 */
+    int32_t tokens;            /* tokens over every source */
+    int32_t layout_tiles;      /* AFD_PATH_TILED: layout workgroups; else 0 */
+    int32_t tile_tokens;       /* AFD_PATH_TILED: token slots per layout tile; else 0 */
+} afd_round_info;
+
+/*
+ * afd_get_round_info (design page, "3:1 Attention:FFN: where the time goes",
+ * which accounts a round kernel by kernel): which kernels the last round
+ * whose dispatch work was enqueued runs, for per-kernel accounting.  Host
+ * state only; enqueues nothing and never synchronises.
+ * Errors: AFD_E_ARG (NULL).
+ */
+afd_status afd_get_round_info(const afd_ctx *ctx, afd_round_info *info);
 
 /* afd_status_string: a static description of a status. */
 const char *afd_status_string(afd_status st);

@@ -19,30 +19,51 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "afd_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+# the same source built with -fopenmp: the row copy and the combine on
+# several threads, for the benchmark's all-cores CPU baseline only
+_OMP_LIB_PATH = os.path.join(_HERE, "_build", "liboracle_omp.so")
 _lib = None
+_serial_lib = None
 
 ROUTE_RANGE, ROUTE_NEG, ROUTE_DUP = 1, 2, 3
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (plain C99, no contraction of a*b+c)."""
-    if not force and os.path.exists(_LIB_PATH):
+    """Compile the oracle with gcc (plain C99, no contraction of a*b+c), and
+    its OpenMP timing build."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.exists(_OMP_LIB_PATH):
         return _LIB_PATH
     os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
-                           "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp, "-lm"])
-    os.replace(tmp, _LIB_PATH)
+    for path, extra in ((_LIB_PATH, ["-Wno-unknown-pragmas"]), (_OMP_LIB_PATH, ["-fopenmp"])):
+        tmp = path + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-Werror", *extra, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, path)
     return _LIB_PATH
 
 
 def lib():
-    global _lib
+    global _lib, _serial_lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
-        _lib = ctypes.CDLL(_LIB_PATH)
+        _serial_lib = _lib = ctypes.CDLL(_LIB_PATH)
     return _lib
+
+
+def set_parallel(on: bool) -> int:
+    """Run the following calls on the OpenMP timing build (on=True) or the
+    plain single-threaded build; returns the threads the row copy and the
+    combine use.  Benchmark only: the tests use the plain build."""
+    global _lib
+    lib()
+    if on:
+        if not os.path.exists(_OMP_LIB_PATH):
+            build()
+        _lib = ctypes.CDLL(_OMP_LIB_PATH)
+    else:
+        _lib = _serial_lib
+    return int(_lib.orc_threads())
 
 
 def _p(a: np.ndarray):
@@ -92,16 +113,21 @@ def layout(T: Sequence[int], ids: np.ndarray, E: int, F: int, K: int, alpha: int
 
 
 def dispatch(x_all: np.ndarray, w_all: np.ndarray, lay: Layout, F: int, rows_cap: Sequence[int],
-             fill_rows: Optional[int] = None):
+             fill_rows: Optional[int] = None, out=None):
     """Expert-major rows and per-row weights for every partition.
 
     x_all: [ntok, H] uint16 (bf16 bits) or uint8 (e4m3 bits).  Rows that are
-    not targets keep ``fill_rows`` bytes (0 if None) and weight NaN."""
+    not targets keep ``fill_rows`` bytes (0 if None) and weight NaN.  With
+    ``out`` = (rows, roww) from an earlier call, those arrays are written
+    again in place (rows that are not targets keep what they held)."""
     ntok, K = lay.slot_part.shape
     x_all = np.ascontiguousarray(x_all)
     row_bytes = x_all.shape[1] * x_all.itemsize if ntok else 0
-    rows = [np.full((rows_cap[f], x_all.shape[1]), fill_rows or 0, dtype=x_all.dtype) for f in range(F)]
-    roww = [np.full(rows_cap[f], np.nan, np.float32) for f in range(F)]
+    if out is not None:
+        rows, roww = out
+    else:
+        rows = [np.full((rows_cap[f], x_all.shape[1]), fill_rows or 0, dtype=x_all.dtype) for f in range(F)]
+        roww = [np.full(rows_cap[f], np.nan, np.float32) for f in range(F)]
     if ntok:
         lib().orc_dispatch(ctypes.c_int64(ntok), K, _p(x_all), ctypes.c_int64(row_bytes),
                            _p(np.ascontiguousarray(w_all, np.float32)), _p(lay.slot_part),
@@ -110,11 +136,12 @@ def dispatch(x_all: np.ndarray, w_all: np.ndarray, lay: Layout, F: int, rows_cap
 
 
 def dispatch_scales(T: Sequence[int], scale_src: List[np.ndarray], strides: List[tuple], G: int,
-                    lay: Layout, F: int, rows_cap: Sequence[int]):
-    """scale_src[s]: float32 buffer of source s; strides[s] = (stride_t, stride_g) in elements."""
+                    lay: Layout, F: int, rows_cap: Sequence[int], out=None):
+    """scale_src[s]: float32 buffer of source s; strides[s] = (stride_t, stride_g) in elements.
+    ``out``: scale arrays of an earlier call, written again in place."""
     T_arr = np.ascontiguousarray(T, dtype=np.int32)
     ntok, K = lay.slot_part.shape
-    scales = [np.full((rows_cap[f], G), np.nan, np.float32) for f in range(F)]
+    scales = out if out is not None else [np.full((rows_cap[f], G), np.nan, np.float32) for f in range(F)]
     st = np.ascontiguousarray([s[0] for s in strides], np.int64)
     sg = np.ascontiguousarray([s[1] for s in strides], np.int64)
     srcs = [np.ascontiguousarray(a, np.float32) if a is not None else np.zeros(1, np.float32) for a in scale_src]
@@ -134,9 +161,11 @@ def identity_experts(fp8: bool, E: int, F: int, f: int, alpha: int, H: int, ends
     return y
 
 
-def combine(w_all: np.ndarray, lay: Layout, H: int, ys: List[np.ndarray]) -> np.ndarray:
+def combine(w_all: np.ndarray, lay: Layout, H: int, ys: List[np.ndarray], out=None) -> np.ndarray:
+    """``out``: a uint16 [ntok, H] array of an earlier call, overwritten."""
     ntok, K = lay.slot_part.shape
-    out = np.zeros((ntok, H), np.uint16)
+    if out is None:
+        out = np.zeros((ntok, H), np.uint16)
     if ntok:
         ys = [np.ascontiguousarray(y, np.uint16) for y in ys]
         lib().orc_combine(ctypes.c_int64(ntok), K, H, _p(np.ascontiguousarray(w_all, np.float32)),

@@ -8,8 +8,12 @@
  * CPU-baseline leg load it.  It shares no source, header, table or helper
  * with the GPU path.
  *
- * Everything here is single-threaded, plain loops, in the order the method
- * defines it.  Build: gcc -std=c99 -O2 -ffp-contract=off -fPIC -shared.
+ * Everything here is plain loops, in the order the method defines it, and
+ * single-threaded.  Build: gcc -std=c99 -O2 -ffp-contract=off -fPIC -shared.
+ * A second build with -fopenmp exists for timing only: it runs the row copy
+ * and the combine's token loop on several threads (every token's rows and
+ * output are its own, so the results are the same bits); counting, the
+ * aligned prefix and the slots stay serial.
  *
  * Pins (tests/): layout against an independent brute-force sort and
  * invariants; combine against the float64 closed form with identity experts,
@@ -30,6 +34,9 @@
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_OK 0
 #define ORC_BAD_CONFIG (-1)
@@ -248,6 +255,7 @@ void orc_dispatch(int64_t ntok, int K, const uint8_t *x, int64_t row_bytes, cons
 {
     int64_t g;
     int k;
+#pragma omp parallel for private(k) schedule(static)
     for (g = 0; g < ntok; ++g) {
         for (k = 0; k < K; ++k) {
             int32_t f = slot_part[g * K + k];
@@ -342,7 +350,10 @@ void orc_combine(int64_t ntok, int K, int H, const float *w, const int32_t *slot
 {
     int64_t g;
     int k, h;
-    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+#pragma omp parallel private(k, h)
+    {
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);   /* one accumulator row per thread */
+#pragma omp for schedule(static)
     for (g = 0; g < ntok; ++g) {
         for (h = 0; h < H; ++h) acc[h] = 0.0f;
         for (k = 0; k < K; ++k) {
@@ -358,6 +369,18 @@ void orc_combine(int64_t ntok, int K, int H, const float *w, const int32_t *slot
         for (h = 0; h < H; ++h) out[g * H + h] = f32_to_bf16_rne(acc[h]);
     }
     free(acc);
+    }
+}
+
+/* Threads the row copy and the combine use: 1, or the OpenMP team size in
+ * the timing build. */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* Exposed for the number-format pins. */

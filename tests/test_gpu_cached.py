@@ -21,8 +21,8 @@ def _gpu():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from tests import gpu_harness
-    return gpu_harness
+    import harness
+    return harness
 
 
 def _with_ids(new, old):

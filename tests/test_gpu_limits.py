@@ -23,8 +23,8 @@ def _gpu():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from tests import gpu_harness
-    return gpu_harness
+    import harness
+    return harness
 
 
 def _run(inst, combine="once", rhc=False):
@@ -133,3 +133,32 @@ def test_wide_fp8_rows_cached(combine):
     g = h.run_round(b, buf, cached=True)
     hyb = gen.Instance(b.cfg, [dataclasses.replace(y, ids=x.ids) for x, y in zip(a.sources, b.sources)])
     assert check_round(hyb, g, oracle.run_round(hyb, rows_cap=g.receive_rows, combine_mode=combine)) == 0
+
+
+EMPTY_OFF_FUSED = [dict(E=512, F=2, K=8, H=256, dtype="bf16"),    # more experts than the one-kernel dispatch takes
+                   dict(E=16, F=2, K=4, H=16640, dtype="bf16"),   # rows wider than it takes
+                   dict(E=512, F=4, K=4, H=16384, dtype="fp8")]
+
+
+@pytest.mark.parametrize("kw", EMPTY_OFF_FUSED, ids=lambda d: f"E{d['E']}-H{d['H']}-{d['dtype']}")
+def test_all_empty_round_off_the_one_kernel_path(kw):
+    """A round in which every source is empty, after a round with tokens on the
+    same buffer: ends[] must be all zero again (not the last round's), host
+    counts zero and the exact receive size zero, at expert counts and row
+    widths the one-kernel dispatch does not take."""
+    h = _gpu()
+    from tests.test_gpu_parity import check_round
+    full = gen.random_small(1210, N=2, alpha=8, T=[30, 700], p_skip=0.1, bucket=700, **kw)
+    buf = h.make_buffer(full)
+    print(f"[limits empty] {kw}", flush=True)
+    g = h.run_round(full, buf, keep_arrays=False)
+    assert any(int(e[-1]) > 0 for e in g.ends)
+    empty = gen.generate(dataclasses.replace(full.cfg, T=[0, 0]))
+    for rhc in (True, False):
+        g = h.run_round(empty, buf, rhc=rhc)
+        ref = oracle.run_round(empty, rows_cap=g.receive_rows)
+        assert check_round(empty, g, ref) == 0
+        assert all(np.all(e == 0) for e in g.ends)
+        if rhc:
+            assert all(r == 0 for r in g.receive_rows)
+            assert all(all(c == 0 for c in hc) for hc in g.host_counts)

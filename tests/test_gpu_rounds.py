@@ -20,8 +20,8 @@ def _gpu():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from tests import gpu_harness
-    return gpu_harness
+    import harness
+    return harness
 
 
 def _small(seed, **kw):
@@ -35,42 +35,42 @@ def _check(inst, g, ref):
     return check_round(inst, g, ref)
 
 
-def test_graph_replay_with_inputs_changed_in_place():
+def _graph_rounds(base, view=False):
+    """Capture a round of `base`'s shapes as two graphs (dispatch + receive,
+    then reply + collect) after an eager warm-up round; returns a function
+    that copies an instance of the same shapes into the captured inputs in
+    place, replays both graphs (identity-expert replies computed eagerly in
+    between) and returns the round read back to the host."""
     h = _gpu()
     import torch
-    inst0 = _small(1)
-    cfg = inst0.cfg
-    buf = h.make_buffer(inst0)
-    dev = h.upload(inst0)
-    outs = [torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda") for T in cfg.T]
-    # warm-up round (eager), then capture dispatch+receive and reply+collect
-    h.run_round(inst0, buf, dev, keep_arrays=False, outs=outs)
+    cfg = base.cfg
+    buf = h.make_buffer(base)
+    dev = h.upload(base)
+    outs = [torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda") for T in cfg.T] if cfg.F > 1 else None
+    h.run_round(base, buf, dev, keep_arrays=False, outs=outs, view=view)
     torch.cuda.synchronize()
     replies = [torch.empty((buf.rows_bound(cfg.bucket), cfg.H), dtype=torch.bfloat16, device="cuda")
                for _ in range(cfg.F)]
     g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    recs = []
     with torch.cuda.graph(g1):
         for s, (x, ids, w, sc) in enumerate(dev):
-            buf.source_dispatch(s, x, ids, w, sc, bucket=cfg.bucket, out=outs[s])
+            buf.source_dispatch(s, x, ids, w, sc, bucket=cfg.bucket, out=outs[s] if outs else None)
         recs = [buf.worker_receive(f, bucket=cfg.bucket) for f in range(cfg.F)]
     with torch.cuda.graph(g2):
         for f in range(cfg.F):
             buf.worker_reply(f, replies[f], recs[f].receipt)
-        for s in range(cfg.N):
-            buf.source_collect(s)
+        results = [buf.source_collect(s, view=view) for s in range(cfg.N)]
     torch.cuda.synchronize()
-    for rep in range(4):
-        inst = _small(100 + rep)
+
+    def replay(inst):
         for (x, ids, w, sc), src in zip(dev, inst.sources):
-            x.view(torch.int16).copy_(torch.from_numpy(src.x.view(np.int16)))
+            if cfg.dtype == "fp8":
+                x.copy_(torch.from_numpy(src.x))
+                sc.copy_(torch.from_numpy(src.scale))
+            else:
+                x.view(torch.int16).copy_(torch.from_numpy(src.x.view(np.int16)))
             ids.copy_(torch.from_numpy(src.ids))
             w.copy_(torch.from_numpy(src.weights))
-        if rep == 3:
-            for (x, ids, w, sc) in dev:
-                ids.fill_(-1)          # every choice inactive
-            for src in inst.sources:
-                src.ids[:] = -1
         torch.cuda.synchronize()
         g1.replay()
         torch.cuda.synchronize()
@@ -78,20 +78,65 @@ def test_graph_replay_with_inputs_changed_in_place():
             replies[f].copy_(h.identity_replies(cfg, rec, f))
         g2.replay()
         torch.cuda.synchronize()
-        r = h.GpuRound()
-        for f, rec in enumerate(recs):
-            r.ends.append(rec.ends.cpu().numpy().copy())
-            r.host_counts.append(None)
-            r.receive_rows.append(rec.receive_rows)
-            r.rows.append(rec.rows.view(torch.int16).cpu().numpy().view(np.uint16).copy())
-            r.row_weights.append(rec.weights.cpu().numpy().copy())
-            r.scales.append(None)
-            r.replies.append(replies[f].view(torch.int16).cpu().numpy().view(np.uint16).copy())
-        r.out = [o.view(torch.int16).cpu().numpy().view(np.uint16).copy() for o in outs]
+        return h.read_round(cfg, recs, replies, results)
+
+    return buf, replay
+
+
+# (name, instance): the one-kernel dispatch at a small bucket and at the
+# decode workload's bucket of 2048, the tiled layout + scatter at the FP8
+# prefill workload, and the single-partition view at the 3A:1F workload
+REPLAY_CASES = ["small_one_kernel", "2a2f_decode", "2a2f_fp8_prefill", "3a1f_e96_view"]
+
+
+def _replay_base(name):
+    return _small(1) if name == "small_one_kernel" else gen.instance_by_name(name)
+
+
+@pytest.mark.parametrize("name", REPLAY_CASES)
+def test_graph_replay_with_inputs_changed_in_place(name):
+    """API contract page, "Graphs, streams and lifetime": a captured round
+    replayed with payloads and ids changed in place, inactive choices as -1.
+    Replays: two fresh instances; every choice -1; invalid ids (the
+    sanitised result, and the sticky first offender); a clean replay (the
+    word stays set: "invalid routes ... including on graph replay"); after
+    clearing it, a clean replay leaves it clear.  Every replay is compared
+    with the oracle on the same inputs."""
+    import dataclasses
+    base = _replay_base(name)
+    cfg = base.cfg
+    view = cfg.F == 1
+    buf, replay = _graph_rounds(base, view=view)
+
+    def variant(i):
+        return gen.generate(dataclasses.replace(cfg, seed=cfg.seed + 100 + i))
+
+    def run(inst, tag):
+        print(f"[replay] {name} {tag}", flush=True)
+        r = replay(inst)
         ref = oracle.run_round(inst, rows_cap=r.receive_rows)
-        assert _check(inst, r, ref) == 0, f"replay {rep}"
-        if rep == 3:
-            assert all(np.all(o == 0) for o in r.out)
+        assert _check(inst, r, ref) == 0, tag
+        return r
+
+    for i in range(2):
+        run(variant(i), f"fresh {i}")
+        assert buf.get_error()[0] == 0
+    skipped = variant(2)
+    for src in skipped.sources:
+        src.ids[:] = -1
+    r = run(skipped, "all -1")
+    assert all(np.all(o == 0) for o in r.out)
+    assert all(np.all(e == 0) for e in r.ends)
+    bad = _inject(variant(3), np.random.default_rng(cfg.seed), n_bad=12)
+    ids = np.concatenate([s.ids for s in bad.sources])
+    err = oracle.layout(cfg.T, ids, cfg.E, cfg.F, cfg.K, cfg.alpha).err
+    assert err[0] != 0
+    run(bad, "invalid ids")
+    assert buf.get_error() == err
+    run(variant(4), "clean after invalid")
+    assert buf.get_error(clear=True) == err                 # sticky across replays until cleared
+    run(variant(5), "clean after clear")
+    assert buf.get_error()[0] == 0
 
 
 def _inject(inst, rng, n_bad=6):
@@ -205,3 +250,38 @@ def test_single_partition_view_and_copy():
     h.run_round(other, buf, view=True)
     torch.cuda.synchronize()
     assert not torch.equal(views[0], kept[0])
+
+
+def test_receive_retried_after_capacity_refusal():
+    """Arenas sized for a smaller bucket: the receive is refused with
+    AFD_E_CAPACITY and nothing runs; binding arenas for the round's bucket and
+    receiving again completes the round, equal to the oracle's."""
+    h = _gpu()
+    import torch
+    from combine_layout_amd import AfdError
+    from combine_layout_amd import _native as nat
+    inst = _small(80, T=[37, 50], bucket=64)
+    cfg = inst.cfg
+    buf = h.make_buffer(inst, arena_bucket=8)
+    dev = h.upload(inst)
+    for s, (x, ids, w, sc) in enumerate(dev):
+        buf.source_dispatch(s, x, ids, w, sc, bucket=cfg.bucket)
+    with pytest.raises(AfdError) as e:
+        buf.worker_receive(0, bucket=cfg.bucket)
+    assert e.value.status == nat.AFD_E_CAPACITY
+    buf.bind_arenas(cfg.bucket)
+    recs = [buf.worker_receive(f, bucket=cfg.bucket) for f in range(cfg.F)]
+    replies = [h.identity_replies(cfg, rec, f) for f, rec in enumerate(recs)]
+    for f, rec in enumerate(recs):
+        buf.worker_reply(f, replies[f], rec.receipt)
+    outs = [buf.source_collect(s) for s in range(cfg.N)]
+    ref = oracle.run_round(inst, rows_cap=[r.receive_rows for r in recs])
+    off = 0
+    for s, T in enumerate(cfg.T):
+        got = outs[s].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref.out[off:off + T])
+        off += T
+    # the next round runs on the new arenas
+    nxt = _small(81, T=[37, 50], bucket=64)
+    g = h.run_round(nxt, buf)
+    assert _check(nxt, g, oracle.run_round(nxt, rows_cap=g.receive_rows)) == 0

@@ -113,7 +113,7 @@ class Ctx:
 
 def test_library_exports_every_declared_symbol():
     syms = nat.header_symbols()
-    assert len(syms) == 12
+    assert sorted(syms) == sorted(nat.SIGNATURES)        # the binding declares every call
     if not os.path.exists(nat.LIB_PATH):
         pytest.skip("HIP library not built")
     lib = ctypes.CDLL(nat.LIB_PATH)
@@ -262,11 +262,62 @@ def test_empty_round_launches_no_combine(lib):
     lib.afd_fake_log_clear()
     assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 0, out=0) == 0
     recs = [x.receive(f)[1] for f in range(2)]
-    assert log(lib) == ["dispatch fused=1 ntok=0 nblk=1 T=0,0"]
+    assert log(lib) == ["dispatch empty E=8 T=0,0"]
     for f in range(2):
         assert x.reply(f, recs[f]) == 0
     assert log(lib) == []
     assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
+    x.destroy()
+
+
+@pytest.mark.parametrize("kw", [dict(E=512, F=2, K=8), dict(H=32768), dict(E=512, F=4, K=4, H=16384, dtype=1)],
+                         ids=["E512", "H32768", "E512-fp8-H16384"])
+def test_empty_round_off_the_one_kernel_path(lib, kw):
+    """A round whose sources are all empty clears ends[] at any E and H
+    (the one-kernel dispatch covers only E <= 256 and rows of at most 2048
+    columns; the tiled path has no tiles to launch)."""
+    c = cfg(**kw)
+    x = Ctx(lib, c)
+    for rnd in range(2):
+        lib.afd_fake_log_clear()
+        assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 0, out=0) == 0
+        recs = [x.receive(f) for f in range(c.num_partitions)]
+        assert all(st == 0 for st, _, _ in recs)
+        assert log(lib) == [f"dispatch empty E={c.num_experts} T=0,0"]
+        for f in range(c.num_partitions):
+            assert x.reply(f, recs[f][1]) == 0
+        assert log(lib) == []
+        assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
+    x.destroy()
+
+
+def test_receive_retry_after_capacity_failure(lib):
+    """A receive refused for a small arena leaves the round open: binding a
+    larger arena and receiving again completes it, and the next round runs."""
+    c = cfg()
+    x = Ctx(lib, c)
+    assert lib.afd_bind_partition(x.ctx, 1, 0x100000 * 5, 0, 0x201000, x.rb - 1) == 0
+    lib.afd_fake_log_clear()
+    assert x.dispatch(0, 2) == 0 and x.dispatch(1, 2) == 0
+    assert x.receive(0)[0] == nat.AFD_E_CAPACITY
+    assert x.receive(1)[0] == nat.AFD_E_CAPACITY
+    assert log(lib) == []                                       # nothing was enqueued
+    assert lib.afd_bind_partition(x.ctx, 1, 0x100000 * 5, 0, 0x201000, x.rb) == 0
+    recs = []
+    for f in range(2):
+        st, rec, _ = x.receive(f)
+        assert st == 0
+        recs.append(rec)
+    assert len([l for l in log(lib) if l.startswith("dispatch")]) == 1
+    # the dispatch work is enqueued: the arenas are fixed until the round ends
+    assert lib.afd_bind_partition(x.ctx, 1, 0x100000 * 5, 0, 0x201000, x.rb) == nat.AFD_E_ORDER
+    for f, rec in enumerate(recs):
+        assert x.reply(f, rec) == 0
+    assert lib.afd_bind_partition(x.ctx, 1, 0x100000 * 5, 0, 0x201000, x.rb) == nat.AFD_E_ORDER
+    for s in range(2):
+        assert x.collect(s)[0] == 0
+    assert lib.afd_bind_partition(x.ctx, 1, 0x100000 * 5, 0, 0x201000, x.rb) == 0   # between rounds
+    x.full_round()
     x.destroy()
 
 
@@ -610,3 +661,47 @@ def test_cached_round_empty_and_fp8(lib):
     lib.afd_fake_log_clear()
     assert y.receive(0)[0] == 0 and log(lib) == ["dispatch cached ntok=5 T=0,5"]
     y.destroy()
+
+
+def _info(lib, x):
+    ri = nat.RoundInfo()
+    assert lib.afd_get_round_info(x.ctx, ctypes.byref(ri)) == 0
+    return ri
+
+
+def test_round_info_names_the_dispatch_path(lib):
+    """afd_get_round_info reports the kernels the executor runs: the
+    one-kernel dispatch for small rounds, the tiled layout + scatter above its
+    limits, the cached scatter, and the empty dispatch."""
+    assert lib.afd_get_round_info(None, None) == nat.AFD_E_ARG
+    c = cfg(E=8, K=2, cap=1024)
+    x = Ctx(lib, c)
+    ri = _info(lib, x)
+    assert ri.round == 0 and ri.dispatch_path == 0
+    x.full_round(T=(4, 3))
+    ri = _info(lib, x)
+    assert (ri.round, nat.DISPATCH_PATHS[ri.dispatch_path], ri.dispatch_kernels, ri.combine_kernels, ri.tokens) == \
+        (1, "one_kernel", 1, 1, 7)
+    x.full_round(T=(600, 3))                                  # more than 512 tokens: tiled
+    ri = _info(lib, x)
+    assert nat.DISPATCH_PATHS[ri.dispatch_path] == "tiled" and ri.dispatch_kernels == 2
+    assert ri.tile_tokens == 64 and ri.layout_tiles == 11     # 640 + 64 slots in tiles of 64
+    for s, T in enumerate((600, 3)):
+        assert x.dispatch_cached(s, T) == 0
+    recs = [x.receive(f)[1] for f in range(2)]
+    ri = _info(lib, x)
+    assert nat.DISPATCH_PATHS[ri.dispatch_path] == "cached" and ri.dispatch_kernels == 1 and ri.round == 3
+    for f, rec in enumerate(recs):
+        assert x.reply(f, rec) == 0
+    for s in range(2):
+        assert x.collect(s)[0] == 0
+    x.full_round(T=(0, 0))
+    ri = _info(lib, x)
+    assert nat.DISPATCH_PATHS[ri.dispatch_path] == "empty" and ri.combine_kernels == 0
+    x.destroy()
+    y = Ctx(lib, cfg(E=8, K=2, cap=16, combine=2))
+    y.full_round(T=(4, 0))
+    ri = _info(lib, y)
+    assert ri.combine_kernels == 2 + 1                        # two stage-one launches, one stage two
+    y.destroy()
+
