@@ -22,6 +22,7 @@ COMBINE_MODES = {"once": AFD_COMBINE_ONCE, "per_stage": AFD_COMBINE_PER_STAGE,
                  "per_stage_fp8": AFD_COMBINE_PER_STAGE_FP8}
 ROUTE_NONE, ROUTE_RANGE, ROUTE_NEG, ROUTE_DUP = 0, 1, 2, 3
 MAX_SOURCES, MAX_PARTITIONS, MAX_EXPERTS, MAX_TOPK = 16, 16, 512, 32
+STATIC_SCRATCH_BYTES = 64 << 20
 
 STATUS_NAMES = {0: "AFD_OK", -1: "AFD_E_ARG", -2: "AFD_E_SHAPE", -3: "AFD_E_ORDER",
                 -4: "AFD_E_CAPACITY", -5: "AFD_E_ROUTE", -6: "AFD_E_HIP"}
@@ -65,6 +66,7 @@ _I64 = ctypes.c_int64
 SIGNATURES = {
     "afd_query": ([ctypes.POINTER(Config), _I32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_I64)], _I32),
     "afd_create": ([ctypes.POINTER(Config), _P, ctypes.c_size_t, ctypes.POINTER(_P)], _I32),
+    "afd_create_static": ([ctypes.POINTER(Config), ctypes.POINTER(_P)], _I32),
     "afd_bind_partition": ([_P, _I32, _P, _P, _P, _I64], _I32),
     "afd_destroy": ([_P], _I32),
     "afd_source_dispatch": ([_P, _I32, _I32, _P, _P, _P, _P, _I64, _I64, _P, _I32, _I32, _P], _I32),

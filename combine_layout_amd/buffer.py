@@ -37,6 +37,15 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+class _DeviceBytes:
+    """A device byte range the library owns (the static scratch array), seen
+    by torch through the CUDA array interface."""
+
+    def __init__(self, ptr: int, nbytes: int):
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False),
+                                         "strides": None, "version": 3}
+
+
 class Buffer:
     """One context over caller-owned (torch) device memory.
 
@@ -44,10 +53,14 @@ class Buffer:
     expert_alignment alpha, capacity (largest bucket), dtype "bf16" | "fp8",
     combine "once" | "per_stage" | "per_stage_fp8" (how the combine rounds;
     the per-stage modes need two or more partitions).
-    Receive arenas are sized for ``arena_bucket`` (default: capacity)."""
+    Receive arenas are sized for ``arena_bucket`` (default: capacity).
+    static_workspace=True makes the context with afd_create_static: no
+    workspace is allocated, the library's static scratch array on the device
+    serves (one such Buffer per device at a time)."""
 
     def __init__(self, num_sources, num_partitions, num_experts, topk, hidden, expert_alignment=1,
-                 capacity=2048, dtype="bf16", device=None, arena_bucket=None, combine="once"):
+                 capacity=2048, dtype="bf16", device=None, arena_bucket=None, combine="once",
+                 static_workspace=False):
         self.lib = nat.load()
         self.device = torch.device(device if device is not None else "cuda", torch.cuda.current_device()) \
             if device is None or isinstance(device, str) and device == "cuda" else torch.device(device)
@@ -64,7 +77,8 @@ class Buffer:
         rb = ctypes.c_int64(0)
         bucket = arena_bucket if arena_bucket is not None else capacity
         nat.check(self.lib.afd_query(ctypes.byref(self.cfg), bucket, ctypes.byref(ws), ctypes.byref(rb)), "afd_query")
-        self.workspace = torch.empty(ws.value, dtype=torch.uint8, device=self.device)
+        self.static_workspace = static_workspace
+        self.workspace = None if static_workspace else torch.empty(ws.value, dtype=torch.uint8, device=self.device)
         self.rows_cap = rb.value
         self.arenas = []
         for _ in range(num_partitions):
@@ -75,8 +89,12 @@ class Buffer:
             roww = torch.empty(self.rows_cap, dtype=torch.float32, device=self.device)
             self.arenas.append((rows, scales, roww))
         ctx = ctypes.c_void_p(0)
-        nat.check(self.lib.afd_create(ctypes.byref(self.cfg), _ptr(self.workspace), ws.value, ctypes.byref(ctx)),
-                  "afd_create")
+        if static_workspace:
+            with torch.cuda.device(self.device):
+                nat.check(self.lib.afd_create_static(ctypes.byref(self.cfg), ctypes.byref(ctx)), "afd_create_static")
+        else:
+            nat.check(self.lib.afd_create(ctypes.byref(self.cfg), _ptr(self.workspace), ws.value,
+                                          ctypes.byref(ctx)), "afd_create")
         self.ctx = ctx
         self._bind()
         self._round_refs = {}
@@ -109,6 +127,8 @@ class Buffer:
 
     # -- helpers -------------------------------------------------------------
     def _ws_view(self, ptr: int, nbytes: int) -> torch.Tensor:
+        if self.workspace is None:
+            return torch.as_tensor(_DeviceBytes(ptr, nbytes), device=self.device)
         off = ptr - self.workspace.data_ptr()
         assert 0 <= off and off + nbytes <= self.workspace.numel()
         return self.workspace[off:off + nbytes]

@@ -127,6 +127,19 @@ int be_device_sync()
     return 0;
 }
 
+int be_static_scratch(int *device, void **ptr)
+{
+    *device = 0;
+    *ptr = reinterpret_cast<void *>(uintptr_t(1) << 32);   // a fake, aligned "device" address
+    return g_fail;
+}
+
+int be_init_static(void *ws, const WorkspacePlan &wp)
+{
+    logf("init_static ws=%p total=%zu", ws, wp.total);
+    return g_fail;
+}
+
 }  // namespace afd
 
 extern "C" {

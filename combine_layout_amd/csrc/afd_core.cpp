@@ -9,6 +9,7 @@
 // collects once.
 
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "afd_plan.h"
@@ -68,7 +69,17 @@ struct afd_ctx {
     bool layout_valid = false;
     int layout_bucket = 0;
     int layout_T[kMaxSources] = {};
+
+    // afd_create_static: the device whose static context this is, else -1
+    int static_dev = -1;
 };
+
+namespace {
+// Host state of the contexts made by afd_create_static, one per device.
+afd_ctx g_static_ctx[kMaxDevices];
+bool g_static_used[kMaxDevices] = {};
+std::mutex g_static_mu;
+}  // namespace
 
 namespace {
 
@@ -294,6 +305,29 @@ afd_status afd_create(const afd_config *cfg, void *workspace, size_t workspace_b
     return AFD_OK;
 }
 
+afd_status afd_create_static(const afd_config *cfg, afd_ctx **out)
+{
+    if (!out) return AFD_E_ARG;
+    *out = nullptr;
+    afd_status st = check_config(cfg);
+    if (st != AFD_OK) return st;
+    const WorkspacePlan wp = plan_workspace(*cfg);
+    if (wp.total > kStaticScratchBytes) return AFD_E_CAPACITY;
+    int dev = -1;
+    void *ws = nullptr;
+    if (be_static_scratch(&dev, &ws) != 0 || dev < 0 || dev >= kMaxDevices || !ws) return AFD_E_HIP;
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (g_static_used[dev]) return AFD_E_ORDER;
+    afd_ctx *c = &g_static_ctx[dev];
+    *c = afd_ctx{};
+    init_ctx(c, cfg, ws, kStaticScratchBytes, wp);
+    c->static_dev = dev;
+    if (be_init_static(ws, wp) != 0) return AFD_E_HIP;
+    g_static_used[dev] = true;
+    *out = c;
+    return AFD_OK;
+}
+
 afd_status afd_bind_partition(afd_ctx *c, int32_t f, void *rows, float *scales, float *row_weights,
                               int64_t rows_cap)
 {
@@ -322,7 +356,13 @@ afd_status afd_destroy(afd_ctx *c)
 {
     if (!c) return AFD_OK;
     int rc = be_device_sync();
-    delete c;
+    if (c->static_dev >= 0) {
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        g_static_used[c->static_dev] = false;
+        c->static_dev = -1;
+    } else {
+        delete c;
+    }
     return rc == 0 ? AFD_OK : AFD_E_HIP;
 }
 

@@ -55,8 +55,16 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "afd_plan.h"
+
+// Workspace of the contexts made by afd_create_static: one array per GPU,
+// held from the library's first use of the device until the process ends.
+// In host code this name is only a stand-in for the device array: host code
+// uses the address hipGetSymbolAddress returns for the current device
+// (be_static_scratch), never the name itself.
+static __device__ __align__(256) unsigned char scratch[afd::kStaticScratchBytes];
 
 namespace afd {
 namespace {
@@ -1421,6 +1429,12 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     }
 }
 
+// A fresh static-scratch workspace: the route-error word starts as "none".
+__global__ __launch_bounds__(64) void k_init_err(unsigned long long *err)
+{
+    if (threadIdx.x == 0) *err = kNoError;
+}
+
 // Dispatch of a round without tokens: every expert's range is empty.
 __global__ __launch_bounds__(256) void k_zero_ends(int32_t *ends, int E)
 {
@@ -1707,5 +1721,34 @@ int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word)
 }
 
 int be_device_sync() { return hipDeviceSynchronize() == hipSuccess ? 0 : 1; }
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int be_static_scratch(int *device, void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // this device's copy of the array, with the device current
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return 1;
+        g_scratch_ptr[dev] = p;
+    }
+    *device = dev;
+    *ptr = g_scratch_ptr[dev];
+    return 0;
+}
+
+int be_init_static(void *workspace, const WorkspacePlan &wp)
+{
+    auto *err = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + wp.err);
+    hipLaunchKernelGGL(k_init_err, dim3(1), dim3(64), 0, nullptr, err);
+    if (launched_ok()) return 1;
+    return hipStreamSynchronize(nullptr) == hipSuccess ? 0 : 1;
+}
 
 }  // namespace afd

@@ -139,6 +139,11 @@ inline int layout_tiles(const RoundPlan &p, TileRec *out)
     return p.nblk;
 }
 
+// Contexts made by afd_create_static use a static scratch array of this many
+// bytes per GPU as their workspace (one such context per device at a time).
+constexpr size_t kStaticScratchBytes = size_t(AFD_STATIC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
 // ---- backend: implemented by the HIP executor or the recording fake ----
 // Each returns 0 on success, nonzero on a runtime failure.
 int be_init_workspace(void *workspace, const WorkspacePlan &wp);
@@ -151,5 +156,11 @@ int be_launch_final(const RoundPlan &p, int s, void *stream);     // per-stage c
 int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream);
 int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word);
 int be_device_sync();
+// The current device and the address of its static scratch array (found
+// once per device); no allocation.
+int be_static_scratch(int *device, void **ptr);
+// Initialise a static scratch workspace (the error word) with a kernel on
+// the null stream and wait for it; no allocation, no host-to-device copy.
+int be_init_static(void *workspace, const WorkspacePlan &wp);
 
 }  // namespace afd

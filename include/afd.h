@@ -41,6 +41,8 @@ extern "C" {
 #define AFD_MAX_PARTITIONS 16
 #define AFD_MAX_EXPERTS 512
 #define AFD_MAX_TOPK 32
+/* Bytes of the static scratch array per GPU behind afd_create_static. */
+#define AFD_STATIC_SCRATCH_BYTES (64u << 20)
 
 typedef struct afd_ctx afd_ctx;
 
@@ -157,6 +159,27 @@ afd_status afd_query(const afd_config *cfg, int32_t bucket, size_t *workspace_by
  * AFD_E_CAPACITY (workspace too small), AFD_E_HIP.
  */
 afd_status afd_create(const afd_config *cfg, void *workspace, size_t workspace_bytes, afd_ctx **out);
+
+/*
+ * afd_create_static: afd_create for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It takes no workspace: the context's workspace is the
+ * library's static scratch array on the current device,
+ * AFD_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's first
+ * use of that device until the process ends, and its host state is static
+ * storage too.  The caller still allocates and binds the receive arenas and
+ * passes inputs, outputs and replies; every later call works as on a context
+ * from afd_create.  It calls no hipMalloc, hipFree or other allocating
+ * routine; it launches one tiny kernel on the null stream and waits for it,
+ * so (like afd_create) it is called outside capture.  One such context may
+ * exist per device at a time: all of them share the device's array, which
+ * keeps the last round's contents, so rounds that overlap on one device
+ * race.  afd_destroy releases it.
+ * Errors: AFD_E_ARG (NULL), AFD_E_SHAPE (config), AFD_E_CAPACITY (the
+ * config's workspace, afd_query's bytes, exceeds AFD_STATIC_SCRATCH_BYTES),
+ * AFD_E_ORDER (the device's static context exists), AFD_E_HIP.
+ */
+afd_status afd_create_static(const afd_config *cfg, afd_ctx **out);
 
 /*
  * afd_bind_partition (contract page, "Graphs, streams and lifetime": receive

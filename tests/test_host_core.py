@@ -705,3 +705,30 @@ def test_round_info_names_the_dispatch_path(lib):
     assert ri.combine_kernels == 2 + 1                        # two stage-one launches, one stage two
     y.destroy()
 
+
+def test_create_static(lib):
+    """afd_create_static: the device's static scratch as the workspace, one
+    context per device at a time, configs whose workspace exceeds the array
+    refused, and every later call as on a context from afd_create."""
+    c = cfg()
+    ctx = ctypes.c_void_p()
+    assert lib.afd_create_static(ctypes.byref(c), None) == nat.AFD_E_ARG
+    big = cfg(N=16, F=1, E=8, K=2, H=16384, cap=2048)            # 1 GiB of single-partition inboxes
+    assert lib.afd_create_static(ctypes.byref(big), ctypes.byref(ctx)) == nat.AFD_E_CAPACITY
+    assert lib.afd_create_static(ctypes.byref(cfg(H=200)), ctypes.byref(ctx)) == nat.AFD_E_SHAPE
+    lib.afd_fake_log_clear()
+    assert lib.afd_create_static(ctypes.byref(c), ctypes.byref(ctx)) == 0
+    assert log(lib)[0].startswith("init_static ws=0x100000000")
+    other = ctypes.c_void_p()
+    assert lib.afd_create_static(ctypes.byref(c), ctypes.byref(other)) == nat.AFD_E_ORDER
+    x = Ctx.__new__(Ctx)
+    x.lib, x.c, x.ctx = lib, c, ctx
+    _, _, x.rb = query(lib, c, c.capacity)
+    for f in range(2):
+        assert lib.afd_bind_partition(ctx, f, 0x100000 * (f + 4), 0, 0x200000 + f * 0x1000, x.rb) == 0
+    recs = x.full_round(T=(4, 3))
+    assert recs[0].ends == (1 << 32) + 256                      # ends[] right after the error word's 256 bytes
+    x.full_round(T=(2, 0))
+    assert lib.afd_destroy(ctx) == 0
+    assert lib.afd_create_static(ctypes.byref(c), ctypes.byref(other)) == 0   # free again
+    assert lib.afd_destroy(other) == 0
