@@ -148,6 +148,7 @@ class RoundSet:
 
 
 def capture(sets, order):
+    """A graph of one round of each set index in `order`, in that order."""
     import torch
     g = torch.cuda.CUDAGraph()
     stream = torch.cuda.Stream()
@@ -164,53 +165,79 @@ def capture(sets, order):
     return g
 
 
-def time_rounds(sets, S, steps, warmup, blocks=5, gmax=32):
-    """Time exactly `steps` rounds in `blocks` consecutive blocks.
+class RoundPlan:
+    """Graphs for `steps` timed rounds in `blocks` blocks after `warmup`
+    untimed ones, rounds numbered from `first`.
 
-    Rounds are numbered from 0 with the `warmup` untimed rounds first; round
-    i runs on set i mod S, so consecutive rounds use different sets and the
-    rounds of a block rotate through distinct ones.  Each block is replayed
-    as graphs of at most `gmax` rounds (cached by starting set and length).
-    The warmup replays stay queued ahead of the first block, so the GPU is
-    busy while the blocks are enqueued, and HIP events between the blocks
-    bracket device work.  Returns the median block's µs per round and every
-    block's value."""
+    Round i runs on set i mod S, so consecutive rounds use different sets and
+    the rounds of a block rotate through distinct ones.  Rounds are replayed
+    as graphs of at most `gmax` rounds (cached in `graphs` by starting set
+    and length).  Every graph launch has a fixed device-side cost (HIP timing
+    events cannot be recorded inside a graph on this runtime), so a block has
+    at least 64 rounds: fewer steps make fewer blocks (one, at 20 steps)."""
+
+    def __init__(self, sets, S, first, steps, warmup, graphs, blocks=5, gmax=64):
+        import torch
+
+        def chunks(start, n):
+            out = []
+            while n > 0:
+                m = min(n, gmax)
+                key = (start % S, m)
+                if key not in graphs:
+                    graphs[key] = capture(sets, [(start + j) % S for j in range(m)])
+                out.append(graphs[key])
+                start += m
+                n -= m
+            return out
+
+        blocks = max(1, min(blocks, steps // 64))
+        self.per = [steps // blocks + (1 if b < steps % blocks else 0) for b in range(blocks)]
+        self.warm = chunks(first, warmup)
+        self.blocks = []
+        i = first + warmup
+        for n in self.per:
+            self.blocks.append(chunks(i, n))
+            i += n
+        self.end = i
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+
+    def enqueue(self):
+        for g in self.warm:
+            g.replay()
+        self.ev[0].record()
+        for b, gs in enumerate(self.blocks):
+            for g in gs:
+                g.replay()
+            self.ev[b + 1].record()
+
+    def result(self):
+        """Median block µs per round and every block's value (after a sync)."""
+        us = [self.ev[b].elapsed_time(self.ev[b + 1]) * 1e3 / n for b, n in enumerate(self.per)]
+        return float(np.median(us)), us
+
+
+def time_rounds(sets, S, steps, warmup, protocol_steps, protocol_warmup=64, gmax=64):
+    """The timed steps and the five-block protocol figure on one rotation.
+
+    Every graph is captured first; then the protocol's rounds and, right
+    behind them, the `warmup` + `steps` rounds of the timed region are
+    enqueued back to back, so the timed steps run on a GPU that has been
+    busy for milliseconds (as in a serving loop) rather than one waking from
+    the host's capture work, and HIP events between blocks bracket device
+    work.  Returns ((median, blocks) of the timed steps, (median, blocks) of
+    the protocol)."""
     import torch
     graphs = {}
-
-    def chunks(start, n):
-        out = []
-        while n > 0:
-            m = min(n, gmax)
-            key = (start % S, m)
-            if key not in graphs:
-                graphs[key] = capture(sets, [(start + j) % S for j in range(m)])
-            out.append(graphs[key])
-            start += m
-            n -= m
-        return out
-
-    blocks = max(1, min(blocks, steps))
-    per = [steps // blocks + (1 if b < steps % blocks else 0) for b in range(blocks)]
-    warm = chunks(0, warmup)
-    plan = []
-    i = warmup
-    for b in range(blocks):
-        plan.append(chunks(i, per[b]))
-        i += per[b]
+    prot = RoundPlan(sets, S, 0, protocol_steps, protocol_warmup, graphs, gmax=gmax)
+    timed = RoundPlan(sets, S, prot.end, steps, warmup, graphs, gmax=gmax)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
-    for g in warm:
-        g.replay()
-    ev[0].record()
-    for b in range(blocks):
-        for g in plan[b]:
-            g.replay()
-        ev[b + 1].record()
+    prot.enqueue()
+    timed.enqueue()
     torch.cuda.synchronize()
-    us = [ev[b].elapsed_time(ev[b + 1]) * 1e3 / per[b] for b in range(blocks)]
+    out = timed.result(), prot.result()
     del graphs
-    return float(np.median(us)), us
+    return out
 
 
 def capture_phase(sets, order, phase):
@@ -253,6 +280,8 @@ def time_kernels_live(sets, launches=48, reps=8):
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            g.replay()                  # untimed, queued ahead: the GPU is busy when t0 is reached
         t0.record()
         for _ in range(reps):
             g.replay()
@@ -305,9 +334,10 @@ def time_identity_experts(rs, reps=20):
     return t0.elapsed_time(t1) * 1e3 / reps
 
 
-def launch_floor(G=32, steps=3200):
-    """Graph of G rounds of two tiny dependent kernels: the floor a round of
-    two launches cannot go below."""
+def launch_floor(G=32, reps=50):
+    """Graph of G rounds of two tiny dependent kernels, replayed `reps` times
+    after ten untimed replays queued ahead: the floor a round of two
+    launches cannot go below."""
     import torch
     a = torch.zeros(1, device="cuda")
     g = torch.cuda.CUDAGraph()
@@ -324,12 +354,14 @@ def launch_floor(G=32, steps=3200):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(10):
+        g.replay()
     t0.record()
-    for _ in range(steps // G):
+    for _ in range(reps):
         g.replay()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) * 1e3 / (steps // G * G)
+    return t0.elapsed_time(t1) * 1e3 / (reps * G)
 
 
 def copy_bandwidth(nbytes=1 << 30, reps=20):
@@ -483,17 +515,22 @@ def measure_workload(name, args):
     nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else 0)
     view = cfg.F == 1
     S = min(MAX_COLD_SETS, max(1, math.ceil(args.cold_bytes / nb["total"])))
-    gmax = args.graph_rounds or (32 if nb["total"] < 32e6 else 4)
+    gmax = args.graph_rounds or 64
     print(f"[bench] {name}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} alpha={cfg.alpha} "
           f"dtype={cfg.dtype} L={L} bytes/round={nb['total']} cold sets={S}", file=sys.stderr, flush=True)
     sets = [RoundSet(inst, view, args.combine, args.cached)]
     info = sets[0].buf.round_info()
-    hot_us, hot_blocks = time_rounds(sets, 1, args.steps, args.warmup, gmax=gmax)
+    # the survey's protocol beside the timed steps: five blocks of
+    # protocol_block rounds after 64 warmup rounds
+    (hot_us, hot_blocks), (prot_hot_us, _) = time_rounds(sets, 1, args.steps, args.warmup,
+                                                         5 * args.protocol_block, gmax=gmax)
     for _ in range(S - 1):
         sets.append(RoundSet(inst, view, args.combine, args.cached))
-    cold_us, cold_blocks = time_rounds(sets, S, args.steps, args.warmup, gmax=gmax)
-    print(f"[bench] {name}: cold {cold_us:.3f} us/round (blocks {', '.join(f'{u:.3f}' for u in cold_blocks)}), "
-          f"hot {hot_us:.3f}", file=sys.stderr, flush=True)
+    (cold_us, cold_blocks), (prot_us, prot_blocks) = time_rounds(sets, S, args.steps, args.warmup,
+                                                                 5 * args.protocol_block, gmax=gmax)
+    print(f"[bench] {name}: cold {cold_us:.3f} us/round ({args.steps} rounds), hot {hot_us:.3f}; "
+          f"protocol cold {prot_us:.3f} (blocks {', '.join(f'{u:.3f}' for u in prot_blocks)}), "
+          f"hot {prot_hot_us:.3f}", file=sys.stderr, flush=True)
     kern = time_kernels_live(sets)
     expert_us = time_identity_experts(sets[0])
     dom, dom_name = dominant_kernel(info, nb, args.cached, args.combine)
@@ -506,6 +543,9 @@ def measure_workload(name, args):
         "us_per_round_blocks": cold_blocks,
         "us_per_round_hot": hot_us,
         "us_per_round_hot_blocks": hot_blocks,
+        "protocol_us_per_round": prot_us,
+        "protocol_us_per_round_blocks": prot_blocks,
+        "protocol_us_per_round_hot": prot_hot_us,
         "gbps": gbps,
         "pct_peak": 100 * gbps / PEAK_HBM_GBPS,
         "bytes_per_round": nb["total"],
@@ -517,6 +557,7 @@ def measure_workload(name, args):
         "layout_tiles": info["layout_tiles"],
         "cold_sets": S,
         "rounds_per_graph_max": gmax,
+        "protocol_block_rounds": args.protocol_block,
         "live_choices": L,
         "config": {"workload": name, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
                    "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
@@ -572,6 +613,8 @@ def aggregate(runs, names, args):
         roof["achieved"] = roof["algorithmic_bytes_per_launch"] / (kern[dom] * 1e-6) / 1e9
         roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
         gbps = nb / (cold * 1e-6) / 1e9
+        prot = _median([r["protocol_us_per_round"] for r in rs])
+        prot_hot = _median([r["protocol_us_per_round_hot"] for r in rs])
         w = {
             "us_per_round": round(cold, 3),
             "us_per_round_per_process": [round(r["us_per_round"], 3) for r in rs],
@@ -581,6 +624,12 @@ def aggregate(runs, names, args):
             "us_per_round_hot": round(hot, 3),
             "gbps_hot": round(nb / (hot * 1e-6) / 1e9, 2),
             "pct_peak_hot": round(100 * nb / (hot * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+            "protocol": {"us_per_round": round(prot, 3), "pct_peak": round(100 * nb / (prot * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+                         "us_per_round_per_process": [round(r["protocol_us_per_round"], 3) for r in rs],
+                         "us_per_round_blocks": [[round(u, 3) for u in r["protocol_us_per_round_blocks"]] for r in rs],
+                         "us_per_round_hot": round(prot_hot, 3),
+                         "pct_peak_hot": round(100 * nb / (prot_hot * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+                         "rounds": 5 * first["protocol_block_rounds"], "blocks": 5},
             "bytes_per_round": nb,
             "kernels_us": {k: round(v, 3) for k, v in kern.items()},
             "identity_experts_us": round(_median([r["identity_experts_us"] for r in rs]), 3),
@@ -592,7 +641,8 @@ def aggregate(runs, names, args):
         }
         if name in GATED and args.combine == "once" and not args.cached:
             budget = nb / (GATE_FRAC * PEAK_HBM_GBPS * 1e9) * 1e6
-            w["gate_60pct"] = {"budget_us": round(budget, 3), "pass": bool(cold <= budget)}
+            w["gate_60pct"] = {"budget_us": round(budget, 3), "pass": bool(cold <= budget),
+                               "pass_protocol": bool(prot <= budget)}
         out[name] = w
     return out
 
@@ -603,7 +653,15 @@ def run_children(args, argv):
     first failing child's status."""
     import subprocess
     runs = []
-    child_argv = [a for a in argv if not a.startswith("--processes")]
+    child_argv = []
+    skip = False
+    for a in argv:                           # every argument but --processes (and its value)
+        if skip:
+            skip = False
+        elif a == "--processes":
+            skip = True
+        elif not a.startswith("--processes="):
+            child_argv.append(a)
     for p in range(args.processes):
         print(f"[bench] process {p + 1} of {args.processes}", file=sys.stderr, flush=True)
         proc = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), *child_argv, "--processes", "0",
@@ -632,7 +690,9 @@ def main(argv=None):
                     help="combine rounding: once (default), or per stage with BF16 or FP8 partials")
     ap.add_argument("--cached", action="store_true",
                     help="time rounds that reuse the previous layout (cached dispatch, unchanged routes)")
-    ap.add_argument("--graph-rounds", type=int, default=0, help="most rounds per captured graph (default by size)")
+    ap.add_argument("--graph-rounds", type=int, default=0, help="most rounds per captured graph (default 64)")
+    ap.add_argument("--protocol-block", type=int, default=256,
+                    help="rounds per block of the five-block protocol figure reported beside the timed steps")
     ap.add_argument("--cold-bytes", type=float, default=512e6, help="bytes the cold rotation spans")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work per setting for the headline workload's CPU baseline")
@@ -694,6 +754,7 @@ def main(argv=None):
         "us_per_round": top["us_per_round"],
         "pct_peak": top["pct_peak"],
         "us_per_round_hot": top["us_per_round_hot"],
+        "protocol": top["protocol"],
         "processes": len(runs),
         "roofline": top["roofline"],
     }

@@ -23,7 +23,9 @@ def test_dominant_kernel_follows_the_reported_path():
 
 def _fake_run(us, hot, disp, comb):
     return {"workloads": {"2a2f_decode": {
-        "us_per_round": us, "us_per_round_blocks": [us] * 5, "us_per_round_hot": hot, "bytes_per_round": 18931712,
+        "us_per_round": us, "us_per_round_blocks": [us], "us_per_round_hot": hot, "bytes_per_round": 18931712,
+        "protocol_us_per_round": us - 1.0, "protocol_us_per_round_blocks": [us - 1.0] * 5,
+        "protocol_us_per_round_hot": hot - 1.0, "protocol_block_rounds": 256,
         "kernels_us": {"dispatch": disp, "combine": comb}, "identity_experts_us": 50.0, "dispatch_path": "one_kernel",
         "cold_sets": 28, "config": {"workload": "2a2f_decode"}, "inputs_sha256": {},
         "roofline": {"bound": "hbm", "kernel": "k_fused", "achieved": 0.0, "peak": 8000.0, "unit": "GB/s",
@@ -42,7 +44,8 @@ def test_aggregate_takes_medians_and_applies_the_gate():
     assert w["roofline"]["avg_launch_us"] == 6.0
     assert abs(w["roofline"]["frac"] - 9478144 / 6e-6 / 1e9 / 8000) < 1e-4
     # 60% of 8 TB/s for 18,931,712 bytes: 3.944 us; 11 us fails it
-    assert w["gate_60pct"] == {"budget_us": 3.944, "pass": False}
+    assert w["gate_60pct"] == {"budget_us": 3.944, "pass": False, "pass_protocol": False}
+    assert w["protocol"]["us_per_round"] == 10.0 and w["protocol"]["rounds"] == 1280
     assert abs(w["pct_peak"] - 100 * 18931712 / 11e-6 / 1e9 / 8000) < 0.01
 
 
