@@ -100,14 +100,14 @@ def round_bytes(cfg, L: int, combine: str = "once", n_partial: int = 0) -> dict:
 class RoundSet:
     """One independent set of inputs, outputs, arenas and replies."""
 
-    def __init__(self, inst, view, combine="once", cached=False):
+    def __init__(self, inst, view, combine="once", cached=False, dispatch="auto"):
         import torch
         import harness as h
         self.inst = inst
         self.cfg = inst.cfg
         self.view = view
         self.dev = h.upload(inst)
-        self.buf = h.make_buffer(inst, combine=combine)
+        self.buf = h.make_buffer(inst, combine=combine, dispatch=dispatch)
         self.outs = [torch.empty((T, self.cfg.H), dtype=torch.bfloat16, device="cuda") for T in self.cfg.T]
         # one eager round to obtain the receive layout, then the replies
         for s, (x, ids, w, scl) in enumerate(self.dev):
@@ -500,7 +500,7 @@ def dominant_kernel(info, nb, cached, combine):
     if combine != "once":
         return "combine", "k_partial+k_final"
     path = info["dispatch_path"]
-    single = {"one_kernel": "k_fused", "cached": "k_scatter_cached"}.get(path)
+    single = {"one_kernel": "k_fused", "cached": "k_scatter_cached", "one_launch": "k_dispatch1"}.get(path)
     if single is not None and nb["dispatch"] >= nb["combine"]:
         return "dispatch", single
     return "combine", "k_combine"
@@ -518,14 +518,14 @@ def measure_workload(name, args):
     gmax = args.graph_rounds or 64
     print(f"[bench] {name}: N={cfg.N} T={cfg.T} H={cfg.H} E={cfg.E} F={cfg.F} K={cfg.K} alpha={cfg.alpha} "
           f"dtype={cfg.dtype} L={L} bytes/round={nb['total']} cold sets={S}", file=sys.stderr, flush=True)
-    sets = [RoundSet(inst, view, args.combine, args.cached)]
+    sets = [RoundSet(inst, view, args.combine, args.cached, args.dispatch)]
     info = sets[0].buf.round_info()
     # the survey's protocol beside the timed steps: five blocks of
     # protocol_block rounds after 64 warmup rounds
     (hot_us, hot_blocks), (prot_hot_us, _) = time_rounds(sets, 1, args.steps, args.warmup,
                                                          5 * args.protocol_block, gmax=gmax)
     for _ in range(S - 1):
-        sets.append(RoundSet(inst, view, args.combine, args.cached))
+        sets.append(RoundSet(inst, view, args.combine, args.cached, args.dispatch))
     (cold_us, cold_blocks), (prot_us, prot_blocks) = time_rounds(sets, S, args.steps, args.warmup,
                                                                  5 * args.protocol_block, gmax=gmax)
     print(f"[bench] {name}: cold {cold_us:.3f} us/round ({args.steps} rounds), hot {hot_us:.3f}; "
@@ -534,7 +534,8 @@ def measure_workload(name, args):
     kern = time_kernels_live(sets)
     expert_us = time_identity_experts(sets[0])
     dom, dom_name = dominant_kernel(info, nb, args.cached, args.combine)
-    mode = ("_cached" if args.cached else "") + ("" if args.combine == "once" else "_" + args.combine)
+    mode = ("_cached" if args.cached else "") + ("" if args.combine == "once" else "_" + args.combine) + \
+        ("_one_launch" if info["dispatch_path"] == "one_launch" else "")
     traffic = load_traffic(dom_name, name, mode, {"k_partial": cfg.F, "k_final": cfg.N})
     dom_gbps = nb[dom] / (kern[dom] * 1e-6) / 1e9
     gbps = nb["total"] / (cold_us * 1e-6) / 1e9
@@ -562,7 +563,7 @@ def measure_workload(name, args):
         "config": {"workload": name, "sources": cfg.N, "tokens_per_source": cfg.T[0], "hidden": cfg.H,
                    "experts": cfg.E, "partitions": cfg.F, "topk": cfg.K, "expert_alignment": cfg.alpha,
                    "activations": cfg.dtype, "bucket": cfg.bucket, "live_choices": L, "cold_sets": S,
-                   "combine": args.combine, "cached_layout": bool(args.cached)},
+                   "combine": args.combine, "cached_layout": bool(args.cached), "dispatch": args.dispatch},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": dom_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": dom_gbps / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": kern[dom]},
@@ -608,7 +609,7 @@ def aggregate(runs, names, args):
         hot = _median([r["us_per_round_hot"] for r in rs])
         kern = {k: _median([r["kernels_us"][k] for r in rs]) for k in first["kernels_us"]}
         roof = dict(first["roofline"])
-        dom = "dispatch" if roof["kernel"] in ("k_fused", "k_scatter_cached") else "combine"
+        dom = "dispatch" if roof["kernel"] in ("k_fused", "k_scatter_cached", "k_dispatch1") else "combine"
         roof["avg_launch_us"] = kern[dom]
         roof["achieved"] = roof["algorithmic_bytes_per_launch"] / (kern[dom] * 1e-6) / 1e9
         roof["frac"] = roof["achieved"] / PEAK_HBM_GBPS
@@ -688,6 +689,8 @@ def main(argv=None):
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--combine", default="once", choices=["once", "per_stage", "per_stage_fp8"],
                     help="combine rounding: once (default), or per stage with BF16 or FP8 partials")
+    ap.add_argument("--dispatch", default="auto", choices=["auto", "split", "one_launch"],
+                    help="how larger rounds' dispatch is launched (afd_dispatch_mode)")
     ap.add_argument("--cached", action="store_true",
                     help="time rounds that reuse the previous layout (cached dispatch, unchanged routes)")
     ap.add_argument("--graph-rounds", type=int, default=0, help="most rounds per captured graph (default 64)")

@@ -15,24 +15,27 @@ LIB_PATH = os.path.join(HERE, "_lib", "libafd.so")
 FAKE_LIB_PATH = os.path.join(HERE, "_lib", "libafd_hostfake.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "afd.h")
 
-AFD_OK, AFD_E_ARG, AFD_E_SHAPE, AFD_E_ORDER, AFD_E_CAPACITY, AFD_E_ROUTE, AFD_E_HIP = 0, -1, -2, -3, -4, -5, -6
+AFD_OK, AFD_E_ARG, AFD_E_SHAPE, AFD_E_ORDER, AFD_E_CAPACITY, AFD_E_ROUTE, AFD_E_HIP, AFD_E_TIMEOUT = \
+    0, -1, -2, -3, -4, -5, -6, -7
 AFD_BF16, AFD_FP8_E4M3 = 0, 1
 AFD_COMBINE_ONCE, AFD_COMBINE_PER_STAGE, AFD_COMBINE_PER_STAGE_FP8 = 0, 1, 2
 COMBINE_MODES = {"once": AFD_COMBINE_ONCE, "per_stage": AFD_COMBINE_PER_STAGE,
                  "per_stage_fp8": AFD_COMBINE_PER_STAGE_FP8}
+AFD_DISPATCH_AUTO, AFD_DISPATCH_SPLIT, AFD_DISPATCH_ONE_LAUNCH = 0, 1, 2
+DISPATCH_MODES = {"auto": AFD_DISPATCH_AUTO, "split": AFD_DISPATCH_SPLIT, "one_launch": AFD_DISPATCH_ONE_LAUNCH}
 ROUTE_NONE, ROUTE_RANGE, ROUTE_NEG, ROUTE_DUP = 0, 1, 2, 3
 MAX_SOURCES, MAX_PARTITIONS, MAX_EXPERTS, MAX_TOPK = 16, 16, 512, 32
 STATIC_SCRATCH_BYTES = 64 << 20
 
 STATUS_NAMES = {0: "AFD_OK", -1: "AFD_E_ARG", -2: "AFD_E_SHAPE", -3: "AFD_E_ORDER",
-                -4: "AFD_E_CAPACITY", -5: "AFD_E_ROUTE", -6: "AFD_E_HIP"}
+                -4: "AFD_E_CAPACITY", -5: "AFD_E_ROUTE", -6: "AFD_E_HIP", -7: "AFD_E_TIMEOUT"}
 
 
 class Config(ctypes.Structure):
     _fields_ = [("num_sources", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("topk", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("expert_alignment", ctypes.c_int32), ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("combine", ctypes.c_int32)]
+                ("combine", ctypes.c_int32), ("dispatch", ctypes.c_int32)]
 
 
 class Receipt(ctypes.Structure):
@@ -50,7 +53,7 @@ class RoundInfo(ctypes.Structure):
                 ("tokens", ctypes.c_int32), ("layout_tiles", ctypes.c_int32), ("tile_tokens", ctypes.c_int32)]
 
 
-DISPATCH_PATHS = {0: "none", 1: "one_kernel", 2: "tiled", 3: "cached", 4: "empty"}
+DISPATCH_PATHS = {0: "none", 1: "one_kernel", 2: "tiled", 3: "cached", 4: "empty", 5: "one_launch"}
 
 
 class AfdError(RuntimeError):
@@ -78,6 +81,7 @@ SIGNATURES = {
                        ctypes.POINTER(_I32)], _I32),
     "afd_get_partials": ([_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64)], _I32),
     "afd_get_round_info": ([_P, ctypes.POINTER(RoundInfo)], _I32),
+    "afd_set_dispatch_wait": ([_P, _I32], _I32),
     "afd_status_string": ([_I32], ctypes.c_char_p),
 }
 
@@ -116,6 +120,7 @@ def load_fake():
     lib.afd_fake_log_get.argtypes = [ctypes.c_int, ctypes.c_char_p, ctypes.c_int]
     lib.afd_fake_set_ends.argtypes = [_P, ctypes.c_int, ctypes.c_uint64]
     lib.afd_fake_tiles.argtypes = [_P, ctypes.c_int]
+    lib.afd_fake_set_stall.argtypes = [ctypes.c_int]
     return lib
 
 

@@ -54,13 +54,14 @@ class Buffer:
     combine "once" | "per_stage" | "per_stage_fp8" (how the combine rounds;
     the per-stage modes need two or more partitions).
     Receive arenas are sized for ``arena_bucket`` (default: capacity).
+    dispatch "auto" | "split" | "one_launch" (afd_dispatch_mode).
     static_workspace=True makes the context with afd_create_static: no
     workspace is allocated, the library's static scratch array on the device
     serves (one such Buffer per device at a time)."""
 
     def __init__(self, num_sources, num_partitions, num_experts, topk, hidden, expert_alignment=1,
                  capacity=2048, dtype="bf16", device=None, arena_bucket=None, combine="once",
-                 static_workspace=False):
+                 static_workspace=False, dispatch="auto"):
         self.lib = nat.load()
         self.device = torch.device(device if device is not None else "cuda", torch.cuda.current_device()) \
             if device is None or isinstance(device, str) and device == "cuda" else torch.device(device)
@@ -68,8 +69,11 @@ class Buffer:
         if combine not in nat.COMBINE_MODES:
             raise ValueError(f"combine must be one of {sorted(nat.COMBINE_MODES)}")
         self.combine = combine
+        if dispatch not in nat.DISPATCH_MODES:
+            raise ValueError(f"dispatch must be one of {sorted(nat.DISPATCH_MODES)}")
         self.cfg = nat.Config(num_sources, num_partitions, num_experts, topk, hidden, expert_alignment, capacity,
-                              nat.AFD_FP8_E4M3 if self.fp8 else nat.AFD_BF16, nat.COMBINE_MODES[combine])
+                              nat.AFD_FP8_E4M3 if self.fp8 else nat.AFD_BF16, nat.COMBINE_MODES[combine],
+                              nat.DISPATCH_MODES[dispatch])
         self.N, self.F, self.E, self.K, self.H = num_sources, num_partitions, num_experts, topk, hidden
         self.E_loc = num_experts // num_partitions
         self.alpha, self.capacity = expert_alignment, capacity
@@ -254,13 +258,22 @@ class Buffer:
                 "tokens": ri.tokens, "layout_tiles": ri.layout_tiles, "tile_tokens": ri.tile_tokens}
 
     # -- errors / teardown ---------------------------------------------------
-    def get_error(self, clear=False):
+    def get_error(self, clear=False, with_status=False):
+        """The sticky first invalid route (code, s, t, k); with_status=True
+        also returns the call's status (AFD_E_TIMEOUT when a one-launch
+        dispatch gave up waiting)."""
         code, s, t, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         st = self.lib.afd_get_error(self.ctx, _stream(self.device), 1 if clear else 0, ctypes.byref(code),
                                     ctypes.byref(s), ctypes.byref(t), ctypes.byref(k))
-        if st not in (nat.AFD_OK, nat.AFD_E_ROUTE):
+        if st not in (nat.AFD_OK, nat.AFD_E_ROUTE, nat.AFD_E_TIMEOUT):
             nat.check(st, "get_error")
-        return code.value, s.value, t.value, k.value
+        err = (code.value, s.value, t.value, k.value)
+        return (err, st) if with_status else err
+
+    def set_dispatch_wait(self, polls):
+        """Polls a one-launch dispatch's workgroups make before giving up
+        (negative: give up at once)."""
+        nat.check(self.lib.afd_set_dispatch_wait(self.ctx, int(polls)), "set_dispatch_wait")
 
     def close(self):
         if getattr(self, "ctx", None):

@@ -17,6 +17,7 @@ std::vector<std::string> g_log;
 std::vector<int32_t> g_ends;
 std::vector<afd::TileRec> g_tiles;   // the last dispatch's layout tile records
 uint64_t g_err = afd::kNoError;
+int g_stall = 0;
 int g_capturing = 0;
 int g_fail = 0;
 
@@ -60,6 +61,9 @@ int be_launch_dispatch(const RoundPlan &p, void *)
         logf("dispatch cached ntok=%d T=%s", p.ntok, srcs.c_str());
     } else if (p.empty) {
         logf("dispatch empty E=%d T=%s", p.E, srcs.c_str());
+    } else if (p.onepass) {
+        logf("dispatch onepass ntok=%d nblk=%d T=%s tile=%d wait=%d", p.ntok, p.nblk, srcs.c_str(), p.tile,
+             p.wait_polls);
     } else if (p.fused) {
         logf("dispatch fused=1 ntok=%d nblk=%d T=%s", p.ntok, p.nblk, srcs.c_str());
     } else {
@@ -121,6 +125,13 @@ int be_read_error(uint64_t *, void *, int clear, uint64_t *word)
     return g_fail;
 }
 
+int be_read_stall(uint32_t *, void *, int clear, int *stalled)
+{
+    *stalled = g_stall;
+    if (clear) g_stall = 0;
+    return g_fail;
+}
+
 int be_device_sync()
 {
     logf("sync");
@@ -157,6 +168,7 @@ void afd_fake_set_ends(const int32_t *ends, int n, uint64_t err)
     g_err = err;
 }
 void afd_fake_set_capturing(int c) { g_capturing = c; }
+void afd_fake_set_stall(int s) { g_stall = s; }
 void afd_fake_set_fail(int f) { g_fail = f; }
 // The last dispatch's layout tile records as (src, t0, n, g0) quadruples;
 // returns their number (0: no table).

@@ -72,6 +72,9 @@ struct afd_ctx {
 
     // afd_create_static: the device whose static context this is, else -1
     int static_dev = -1;
+
+    // polls of a one-launch dispatch's wait before it gives up
+    int wait_polls = kDefaultWaitPolls;
 };
 
 namespace {
@@ -99,6 +102,8 @@ afd_status check_config(const afd_config *c)
         c->combine != AFD_COMBINE_PER_STAGE_FP8)
         return AFD_E_SHAPE;
     if (c->combine != AFD_COMBINE_ONCE && c->num_partitions < 2) return AFD_E_SHAPE;
+    if (c->dispatch != AFD_DISPATCH_AUTO && c->dispatch != AFD_DISPATCH_SPLIT && c->dispatch != AFD_DISPATCH_ONE_LAUNCH)
+        return AFD_E_SHAPE;
     // index ranges used by the kernels: tokens * K in int32, rows below 2^24
     const int64_t ntok = int64_t(c->num_sources) * c->capacity;
     if (ntok * c->topk >= (int64_t(1) << 31)) return AFD_E_SHAPE;
@@ -138,6 +143,8 @@ WorkspacePlan plan_workspace(const afd_config &c)
     w.partials = off;
     if (c.combine != AFD_COMBINE_ONCE)
         off += a(size_t(c.num_partitions) * ntok * size_t(partial_row_bytes(c.combine, c.hidden)));
+    w.tcount = off;
+    off += a(size_t(kLayoutMaxTiles) * c.num_experts * 4);
     w.total = off;
     return w;
 }
@@ -164,7 +171,7 @@ void *inbox_of(afd_ctx *c, int s)
 }
 
 // Fill the launch plan from the recorded dispatches and bound arenas.
-void build_plan(afd_ctx *c)
+void build_plan(afd_ctx *c, bool cached)
 {
     RoundPlan &p = c->plan;
     const afd_config &g = c->cfg;
@@ -191,6 +198,12 @@ void build_plan(afd_ctx *c)
               p.E <= kFusedMaxExperts && p.row_bytes / 16 <= kFusedMaxCols;
     p.tile = place_sources(c->T, p.N, p.voff);
     p.nblk = p.fused || p.empty ? 1 : p.voff[p.N] / p.tile;   // the one-kernel dispatch has no tiles
+    p.cached = cached;
+    // the one-launch dispatch publishes at most kLayoutMaxTiles tile counts,
+    // one expert per thread of a workgroup
+    p.onepass = g.dispatch == AFD_DISPATCH_ONE_LAUNCH && !cached && !p.empty && !p.fused &&
+                p.nblk <= kLayoutMaxTiles && p.E <= 256;
+    p.wait_polls = c->wait_polls;
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];
     for (int f = 0; f < p.F; ++f) {
         p.rows[f] = c->part[f].rows;
@@ -203,6 +216,8 @@ void build_plan(afd_ctx *c)
     p.packed = reinterpret_cast<int32_t *>(c->ws + c->wp.packed);
     p.slot = reinterpret_cast<int32_t *>(c->ws + c->wp.slot);
     p.partials = g.combine != AFD_COMBINE_ONCE ? reinterpret_cast<uint8_t *>(c->ws + c->wp.partials) : nullptr;
+    p.tcount = reinterpret_cast<uint32_t *>(c->ws + c->wp.tcount);
+    p.sync = reinterpret_cast<uint32_t *>(c->ws + kSyncOffset);
 }
 
 // Which kernels the round just enqueued runs (mirrors the executor's choice
@@ -217,6 +232,11 @@ void record_info(afd_ctx *c)
     if (p.cached) {
         i.dispatch_path = AFD_PATH_CACHED;
         i.dispatch_kernels = p.ntok > 0 ? 1 : 0;
+    } else if (p.onepass) {
+        i.dispatch_path = AFD_PATH_ONE_LAUNCH;
+        i.dispatch_kernels = 1;
+        i.layout_tiles = p.nblk;
+        i.tile_tokens = p.tile;
     } else if (p.empty) {
         i.dispatch_path = AFD_PATH_EMPTY;
         i.dispatch_kernels = 1;
@@ -243,6 +263,13 @@ void record_info(afd_ctx *c)
 
 extern "C" {
 
+afd_status afd_set_dispatch_wait(afd_ctx *c, int32_t polls)
+{
+    if (!c) return AFD_E_ARG;
+    c->wait_polls = polls;
+    return AFD_OK;
+}
+
 afd_status afd_get_round_info(const afd_ctx *c, afd_round_info *info)
 {
     if (!c || !info) return AFD_E_ARG;
@@ -260,6 +287,7 @@ const char *afd_status_string(afd_status st)
     case AFD_E_CAPACITY: return "buffer too small for the round";
     case AFD_E_ROUTE: return "invalid expert ids were routed (skipped)";
     case AFD_E_HIP: return "HIP runtime failure";
+    case AFD_E_TIMEOUT: return "a one-launch dispatch gave up waiting between workgroups";
     }
     return "unknown status";
 }
@@ -456,8 +484,7 @@ afd_status afd_worker_receive(afd_ctx *c, int32_t f, int32_t bucket, int32_t rhc
             if (be_is_capturing(stream, &capturing) != 0) return AFD_E_HIP;
             if (capturing) return AFD_E_ARG;
         }
-        build_plan(c);
-        c->plan.cached = c->round_cached;
+        build_plan(c, c->round_cached);
         if (be_launch_dispatch(c->plan, stream) != 0) return AFD_E_HIP;
         c->launched = true;
         record_info(c);
@@ -581,11 +608,15 @@ afd_status afd_get_error(afd_ctx *c, void *stream, int32_t clear, int32_t *code,
     uint64_t word = kNoError;
     if (be_read_error(reinterpret_cast<uint64_t *>(c->ws + c->wp.err), stream, clear, &word) != 0)
         return AFD_E_HIP;
+    int stalled = 0;
+    if (be_read_stall(reinterpret_cast<uint32_t *>(c->ws + kSyncOffset), stream, clear, &stalled) != 0)
+        return AFD_E_HIP;
     const bool set = word != kNoError;
     if (code) *code = set ? int32_t(word & 0xFFFF) : AFD_ROUTE_NONE;
     if (s) *s = set ? int32_t(word >> 56) : -1;
     if (t) *t = set ? int32_t((word >> 24) & 0xFFFFFFFFull) : -1;
     if (k) *k = set ? int32_t((word >> 16) & 0xFF) : -1;
+    if (stalled) return AFD_E_TIMEOUT;
     return set ? AFD_E_ROUTE : AFD_OK;
 }
 

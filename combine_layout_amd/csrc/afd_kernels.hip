@@ -112,7 +112,10 @@ struct DispatchHdr {
     uint64_t *err;           // sticky route-error word
     int64_t row_bytes;
     int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
-    int pad[8];
+    uint32_t *tcount;        // one-launch dispatch: [E][kLayoutMaxTiles] tagged tile counts
+    uint32_t *sync;          // one-launch dispatch: launch counter, finished workgroups, gave-up flag
+    int wait_polls;          // one-launch dispatch: polls before giving up
+    int pad[3];
 };
 
 // Layout tile record, 16 bytes, for rounds of at most kLayoutMaxTiles tiles:
@@ -144,6 +147,8 @@ struct Hdr {
     gptr<unsigned long long> err;
     int64_t row_bytes;
     int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
+    gptr<uint32_t> tcount, sync;
+    int wait_polls;
 };
 
 __device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a, u32x16 &r0, u32x16 &r1)
@@ -171,6 +176,9 @@ __device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a, u32x16 &r0, u32x1
     h.G = int(r1[5]);
     h.fp8 = int(r1[6]);
     h.tile = int(r1[7]);
+    h.tcount = (gptr<uint32_t>)((uint64_t(r1[9]) << 32) | uint64_t(r1[8]));
+    h.sync = (gptr<uint32_t>)((uint64_t(r1[11]) << 32) | uint64_t(r1[10]));
+    h.wait_polls = int(r1[12]);
     return h;
 }
 
@@ -907,6 +915,387 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
     }
 }
 
+// ---------------------------------------------------- one-launch dispatch ----
+//
+// Counts first, then the expansion, in one launch (design page, section 16)
+// for rounds of at most kLayoutMaxTiles layout tiles and 256 experts.
+// Workgroups 0 .. kLayoutMaxTiles - 1 each count the live choices of one
+// layout tile per expert and publish them as tagged words (tag << 9 |
+// count; a tile holds at most 256 tokens) with device-scope stores; a
+// counting workgroup past the round's last tile publishes zeros, so every
+// launch rewrites every word and a stale word always carries the previous
+// launch's tag, and then add one to the arrival counter.
+// Every other workgroup scatters TB slots of the tiled token space as
+// k_scatter does, but ranks its tokens' choices inside their tile itself
+// (lane masks over the tile's tokens up to its own, as k_layout builds them)
+// and takes the tile counts from the published words: one lane polls the
+// arrival counter until every counting workgroup has published, then the
+// workgroup reads the words once with device-scope loads (and checks their
+// tags, reading again if one is stale): the one hand-off between
+// workgroups.  The counting workgroups have the lowest
+// indices and never wait, so the hand-off completes whatever number of
+// workgroups is resident at once.  The wait is bounded: past h.wait_polls
+// polls a workgroup sets the sticky gave-up flag, marks its tokens' choices
+// skipped in the slot map (the combine then reads nothing for them), clears
+// ends[] if it is the first, stores no row and exits.  The tag is one more
+// than the launch counter; the last workgroup to finish advances the
+// counter and clears the arrival counter, and stream order shows the next
+// launch the new values.
+
+constexpr int kTagShift = 9;
+constexpr uint32_t kTagMask = 0x7FFFFFu;
+
+__device__ __forceinline__ void onepass_finish(const Hdr &h, uint32_t launch)
+{
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(&h.sync[kSyncDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n + 1u == gridDim.x) {
+            __hip_atomic_store(&h.sync[kSyncDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&h.sync[kSyncArrive], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&h.sync[0], launch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Ids of the token in tile slot `slot` (-1 past K or when `have` is false).
+template <int KMAX>
+__device__ __forceinline__ void load_token_ids(const int32_t *ids_first, int slot, int K, bool have, int (&ev)[KMAX])
+{
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) ev[k] = -1;
+    if (!have) return;
+    const gptr<const int32_t> idp = (gptr<const int32_t>)ids_first + int64_t(slot) * K;
+    if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(idp) & 15u) == 0) {
+#pragma unroll
+        for (int q = 0; q < KMAX / 4; ++q) {
+            u32x4 v4 = u32x4{~0u, ~0u, ~0u, ~0u};
+            if (4 * q < K) v4 = ((gptr<const u32x4>)idp)[q];
+            ev[4 * q] = int(v4.x);
+            ev[4 * q + 1] = int(v4.y);
+            ev[4 * q + 2] = int(v4.z);
+            ev[4 * q + 3] = int(v4.w);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int val = idp[k < K ? k : K - 1];
+            ev[k] = k < K ? val : -1;
+        }
+    }
+}
+
+template <int KMAX, int VMAX>
+__global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
+{
+    static_assert(kLayoutMaxTiles == 32, "tile counts polled into 32 registers");
+    const u32x4 tr = reinterpret_cast<const u32x4 *>(a.tiles)[blockIdx.x < kLayoutMaxTiles ? blockIdx.x : 0];
+    const Hdr h = load_hdr(a);
+    const uint32_t launch = __hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tag = (launch + 1u) & kTagMask;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int E = h.E, K = h.K, nblk = h.nblk;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+
+    if (blockIdx.x < kLayoutMaxTiles) {
+        // ---- counting workgroup of tile b: route check, count, publish
+        int *hist = reinterpret_cast<int *>(lds);          // [E + 1] (spare slot E for choices not live)
+        const int b = blockIdx.x;
+        for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
+        const int n_tile = b < nblk ? int(tr.w & 0xFFFFu) : 0;
+        const int s = int(tr.w >> 16);
+        const int32_t *ids_first = reinterpret_cast<const int32_t *>((uint64_t(tr.y) << 32) | uint64_t(tr.x));
+        int ev[KMAX];
+        load_token_ids<KMAX>(ids_first, tid, K, tid < n_tile, ev);
+        lds_barrier();
+        {
+            uint64_t err = kNoError;
+            const int g = int(tr.z) + tid;
+            const uint32_t live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);
+            if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], 1);
+        }
+        lds_barrier();
+        for (int e = tid; e < E; e += 256)
+            __hip_atomic_store(&h.tcount[e * kLayoutMaxTiles + b], (tag << kTagShift) | uint32_t(hist[e]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every thread's count stores acknowledged (the barrier waits for them)
+        // before the arrival; readers check the tags anyway, so no release
+        // fence (an L2 write-back) is needed
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        onepass_finish(h, launch);
+        return;
+    }
+
+    // ---- scatter workgroup: W tokens per wavefront, TB per workgroup
+    constexpr int W = VMAX >= 4 ? 1 : 4 / VMAX;
+    constexpr int TB = 4 * W;
+    __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
+    __shared__ int s_gaveup;
+    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);   // [4][E + 1]
+    int *pre = reinterpret_cast<int *>(mask + 4 * (E + 1));                   // [4][E]
+    int *pkl = pre + 4 * E;                                                   // [TB][K] (expert << 16 | rank), -1
+    int *base = pkl + TB * K;                                                 // [E]
+    int *A = base + E;                                                        // [E]
+    int *Cs = A + E;                                                          // [E]
+    const int nvec = h.nvec;
+    const int jb = blockIdx.x - kLayoutMaxTiles;
+    const int v_first = jb * TB;                 // first slot of the tiled token space
+    const int tile = v_first / h.tile;
+    const SourceRec src = load_source(a, source_of_tiled(a, h.N, v_first));
+    const int T_s = src.T;
+    const int t_first = v_first - src.voff + wave * W;    // source token of the wavefront's first slot
+    const int g_src = src.off;
+
+    // 1. the ids of the tile's tokens up to this workgroup's last slot
+    // (thread = slot of the tile), then the rows, weights and scales of this
+    // wavefront's tokens: loads complete in issue order, so the ids (needed
+    // first, for the ranks) go ahead of the rows
+    const int o = v_first - tile * h.tile;       // this workgroup's first slot inside its tile
+    const int tt0 = tile * h.tile - src.voff;    // source token of the tile's first slot
+    int ev[KMAX];
+    load_token_ids<KMAX>(src.ids + int64_t(tt0) * K, tid, K, tid < o + TB && tt0 + tid < T_s, ev);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 v[W][VMAX];
+    float wk[W];
+    float scv[W];
+    {
+        const int kl = lane < K ? lane : 0;
+        const bool fp8 = h.fp8 != 0;
+        const float *sbase = fp8 ? src.scale : src.w;
+        const int64_t sst = fp8 ? src.sst : int64_t(K);
+        const int64_t sgl = fp8 ? int64_t(lane < h.G ? lane : 0) * src.ssg : 0;
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int t = t_first + j < T_s ? t_first + j : T_s - 1;
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = i * kWave + lane;
+                v[j][i] = xs[c < nvec ? c : 0];
+            }
+            wk[j] = ((gptr<const float>)src.w)[int64_t(t) * K + kl];
+            scv[j] = ((gptr<const float>)sbase)[int64_t(t) * sst + sgl];
+        }
+    }
+    if (lane == 0) {
+        if (wave == 0) table_to_lds(s_prow, a.rows);
+        if (wave == 1) table_to_lds(s_pw, a.roww);
+        if (wave == 2) table_to_lds(s_ps, a.scales);
+        if (wave == 3) s_gaveup = 0;
+    }
+    for (int i = tid; i < 4 * (E + 1); i += 256) mask[i] = 0ull;
+    lds_barrier();
+
+    // 2. in-tile ranks of this workgroup's tokens (route errors are recorded
+    // by the counting workgroups)
+    uint32_t live;
+    {
+        uint64_t err_unused = kNoError;
+        live = classify_token<KMAX>(ev, E, 0, 0, err_unused);
+        unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        const unsigned long long bit = 1ull << lane;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E], bit);
+    }
+    lds_barrier();
+    for (int e = tid; e < E; e += 256) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            pre[w * E + e] = run;
+            run += __popcll(mask[w * (E + 1) + e]);
+        }
+    }
+    lds_barrier();
+    if (tid >= o && tid < o + TB) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        int *dst = pkl + (tid - o) * K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const bool l = (live >> k) & 1u;
+            const int e = l ? ev[k] : 0;
+            if (k < K) dst[k] = l ? ((e << 16) | (pre[wave * E + e] + __popcll(mrow[e] & below))) : -1;
+        }
+    }
+
+    // 3. the published tile counts: one lane polls the arrival counter until
+    // every counting workgroup has published (bounded); then thread e reads
+    // expert e's run of words (expert-major, two tiles per 8-byte
+    // device-scope load) and checks that every one of the round's tiles
+    // carries this launch's tag, reading again if not (bounded)
+    if (tid == 0) {
+        for (int it = 0;; ++it) {
+            if (it > h.wait_polls) {
+                s_gaveup = 1;
+                break;
+            }
+            if (__hip_atomic_load(&h.sync[kSyncArrive], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                uint32_t(kLayoutMaxTiles))
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    // (no acquire fence: on this GPU it invalidates the XCD's L2, which
+    // measured far slower than device-scope reads of the words, whose tags
+    // show whether they are this launch's)
+    lds_barrier();
+    uint32_t cw[kLayoutMaxTiles];
+    if (tid < E && !s_gaveup) {
+        const gptr<unsigned long long> run = (gptr<unsigned long long>)(h.tcount + tid * kLayoutMaxTiles);
+        for (int it = 0;; ++it) {
+            if (it > h.wait_polls) {
+                s_gaveup = 1;
+                break;
+            }
+#pragma unroll
+            for (int q = 0; q < kLayoutMaxTiles / 2; ++q) {
+                const unsigned long long two = __hip_atomic_load(&run[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                cw[2 * q] = uint32_t(two);
+                cw[2 * q + 1] = uint32_t(two >> 32);
+            }
+            bool fresh = true;
+#pragma unroll
+            for (int b = 0; b < kLayoutMaxTiles; ++b) fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
+            if (fresh) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    lds_barrier();
+    if (s_gaveup) {
+        // no counts: this workgroup's choices are skipped, nothing is stored
+        __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            const int t = t_first + j;
+            if (t < T_s && lane < K) {
+                i32x2 sl;
+                sl.x = -1;
+                sl.y = __float_as_int(wk[j]);
+                ((gptr<i32x2>)h.slot)[int64_t(g_src + t) * K + lane] = sl;
+            }
+        }
+        if (jb == 0)
+            for (int e = tid; e < E; e += 256) h.ends[e] = 0;
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        onepass_finish(h, launch);
+        return;
+    }
+
+    // 4. this tile's first row of every expert (as k_scatter)
+    for (int e = tid; e < E; e += 256) {
+        int C = 0, before = 0;
+#pragma unroll
+        for (int b = 0; b < kLayoutMaxTiles; ++b) {
+            const int c = b < nblk ? int(cw[b] & ((1u << kTagShift) - 1u)) : 0;
+            C += c;
+            before += b < tile ? c : 0;
+        }
+        A[e] = align_up_i(C, h.alpha);
+        Cs[e] = C;
+        base[e] = before;
+    }
+    lds_barrier();
+    block_exclusive_scan(A, E);
+    for (int e = tid; e < E; e += 256) {
+        const int start = A[e] - A[(e / h.E_loc) * h.E_loc];
+        base[e] += start;
+        if (jb == 0) h.ends[e] = start + Cs[e];
+    }
+    lds_barrier();
+    // every row, weight and scale load (and every poll) has been waited for
+    // here, once, before the first store (see k_scatter)
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // 5. slots and stores, token by token (as k_scatter)
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const int t = t_first + j;
+        if (t >= T_s) break;
+        const int g = g_src + t;
+        int part = -1, row = -1;
+        uint64_t d = 0, ds = 0;
+        const int pkj = lane < K ? pkl[(wave * W + j) * K + lane] : -1;
+        if (pkj >= 0) {
+            const int e = pkj >> 16;
+            row = base[e] + (pkj & 0xFFFF);
+            part = e / h.E_loc;
+            d = s_prow[part] + uint64_t(row) * uint64_t(h.row_bytes);
+            ds = s_ps[part] + uint64_t(row) * uint64_t(h.G) * 4u;
+            ((gptr<float>)s_pw[part])[row] = wk[j];
+        }
+        if (lane < K) {
+            i32x2 sl;
+            sl.x = part < 0 ? -1 : ((part << 24) | row);
+            sl.y = __float_as_int(wk[j]);
+            ((gptr<i32x2>)h.slot)[int64_t(g) * K + lane] = sl;
+        }
+        const int dlo = int(uint32_t(d)), dhi = int(uint32_t(d >> 32));
+        for (int k = 0; k < K; ++k) {
+            const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                                (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+            if (dk == 0) continue;
+            const gptr<u32x4> dst = (gptr<u32x4>)dk;
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = i * kWave + lane;
+                if (c < nvec) __builtin_nontemporal_store(v[j][i], &dst[c]);
+            }
+        }
+        if (nvec > kWave * VMAX) {
+            const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
+            for (int cb = kWave * VMAX; cb < nvec; cb += kWave * VMAX) {
+                u32x4 r[VMAX];
+#pragma unroll
+                for (int i = 0; i < VMAX; ++i) {
+                    const int c = cb + i * kWave + lane;
+                    if (c < nvec) r[i] = xs[c];
+                }
+                for (int k = 0; k < K; ++k) {
+                    const uint64_t dk = uint64_t(uint32_t(__builtin_amdgcn_readlane(dlo, k))) |
+                                        (uint64_t(uint32_t(__builtin_amdgcn_readlane(dhi, k))) << 32);
+                    if (dk == 0) continue;
+                    const gptr<u32x4> dst = (gptr<u32x4>)dk;
+#pragma unroll
+                    for (int i = 0; i < VMAX; ++i) {
+                        const int c = cb + i * kWave + lane;
+                        if (c < nvec) __builtin_nontemporal_store(r[i], &dst[c]);
+                    }
+                }
+            }
+        }
+        if (h.fp8) {
+            const int G = h.G;
+            const int slo = int(uint32_t(ds)), shi = int(uint32_t(ds >> 32));
+            if (lane < G) {
+                for (int k = 0; k < K; ++k) {
+                    const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                        (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                    if (sk == 0) continue;
+                    ((gptr<float>)sk)[lane] = scv[j];
+                }
+            }
+            if (G > kWave) {
+                const gptr<const float> sc = (gptr<const float>)src.scale + int64_t(t) * src.sst;
+                for (int bb = kWave + lane; bb < G; bb += kWave) {
+                    const float val = sc[int64_t(bb) * src.ssg];
+                    for (int k = 0; k < K; ++k) {
+                        const uint64_t sk = uint64_t(uint32_t(__builtin_amdgcn_readlane(slo, k))) |
+                                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(shi, k))) << 32);
+                        if (sk == 0) continue;
+                        ((gptr<float>)sk)[bb] = val;
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+        }
+    }
+    onepass_finish(h, launch);
+}
+
 // Dispatch of a cached round.  Block = 256 threads = 256 / LPT tokens, LPT
 // (64, 128 or 256) lanes per token, each lane holding VMAX 16-byte columns
 // (column i * LPT + lane of its token); longer rows loop over chunks.  Every
@@ -1429,10 +1818,14 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     }
 }
 
-// A fresh static-scratch workspace: the route-error word starts as "none".
-__global__ __launch_bounds__(64) void k_init_err(unsigned long long *err)
+// A fresh static-scratch workspace: the route-error word starts as "none",
+// and the one-launch dispatch's counters and tagged tile counts as zero.
+__global__ __launch_bounds__(256) void k_init_ws(unsigned long long *err, uint32_t *sync, uint32_t *tcount,
+                                                 int ncount)
 {
     if (threadIdx.x == 0) *err = kNoError;
+    if (threadIdx.x < 48) sync[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < ncount; i += 256) tcount[i] = 0u;
 }
 
 // Dispatch of a round without tokens: every expert's range is empty.
@@ -1490,6 +1883,9 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.h.blkcnt = p.blkcnt;
     a.h.packed = p.packed;
     a.h.slot = p.slot;
+    a.h.tcount = p.tcount;
+    a.h.sync = p.sync;
+    a.h.wait_polls = p.wait_polls;
     TileRec tr[kLayoutMaxTiles];
     const int ntr = layout_tiles(p, tr);
     for (int b = 0; b < ntr; ++b) {
@@ -1516,6 +1912,20 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
 {
     if (k32) hipLaunchKernelGGL((k_fused<VMAX, 32>), grid, dim3(256), lds, st, a);
     else hipLaunchKernelGGL((k_fused<VMAX, 8>), grid, dim3(256), lds, st, a);
+    return launched_ok();
+}
+
+// One-launch dispatch: kLayoutMaxTiles counting workgroups, then one
+// scatter workgroup per TB slots of the tiled token space.
+template <int VMAX>
+int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, hipStream_t st)
+{
+    constexpr int TB = 4 * (VMAX >= 4 ? 1 : 4 / VMAX);
+    const size_t scatter_lds = size_t(4) * (E + 1) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(3) * E * 4;
+    const size_t lds = scatter_lds > size_t(E + 1) * 4 ? scatter_lds : size_t(E + 1) * 4;
+    const dim3 grid(kLayoutMaxTiles + nslots / TB);
+    if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(256), lds, st, a);
     return launched_ok();
 }
 
@@ -1561,11 +1971,14 @@ StageArgs make_stage_args(const RoundPlan &p)
 
 int be_init_workspace(void *workspace, const WorkspacePlan &wp)
 {
+    // the error word "none", the one-launch dispatch's counters zero, and its
+    // tagged tile counts zero (tag 0 is never a launch's tag)
     uint64_t hdr[32];
     std::memset(hdr, 0, sizeof(hdr));
     hdr[wp.err / 8] = kNoError;
     if (hipMemcpy(workspace, hdr, sizeof(hdr), hipMemcpyHostToDevice) != hipSuccess) return 1;
-    return 0;
+    if (hipMemset(static_cast<char *>(workspace) + wp.tcount, 0, wp.total - wp.tcount) != hipSuccess) return 1;
+    return hipDeviceSynchronize() == hipSuccess ? 0 : 1;
 }
 
 int be_is_capturing(void *stream, int *capturing)
@@ -1597,6 +2010,14 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     if (p.empty) {
         hipLaunchKernelGGL(k_zero_ends, dim3(1), dim3(256), 0, st, p.ends, p.E);
         return launched_ok();
+    }
+    if (p.onepass) {
+        switch (vm) {
+        case 1: return launch_onepass_v<1>(a, k32, p.voff[p.N], p.E, p.K, st);
+        case 2: return launch_onepass_v<2>(a, k32, p.voff[p.N], p.E, p.K, st);
+        case 4: return launch_onepass_v<4>(a, k32, p.voff[p.N], p.E, p.K, st);
+        default: return launch_onepass_v<8>(a, k32, p.voff[p.N], p.E, p.K, st);
+        }
     }
     if (p.fused) {
         // one block per token; 256 threads hold the row, VMAX columns each
@@ -1707,6 +2128,21 @@ int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream)
     return launched_ok();
 }
 
+int be_read_stall(uint32_t *dev_sync, void *stream, int clear, int *stalled)
+{
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, dev_sync + kSyncStall, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return 1;
+    if (hipStreamSynchronize(st) != hipSuccess) return 1;
+    *stalled = v != 0;
+    if (clear && v != 0) {
+        const uint32_t zero = 0;
+        if (hipMemcpyAsync(dev_sync + kSyncStall, &zero, 4, hipMemcpyHostToDevice, st) != hipSuccess) return 1;
+        if (hipStreamSynchronize(st) != hipSuccess) return 1;
+    }
+    return 0;
+}
+
 int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word)
 {
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1745,8 +2181,10 @@ int be_static_scratch(int *device, void **ptr)
 
 int be_init_static(void *workspace, const WorkspacePlan &wp)
 {
-    auto *err = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + wp.err);
-    hipLaunchKernelGGL(k_init_err, dim3(1), dim3(64), 0, nullptr, err);
+    char *ws = static_cast<char *>(workspace);
+    auto *err = reinterpret_cast<unsigned long long *>(ws + wp.err);
+    hipLaunchKernelGGL(k_init_ws, dim3(1), dim3(256), 0, nullptr, err, reinterpret_cast<uint32_t *>(ws + kSyncOffset),
+                       reinterpret_cast<uint32_t *>(ws + wp.tcount), int((wp.total - wp.tcount) / 4));
     if (launched_ok()) return 1;
     return hipStreamSynchronize(nullptr) == hipSuccess ? 0 : 1;
 }

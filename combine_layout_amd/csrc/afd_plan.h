@@ -37,6 +37,16 @@ constexpr int kFusedMaxCols = 2048;
 // numeric minimum is the first offender in (source, token, k) order.
 constexpr uint64_t kNoError = ~0ull;
 
+// The workspace's first 256 bytes: the route-error word at 0, and the
+// one-launch dispatch's words (uint32) at byte 64: launch counter at index
+// 0, finished workgroups at 16, the sticky gave-up flag at 32, published
+// tiles at 40.
+constexpr size_t kSyncOffset = 64;
+constexpr int kSyncDone = 16;
+constexpr int kSyncStall = 32;
+constexpr int kSyncArrive = 40;
+constexpr int kDefaultWaitPolls = 1000000;
+
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 // Larger rounds place every source on a tile boundary of a "tiled" token
@@ -73,6 +83,7 @@ struct WorkspacePlan {
                            // bytes of slack (the combine reads slots 64 bytes at a time)
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
     size_t partials = 0;   // per-stage combine: [F][N][capacity] rows of partial_row_bytes
+    size_t tcount = 0;     // one-launch dispatch: uint32 [E][kLayoutMaxTiles] tagged tile counts
     size_t total = 0;
     int nblk_max = 0;
 };
@@ -91,6 +102,7 @@ struct RoundPlan {
     int tok_off[kMaxSources + 1] = {};
     bool fused = false;      // one-kernel dispatch
     bool empty = false;      // no tokens: the dispatch only clears ends[]
+    bool onepass = false;    // one-launch dispatch (counting and scatter in one kernel)
     bool cached = false;     // scatter from the slot map of the last layout
     int nblk = 0;            // layout tiles (split path)
     int tile = 0;            // tokens per layout tile
@@ -115,6 +127,10 @@ struct RoundPlan {
     int32_t *slot = nullptr;
     // per-stage combine: row (f, s, t) at partials + ((f * N + s) * capacity + t) * prow
     uint8_t *partials = nullptr;
+    // one-launch dispatch
+    uint32_t *tcount = nullptr;   // [E][kLayoutMaxTiles]
+    uint32_t *sync = nullptr;     // launch counter, finished workgroups, gave-up flag
+    int wait_polls = kDefaultWaitPolls;
 };
 
 // Layout tile records of a round of at most kLayoutMaxTiles tiles: tile b
@@ -155,6 +171,8 @@ int be_launch_partial(const RoundPlan &p, int f, void *stream);   // per-stage c
 int be_launch_final(const RoundPlan &p, int s, void *stream);     // per-stage combine, stage two
 int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream);
 int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word);
+// The one-launch dispatch's gave-up flag (and clears it when asked).
+int be_read_stall(uint32_t *dev_sync, void *stream, int clear, int *stalled);
 int be_device_sync();
 // The current device and the address of its static scratch array (found
 // once per device); no allocation.

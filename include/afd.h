@@ -53,7 +53,8 @@ typedef enum {
     AFD_E_ORDER = -3,     /* call out of the round order */
     AFD_E_CAPACITY = -4,  /* a buffer is smaller than the round needs */
     AFD_E_ROUTE = -5,     /* invalid expert ids were seen (work was done) */
-    AFD_E_HIP = -6        /* a HIP runtime call failed */
+    AFD_E_HIP = -6,       /* a HIP runtime call failed */
+    AFD_E_TIMEOUT = -7    /* a one-launch dispatch gave up waiting between workgroups */
 } afd_status;
 
 typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
@@ -86,6 +87,23 @@ typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
  */
 typedef enum { AFD_COMBINE_ONCE = 0, AFD_COMBINE_PER_STAGE = 1, AFD_COMBINE_PER_STAGE_FP8 = 2 } afd_combine_mode;
 
+/*
+ * How a round's dispatch is launched (design page, section 16: counts
+ * first, then the expansion).  Rounds of at most 512 tokens always take the
+ * one-kernel dispatch, and cached rounds the cached scatter.
+ *   AFD_DISPATCH_AUTO        the library chooses (currently AFD_DISPATCH_SPLIT)
+ *   AFD_DISPATCH_SPLIT       a layout kernel over token tiles, then the scatter
+ *   AFD_DISPATCH_ONE_LAUNCH  one launch: its first 32 workgroups count one
+ *                            tile each and publish the counts; every other
+ *                            workgroup ranks its tokens inside their tile
+ *                            itself, waits for the published counts (the one
+ *                            hand-off between workgroups, a bounded wait) and
+ *                            scatters.  Applies to rounds of at most 32
+ *                            tiles (8192 token slots) and 256 experts; other
+ *                            rounds take the split path.
+ */
+typedef enum { AFD_DISPATCH_AUTO = 0, AFD_DISPATCH_SPLIT = 1, AFD_DISPATCH_ONE_LAUNCH = 2 } afd_dispatch_mode;
+
 /* Route error codes (contract page: ids unique per token, in [0, E), or -1). */
 typedef enum { AFD_ROUTE_NONE = 0, AFD_ROUTE_RANGE = 1, AFD_ROUTE_NEG = 2, AFD_ROUTE_DUP = 3 } afd_route_code;
 
@@ -102,6 +120,7 @@ typedef enum { AFD_ROUTE_NONE = 0, AFD_ROUTE_RANGE = 1, AFD_ROUTE_NEG = 2, AFD_R
  *   dtype            activation format: BF16, or float8_e4m3fn with FP32
  *                    block-128 scales [T, H/128]
  *   combine          afd_combine_mode (fixed for the context's lifetime)
+ *   dispatch         afd_dispatch_mode (fixed for the context's lifetime)
  */
 typedef struct {
     int32_t num_sources;
@@ -112,7 +131,8 @@ typedef struct {
     int32_t expert_alignment;
     int32_t capacity;
     int32_t dtype;   /* afd_dtype */
-    int32_t combine; /* afd_combine_mode */
+    int32_t combine;  /* afd_combine_mode */
+    int32_t dispatch; /* afd_dispatch_mode */
 } afd_config;
 
 /* Opaque receipt (contract page: keep it unchanged through the matching
@@ -301,13 +321,26 @@ afd_status afd_source_collect(afd_ctx *ctx, int32_t s, int32_t view, const void 
                               int64_t *row_stride, void *stream);
 
 /*
+ * afd_set_dispatch_wait: the number of polls a workgroup of a one-launch
+ * dispatch makes for the published tile counts before it gives up (default
+ * 1,000,000, about a second; a negative value gives up at once).  A
+ * workgroup that gives up stores no rows and marks its tokens' choices as
+ * skipped, so the round's outputs are defined (its tokens' outputs are +0);
+ * afd_get_error then reports AFD_E_TIMEOUT.  Host state only.
+ * Errors: AFD_E_ARG (NULL).
+ */
+afd_status afd_set_dispatch_wait(afd_ctx *ctx, int32_t polls);
+
+/*
  * afd_get_error: synchronise `stream` and read the sticky route-error word:
  * the first invalid choice in (source, token, k) order among every round
  * since the last clear, with its code (afd_route_code).  Invalid choices are
  * skipped everywhere (count, rank, scatter, combine), so nothing is written
  * out of bounds.  clear = 1 resets the word.  Outputs may be NULL.
- * Returns AFD_OK (no error), AFD_E_ROUTE (word set), AFD_E_ARG (stream
- * capturing), AFD_E_HIP.
+ * Returns AFD_OK (no error), AFD_E_ROUTE (word set), AFD_E_TIMEOUT (a
+ * one-launch dispatch gave up waiting since the last clear; sticky the same
+ * way, reported before route errors), AFD_E_ARG (stream capturing),
+ * AFD_E_HIP.
  */
 afd_status afd_get_error(afd_ctx *ctx, void *stream, int32_t clear, int32_t *code, int32_t *s, int32_t *t,
                          int32_t *k);
@@ -330,7 +363,8 @@ typedef enum {
     AFD_PATH_ONE_KERNEL = 1,  /* small rounds: layout and scatter in one kernel */
     AFD_PATH_TILED = 2,       /* layout kernel over token tiles, then the scatter */
     AFD_PATH_CACHED = 3,      /* afd_source_dispatch_cached: the scatter alone */
-    AFD_PATH_EMPTY = 4        /* no tokens: ends[] cleared */
+    AFD_PATH_EMPTY = 4,       /* no tokens: ends[] cleared */
+    AFD_PATH_ONE_LAUNCH = 5   /* AFD_DISPATCH_ONE_LAUNCH: counting and scatter in one launch */
 } afd_dispatch_path;
 
 typedef struct {

@@ -31,8 +31,8 @@ def log(lib):
     return out
 
 
-def cfg(N=2, F=2, E=8, K=2, H=256, alpha=4, cap=16, dtype=0, combine=0):
-    return nat.Config(N, F, E, K, H, alpha, cap, dtype, combine)
+def cfg(N=2, F=2, E=8, K=2, H=256, alpha=4, cap=16, dtype=0, combine=0, dispatch=0):
+    return nat.Config(N, F, E, K, H, alpha, cap, dtype, combine, dispatch)
 
 
 def query(lib, c, bucket):
@@ -732,3 +732,49 @@ def test_create_static(lib):
     assert lib.afd_destroy(ctx) == 0
     assert lib.afd_create_static(ctypes.byref(c), ctypes.byref(other)) == 0   # free again
     assert lib.afd_destroy(other) == 0
+
+
+def test_one_launch_dispatch_plan(lib):
+    """AFD_DISPATCH_ONE_LAUNCH runs tiled rounds of at most 32 tiles and 256
+    experts as one launch; small rounds keep the one-kernel dispatch, larger
+    ones (more tiles, more experts) and cached rounds the other paths."""
+    assert lib.afd_query(ctypes.byref(cfg(dispatch=3)), 8, None, None) == nat.AFD_E_SHAPE
+    x = Ctx(lib, cfg(E=8, K=2, cap=8192, dispatch=nat.AFD_DISPATCH_ONE_LAUNCH))
+    assert lib.afd_set_dispatch_wait(None, 5) == nat.AFD_E_ARG
+    assert lib.afd_set_dispatch_wait(x.ctx, 77) == 0
+    lib.afd_fake_log_clear()
+    x.full_round(T=(4, 3))
+    assert log(lib)[0].startswith("dispatch fused=1")
+    x.full_round(T=(600, 3))
+    assert log(lib)[0] == "dispatch onepass ntok=603 nblk=11 T=600,3 tile=64 wait=77"
+    assert nat.DISPATCH_PATHS[_info(lib, x).dispatch_path] == "one_launch"
+    x.full_round(T=(8192, 0))                                   # 32 tiles of 256: still one launch
+    assert log(lib)[0].startswith("dispatch onepass ntok=8192 nblk=32")
+    x.full_round(T=(8192, 1))                                   # 33 tiles: the split path
+    assert log(lib)[0].startswith("dispatch fused=0 ntok=8193 nblk=33")
+    for s, T in enumerate((8192, 1)):
+        assert x.dispatch_cached(s, T) == 0
+    recs = [x.receive(f)[1] for f in range(2)]
+    assert log(lib)[0].startswith("dispatch cached")
+    for f, rec in enumerate(recs):
+        assert x.reply(f, rec) == 0
+    for s in range(2):
+        assert x.collect(s)[0] == 0
+    x.destroy()
+    y = Ctx(lib, cfg(E=512, F=2, K=2, cap=1024, dispatch=nat.AFD_DISPATCH_ONE_LAUNCH))
+    lib.afd_fake_log_clear()
+    y.full_round(T=(600, 3))                                    # more than 256 experts: the split path
+    assert log(lib)[0].startswith("dispatch fused=0")
+    y.destroy()
+
+
+def test_timeout_reported_by_get_error(lib):
+    x = Ctx(lib, cfg())
+    code, s, t, k = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    lib.afd_fake_set_stall(1)
+    args = (ctypes.byref(code), ctypes.byref(s), ctypes.byref(t), ctypes.byref(k))
+    assert lib.afd_get_error(x.ctx, None, 0, *args) == nat.AFD_E_TIMEOUT
+    assert lib.afd_get_error(x.ctx, None, 1, *args) == nat.AFD_E_TIMEOUT     # reported, then cleared
+    assert lib.afd_get_error(x.ctx, None, 0, *args) == nat.AFD_OK
+    assert lib.afd_status_string(nat.AFD_E_TIMEOUT)
+    x.destroy()
