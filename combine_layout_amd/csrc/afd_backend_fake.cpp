@@ -105,9 +105,15 @@ int be_launch_partial(const RoundPlan &p, int f, void *)
     return g_fail;
 }
 
-int be_launch_final(const RoundPlan &p, int s, void *)
+int be_launch_final(const RoundPlan &p, void *)
 {
-    logf("final s=%d T=%d out=%p", s, p.tok_off[s + 1] - p.tok_off[s], p.out[s]);
+    std::string outs;
+    for (int s = 0; s < p.N; ++s) {
+        char b[64];
+        snprintf(b, sizeof(b), "%s%p", s ? "," : "", p.out[s]);
+        outs += b;
+    }
+    logf("final ntok=%d out=%s", p.ntok, outs.c_str());
     return g_fail;
 }
 

@@ -250,12 +250,7 @@ void record_info(afd_ctx *c)
         i.tile_tokens = p.tile;
     }
     if (p.ntok > 0) {
-        if (p.combine == AFD_COMBINE_ONCE) {
-            i.combine_kernels = 1;
-        } else {
-            i.combine_kernels = p.F;
-            for (int s = 0; s < p.N; ++s) i.combine_kernels += p.tok_off[s + 1] > p.tok_off[s] ? 1 : 0;
-        }
+        i.combine_kernels = p.combine == AFD_COMBINE_ONCE ? 1 : p.F + 1;
     }
 }
 
@@ -565,7 +560,9 @@ afd_status afd_source_collect(afd_ctx *c, int32_t s, int32_t view, const void **
     if (c->collected[s]) return AFD_E_ORDER;
     const void *res;
     if (g.num_partitions > 1) {
-        if (g.combine != AFD_COMBINE_ONCE && c->T[s] > 0 && be_launch_final(c->plan, s, stream) != 0)
+        // per-stage: the round's first collect runs stage two for every source
+        if (g.combine != AFD_COMBINE_ONCE && c->ncollected == 0 && c->plan.ntok > 0 &&
+            be_launch_final(c->plan, stream) != 0)
             return AFD_E_HIP;
         res = c->out_user[s];
     } else if (view) {

@@ -42,9 +42,10 @@
 //             stores it, or its FP8 form (codes plus one power-of-two scale
 //             byte per 128 elements, found with a 16-lane max), into the
 //             source's partial rows in the workspace.
-//   k_final   per-stage combine, stage two (at source s's collect): adds the
-//             token's partials in float32, partitions in ascending order of
-//             their last live top-k lane, and rounds once to BF16.
+//   k_final   per-stage combine, stage two (at the round's first collect, for
+//             every source): adds each token's partials in float32,
+//             partitions in ascending order of their last live top-k lane,
+//             and rounds once to BF16.
 //
 // Nothing here uses MFMA: the round is data movement plus one multiply-add
 // per reply element, bound by HBM bandwidth.  Expanded rows are written and
@@ -192,12 +193,12 @@ __device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a)
 // partials + ((f * N + s) * capacity + t) * prow.
 struct StageArgs {
     const uint16_t *reply;   // stage one: partition f's replies
-    uint16_t *out;           // stage two: source s's output
     uint8_t *partials;
     const int32_t *slot;
     int64_t prow;
     int tok_off[kMaxSources + 1];
-    int N, F, ntok, K, H, nvec, nseg, capacity, f, s, T;
+    int N, F, ntok, K, H, nvec, nseg, capacity, f;
+    uint16_t *outs[kMaxSources];   // stage two: every source's output
 };
 
 // The combine's scalars and the first four partitions' reply bases fill the
@@ -1579,8 +1580,11 @@ __device__ __forceinline__ int fp8_group_exponent(uint32_t amax_bits)
     return e < -117 ? -117 : e;
 }
 
-// Stage one of the per-stage combine for partition a.f.
-template <bool FP8>
+// Stage one of the per-stage combine for partition a.f: one wavefront per
+// (token, segment of 64 * VPL 16-byte columns).  A token has about K/F live
+// rows in one partition, so a wavefront takes VPL columns per lane to keep
+// as many row loads in flight as the single-rounding combine does.
+template <bool FP8, int VPL>
 __global__ __launch_bounds__(256) void k_partial(StageArgs a)
 {
 #pragma clang fp contract(off)
@@ -1599,97 +1603,112 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
     const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
     const int t = g - t0;
     const int nvec = a.nvec;
-    const int c = seg * kWave + lane;
+    const int c0 = seg * kWave * VPL + lane;
     uint64_t raddr = 0;
     if (mine) raddr = reinterpret_cast<uint64_t>(a.reply) + uint64_t(sl.x & 0xFFFFFF) * uint64_t(a.H) * 2u;
     const int rlo = int(uint32_t(raddr)), rhi = int(uint32_t(raddr >> 32));
-    float acc[8];
+    float acc[VPL][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
     for (int k0 = 0; k0 < a.K; k0 += 8) {
-        u32x4 y[8];
+        u32x4 y[8][VPL];
         uint64_t rk[8];
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             rk[kk] = uint64_t(uint32_t(__builtin_amdgcn_readlane(rlo, k0 + kk))) |
                      (uint64_t(uint32_t(__builtin_amdgcn_readlane(rhi, k0 + kk))) << 32);
             const gptr<const u32x4> src = (gptr<const u32x4>)rk[kk];
-            y[kk] = (rk[kk] != 0 && c < nvec) ? __builtin_nontemporal_load(&src[c]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int c = c0 + i * kWave;
+                y[kk][i] = (rk[kk] != 0 && c < nvec) ? __builtin_nontemporal_load(&src[c]) : u32x4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             if (rk[kk] == 0) continue;
             const float w = __int_as_float(__builtin_amdgcn_readlane(sl.y, k0 + kk));
-            const uint32_t q[4] = {y[kk].x, y[kk].y, y[kk].z, y[kk].w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float plo = w * __uint_as_float(q[j] << 16);
-                const float phi = w * __uint_as_float(q[j] & 0xFFFF0000u);
-                acc[2 * j] = acc[2 * j] + plo;
-                acc[2 * j + 1] = acc[2 * j + 1] + phi;
+            for (int i = 0; i < VPL; ++i) {
+                const uint32_t q[4] = {y[kk][i].x, y[kk][i].y, y[kk][i].z, y[kk][i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float plo = w * __uint_as_float(q[j] << 16);
+                    const float phi = w * __uint_as_float(q[j] & 0xFFFF0000u);
+                    acc[i][2 * j] = acc[i][2 * j] + plo;
+                    acc[i][2 * j + 1] = acc[i][2 * j + 1] + phi;
+                }
             }
         }
     }
-    uint32_t b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = bf16_rne_bits(acc[j]);
     uint8_t *row = a.partials + ((int64_t(a.f) * a.N + s) * a.capacity + t) * a.prow;
-    if (!FP8) {
-        if (c < nvec) {
-            u32x4 r;
-            r.x = b[0] | (b[1] << 16);
-            r.y = b[2] | (b[3] << 16);
-            r.z = b[4] | (b[5] << 16);
-            r.w = b[6] | (b[7] << 16);
-            reinterpret_cast<u32x4 *>(row)[c] = r;
-        }
-        return;
-    }
-    // FP8: a group of 128 elements is 16 lanes; amax over the magnitudes of
-    // its non-NaN elements (integer order equals float order for them)
-    uint32_t am = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t m = (b[j] << 16) & 0x7FFFFFFFu;
-        am = (m <= 0x7F800000u && m > am) ? m : am;
+    for (int i = 0; i < VPL; ++i) {
+        const int c = c0 + i * kWave;
+        uint32_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = bf16_rne_bits(acc[i][j]);
+        if (!FP8) {
+            if (c < nvec) {
+                u32x4 r;
+                r.x = b[0] | (b[1] << 16);
+                r.y = b[2] | (b[3] << 16);
+                r.z = b[4] | (b[5] << 16);
+                r.w = b[6] | (b[7] << 16);
+                reinterpret_cast<u32x4 *>(row)[c] = r;
+            }
+            continue;
+        }
+        // FP8: a group of 128 elements is 16 lanes; amax over the magnitudes
+        // of its non-NaN elements (integer order equals float order for them)
+        uint32_t am = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t m = (b[j] << 16) & 0x7FFFFFFFu;
+            am = (m <= 0x7F800000u && m > am) ? m : am;
+        }
+        // max over the 16-lane DPP row: rotations by 1, 2, 4 and 8
+        {
+            uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x121, 0xF, 0xF, false));  // row_ror:1
+            am = o > am ? o : am;
+            o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x122, 0xF, 0xF, false));           // row_ror:2
+            am = o > am ? o : am;
+            o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x124, 0xF, 0xF, false));           // row_ror:4
+            am = o > am ? o : am;
+            o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x128, 0xF, 0xF, false));           // row_ror:8
+            am = o > am ? o : am;
+        }
+        const int e = fp8_group_exponent(am);
+        const float inv = __uint_as_float(uint32_t(127 - e) << 23);              // 2^-e, a normal float
+        const uint32_t lo = e4m3_codes4(__uint_as_float(b[0] << 16) * inv, __uint_as_float(b[1] << 16) * inv,
+                                        __uint_as_float(b[2] << 16) * inv, __uint_as_float(b[3] << 16) * inv);
+        const uint32_t hi = e4m3_codes4(__uint_as_float(b[4] << 16) * inv, __uint_as_float(b[5] << 16) * inv,
+                                        __uint_as_float(b[6] << 16) * inv, __uint_as_float(b[7] << 16) * inv);
+        if (c < nvec) {
+            uint2 v2;
+            v2.x = lo;
+            v2.y = hi;
+            reinterpret_cast<uint2 *>(row)[c] = v2;
+            if ((lane & 15) == 0) row[a.H + c / 16] = uint8_t(127 + e);
+        }
     }
-    // max over the 16-lane DPP row: rotations by 1, 2, 4 and 8
-    {
-        uint32_t o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x121, 0xF, 0xF, false));  // row_ror:1
-        am = o > am ? o : am;
-        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x122, 0xF, 0xF, false));           // row_ror:2
-        am = o > am ? o : am;
-        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x124, 0xF, 0xF, false));           // row_ror:4
-        am = o > am ? o : am;
-        o = uint32_t(__builtin_amdgcn_update_dpp(0, int(am), 0x128, 0xF, 0xF, false));           // row_ror:8
-        am = o > am ? o : am;
+    if (FP8) {
+        const int G = a.H / 128;
+        const int pad = int(a.prow) - a.H - G;
+        if (seg == 0 && lane < pad) row[a.H + G + lane] = 0;
     }
-    const int e = fp8_group_exponent(am);
-    const float inv = __uint_as_float(uint32_t(127 - e) << 23);              // 2^-e, a normal float
-    const uint32_t lo = e4m3_codes4(__uint_as_float(b[0] << 16) * inv, __uint_as_float(b[1] << 16) * inv,
-                                    __uint_as_float(b[2] << 16) * inv, __uint_as_float(b[3] << 16) * inv);
-    const uint32_t hi = e4m3_codes4(__uint_as_float(b[4] << 16) * inv, __uint_as_float(b[5] << 16) * inv,
-                                    __uint_as_float(b[6] << 16) * inv, __uint_as_float(b[7] << 16) * inv);
-    const int G = a.H / 128;
-    if (c < nvec) {
-        uint2 v2;
-        v2.x = lo;
-        v2.y = hi;
-        reinterpret_cast<uint2 *>(row)[c] = v2;
-        if ((lane & 15) == 0) row[a.H + c / 16] = uint8_t(127 + e);
-    }
-    const int pad = int(a.prow) - a.H - G;
-    if (seg == 0 && lane < pad) row[a.H + G + lane] = 0;
 }
 
-// Stage two of the per-stage combine for source a.s: one wavefront per
-// (token, column segment).  A partition's partial row is added when no later
-// live top-k lane of the token maps to that partition, so partitions are
-// visited in ascending order of their last live lane.  The address of a
-// partial row does not depend on the slot map, so with at most four
-// partitions the rows of every partition are requested together with the
-// token's slots (rows of partitions without a live choice are loaded but
-// never added), and the wavefront waits on memory once.
+// Stage two of the per-stage combine, for every source at once (the round's
+// first collect): one wavefront per (token, column segment).  A partition's
+// partial row is added when no later live top-k lane of the token maps to
+// that partition, so partitions are visited in ascending order of their last
+// live lane.  The address of a partial row does not depend on the slot map,
+// so with at most four partitions the rows of every partition are requested
+// together with the token's slots (rows of partitions without a live choice
+// are loaded but never added), and the wavefront waits on memory once.
 template <bool FP8>
 __device__ __forceinline__ void add_partial(float (&acc)[8], const u32x4 &y, uint32_t sf)
 {
@@ -1738,15 +1757,17 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int t = gw / a.nseg;
-    const int seg = gw - t * a.nseg;
-    if (t >= a.T) return;
-    const int g = a.tok_off[a.s] + t;
+    const int g = gw / a.nseg;
+    const int seg = gw - g * a.nseg;
+    if (g >= a.ntok) return;
+    int t0;
+    const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
+    const int t = g - t0;
     const int nvec = a.nvec;
     const int c = seg * kWave + lane;
     const bool col = c < nvec;
     const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
-    const uint8_t *base = a.partials + (int64_t(a.s) * a.capacity + t) * a.prow;
+    const uint8_t *base = a.partials + (int64_t(s) * a.capacity + t) * a.prow;
     int part = -1;
     if (lane < a.K) {
         const int sx = a.slot[(int64_t(g) * a.K + lane) * 2];
@@ -1814,7 +1835,7 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
         r.y = bf16_rne_bits(acc[2]) | (bf16_rne_bits(acc[3]) << 16);
         r.z = bf16_rne_bits(acc[4]) | (bf16_rne_bits(acc[5]) << 16);
         r.w = bf16_rne_bits(acc[6]) | (bf16_rne_bits(acc[7]) << 16);
-        reinterpret_cast<u32x4 *>(a.out + int64_t(t) * a.H)[c] = r;
+        reinterpret_cast<u32x4 *>(a.outs[s] + int64_t(t) * a.H)[c] = r;
     }
 }
 
@@ -1947,6 +1968,9 @@ int launch_scatter_v(const DispatchArgs &a, int nslots, int E, hipStream_t st)
     hipLaunchKernelGGL(k_scatter<VMAX>, dim3(nslots / TB), dim3(256), lds, st, a);
     return launched_ok();
 }
+
+// 16-byte columns per lane of a stage-one wavefront (two measured slower)
+constexpr int kPartialVpl = 1;
 
 StageArgs make_stage_args(const RoundPlan &p)
 {
@@ -2091,24 +2115,24 @@ int be_launch_combine(const RoundPlan &p, void *stream)
 
 int be_launch_partial(const RoundPlan &p, int f, void *stream)
 {
+    constexpr int VPL = kPartialVpl;
     StageArgs a = make_stage_args(p);
     a.f = f;
     a.reply = static_cast<const uint16_t *>(p.reply[f]);
+    a.nseg = (a.nvec + kWave * VPL - 1) / (kWave * VPL);
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_partial<true>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(k_partial<false>, grid, dim3(256), 0, st, a);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL((k_partial<true, VPL>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_partial<false, VPL>), grid, dim3(256), 0, st, a);
     return launched_ok();
 }
 
-int be_launch_final(const RoundPlan &p, int s, void *stream)
+int be_launch_final(const RoundPlan &p, void *stream)
 {
     StageArgs a = make_stage_args(p);
-    a.s = s;
-    a.T = p.tok_off[s + 1] - p.tok_off[s];
-    a.out = static_cast<uint16_t *>(p.out[s]);
-    const int64_t waves = int64_t(a.T) * a.nseg;
+    for (int s = 0; s < p.N; ++s) a.outs[s] = static_cast<uint16_t *>(p.out[s]);
+    const int64_t waves = int64_t(p.ntok) * a.nseg;
     if (waves == 0) return 0;
     dim3 grid(unsigned((waves + 3) / 4));
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -71,7 +71,9 @@ typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
  *                              (float32 sum in ascending k, one rounding);
  *                              source_collect(s) sums source s's partials in
  *                              float32, partitions ordered by the last live
- *                              top-k lane that maps to them, and rounds once.
+ *                              top-k lane that maps to them, and rounds once
+ *                              (the round's first source_collect runs this
+ *                              stage for every source, in one launch).
  *   AFD_COMBINE_PER_STAGE_FP8  as AFD_COMBINE_PER_STAGE, but each partial
  *                              is carried as E4M3 codes with one
  *                              power-of-two scale per 128 elements: e is the
@@ -308,9 +310,10 @@ afd_status afd_worker_reply(afd_ctx *ctx, int32_t f, const void *reply_bf16, int
  * partition replied.  *result is device BF16 [T, H] in token order with row
  * stride *row_stride elements.
  *   F > 1, AFD_COMBINE_ONCE: the source's out_bf16 (nothing is enqueued).
- *   F > 1, per-stage modes: stage two for source s is enqueued on `stream`
- *          into out_bf16 (every partition's stage one must be complete in
- *          `stream` order); *result is out_bf16.
+ *   F > 1, per-stage modes: the round's first collect enqueues stage two
+ *          for every source on `stream` (every partition's stage one must be
+ *          complete in `stream` order; every source's result is complete in
+ *          that stream's order); *result is out_bf16.
  *   F = 1, view = 1: a read-only view of the source's combine inbox in the
  *          workspace, valid until the next afd_source_dispatch (design page
  *          section 13); nothing is enqueued.
@@ -372,7 +375,7 @@ typedef struct {
     int32_t dispatch_path;     /* afd_dispatch_path */
     int32_t dispatch_kernels;  /* kernels the round's dispatch launched */
     int32_t combine_kernels;   /* kernels its combine launches: 1 (AFD_COMBINE_ONCE
-                                  with tokens), F + sources with tokens (per stage), 0 */
+                                  with tokens), F + 1 (per stage, with tokens), 0 */
     int32_t tokens;            /* tokens over every source */
     int32_t layout_tiles;      /* AFD_PATH_TILED: layout workgroups; else 0 */
     int32_t tile_tokens;       /* AFD_PATH_TILED: token slots per layout tile; else 0 */

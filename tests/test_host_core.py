@@ -555,8 +555,9 @@ def test_hip_failure_leaves_state(lib):
 
 @pytest.mark.parametrize("mode", [1, 2])
 def test_per_stage_round_launches(lib, mode):
-    """Per-stage combine: each reply runs its partition's stage one, each
-    collect its source's stage two; nothing runs at the last reply."""
+    """Per-stage combine: each reply runs its partition's stage one, the
+    round's first collect stage two for every source; nothing runs at the
+    last reply or at the other collects."""
     c = cfg(N=2, F=3, E=6, K=2, H=512, cap=16, combine=mode)
     _, ws_once, _ = query(lib, cfg(N=2, F=3, E=6, K=2, H=512, cap=16), 16)
     x = Ctx(lib, c)
@@ -576,8 +577,8 @@ def test_per_stage_round_launches(lib, mode):
     assert x.reply(1, recs[1]) == 0 and log(lib)[0].startswith("partial f=1")
     st, res, stride = x.collect(1)
     assert st == 0 and res == 0x7100000 and stride == 512
-    assert log(lib) == ["final s=1 T=4 out=0x7100000"]
-    assert x.collect(0)[0] == 0 and log(lib) == ["final s=0 T=5 out=0x7000000"]
+    assert log(lib) == ["final ntok=9 out=0x7000000,0x7100000"]
+    assert x.collect(0)[0] == 0 and log(lib) == []
     # where source s's rows from partition f live
     ptr, rb = ctypes.c_void_p(), ctypes.c_int64()
     for (s_, f_) in [(0, 0), (1, 0), (0, 2), (1, 1)]:
@@ -585,13 +586,21 @@ def test_per_stage_round_launches(lib, mode):
         assert rb.value == prow and ptr.value == base + ((f_ * 2 + s_) * 16) * prow
     assert lib.afd_get_partials(x.ctx, 2, 0, ctypes.byref(ptr), None) == nat.AFD_E_ARG
     assert lib.afd_get_partials(x.ctx, 0, 3, ctypes.byref(ptr), None) == nat.AFD_E_ARG
-    # an empty source runs no stage two
+    # stage two runs once, at the first collect, whichever source it is
     assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 3) == 0
     recs = [x.receive(f)[1] for f in range(3)]
     for f in range(3):
         assert x.reply(f, recs[f]) == 0
     log(lib)
-    assert x.collect(0)[0] == 0 and log(lib) == []
+    assert x.collect(0)[0] == 0 and log(lib) == ["final ntok=3 out=(nil),0x7000000"]
+    assert x.collect(1)[0] == 0 and log(lib) == []
+    # a round without tokens runs none
+    assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 0, out=0) == 0
+    recs = [x.receive(f)[1] for f in range(3)]
+    for f in range(3):
+        assert x.reply(f, recs[f]) == 0
+    log(lib)
+    assert x.collect(1)[0] == 0 and x.collect(0)[0] == 0 and log(lib) == []
     x.destroy()
 
 
