@@ -12,7 +12,9 @@ import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "libafd.so")
-FAKE_LIB_PATH = os.path.join(HERE, "_lib", "libafd_hostfake.so")
+# the host core over the recording backend, for CPU tests; AFD_HOSTFAKE_LIB
+# points them at another build (the sanitizer test's)
+FAKE_LIB_PATH = os.environ.get("AFD_HOSTFAKE_LIB") or os.path.join(HERE, "_lib", "libafd_hostfake.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "afd.h")
 
 AFD_OK, AFD_E_ARG, AFD_E_SHAPE, AFD_E_ORDER, AFD_E_CAPACITY, AFD_E_ROUTE, AFD_E_HIP, AFD_E_TIMEOUT = \

@@ -45,9 +45,15 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib, _serial_lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        _serial_lib = _lib = ctypes.CDLL(_LIB_PATH)
+        # AFD_ORACLE_LIB loads another build of the same source instead (the
+        # sanitizer test's AddressSanitizer/UBSan build); build() never
+        # writes it
+        path = os.environ.get("AFD_ORACLE_LIB")
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(path):
+                build()
+        _serial_lib = _lib = ctypes.CDLL(path)
     return _lib
 
 
