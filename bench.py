@@ -72,26 +72,28 @@ def byte_terms(cfg, L: int) -> dict:
     }
 
 
-def partial_rows(inst) -> int:
-    """Number of (token, partition) pairs with a live choice: the partial rows
-    a per-stage combine writes and reads."""
+def partial_rows(inst) -> list:
+    """Per partition, the number of tokens with a live choice in it: the
+    partial rows that partition's stage one writes."""
     ids = np.concatenate([s.ids for s in inst.sources])
     E_loc = inst.cfg.E // inst.cfg.F
     part = np.where(ids >= 0, ids // E_loc, -1)
-    return int(sum((part == f).any(axis=1).sum() for f in range(inst.cfg.F)))
+    return [int((part == f).any(axis=1).sum()) for f in range(inst.cfg.F)]
 
 
-def round_bytes(cfg, L: int, combine: str = "once", n_partial: int = 0) -> dict:
+def round_bytes(cfg, L: int, combine: str = "once", n_partial=()) -> dict:
     """Algorithmic HBM bytes of one round, split by kernel role.  The
-    per-stage combine also writes and reads one partial row per (token,
-    partition) with a live choice (BF16, or H codes + scale bytes padded to
-    32), and every partition's stage one reads the slot map."""
+    per-stage combine also writes one partial row per (token, partition)
+    with a live choice (BF16, or H codes + scale bytes padded to 32) and
+    reads back those of every partition but the last to reply (replies go
+    in partition order; the last one's partials are added from registers),
+    and each of its F launches reads the slot map."""
     t = byte_terms(cfg, L)
     dispatch = t["x_read"] + t["ids_weights_read"] + t["slot_map_write"] + t["rows_write"] + t["row_weights_write"]
     combine_b = t["replies_read"] + t["slot_map_read"] + t["out_write"]
     if combine != "once":
         prow = 2 * cfg.H if combine == "per_stage" else cfg.H + (cfg.H // 128 + 31) // 32 * 32
-        combine_b += 2 * n_partial * prow + cfg.F * t["slot_map_read"]
+        combine_b += (sum(n_partial) + sum(n_partial[:-1])) * prow + (cfg.F - 1) * t["slot_map_read"]
     return {"dispatch": dispatch, "combine": combine_b, "total": dispatch + combine_b}
 
 
@@ -498,7 +500,7 @@ def dominant_kernel(info, nb, cached, combine):
     kernel (the one-kernel or cached scatter), else the combine; the
     per-stage combine is timed as its whole phase."""
     if combine != "once":
-        return "combine", "k_partial+k_final"
+        return "combine", "k_partial+k_last"
     path = info["dispatch_path"]
     single = {"one_kernel": "k_fused", "cached": "k_scatter_cached", "one_launch": "k_dispatch1"}.get(path)
     if single is not None and nb["dispatch"] >= nb["combine"]:
@@ -512,7 +514,7 @@ def measure_workload(name, args):
     inst = gen.instance_by_name(name)
     cfg = inst.cfg
     L = live_choices(inst)
-    nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else 0)
+    nb = round_bytes(cfg, L, args.combine, partial_rows(inst) if args.combine != "once" else ())
     view = cfg.F == 1
     S = min(MAX_COLD_SETS, max(1, math.ceil(args.cold_bytes / nb["total"])))
     gmax = args.graph_rounds or 64
@@ -536,7 +538,7 @@ def measure_workload(name, args):
     dom, dom_name = dominant_kernel(info, nb, args.cached, args.combine)
     mode = ("_cached" if args.cached else "") + ("" if args.combine == "once" else "_" + args.combine) + \
         ("_one_launch" if info["dispatch_path"] == "one_launch" else "")
-    traffic = load_traffic(dom_name, name, mode, {"k_partial": cfg.F, "k_final": cfg.N})
+    traffic = load_traffic(dom_name, name, mode, {"k_partial": cfg.F - 1, "k_last": 1})
     dom_gbps = nb[dom] / (kern[dom] * 1e-6) / 1e9
     gbps = nb["total"] / (cold_us * 1e-6) / 1e9
     res = {

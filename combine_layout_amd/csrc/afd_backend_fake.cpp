@@ -105,7 +105,7 @@ int be_launch_partial(const RoundPlan &p, int f, void *)
     return g_fail;
 }
 
-int be_launch_final(const RoundPlan &p, void *)
+int be_launch_last(const RoundPlan &p, int f, void *)
 {
     std::string outs;
     for (int s = 0; s < p.N; ++s) {
@@ -113,7 +113,8 @@ int be_launch_final(const RoundPlan &p, void *)
         snprintf(b, sizeof(b), "%s%p", s ? "," : "", p.out[s]);
         outs += b;
     }
-    logf("final ntok=%d out=%s", p.ntok, outs.c_str());
+    logf("last f=%d ntok=%d prow=%lld base=%p out=%s", f, p.ntok, static_cast<long long>(p.prow),
+         static_cast<void *>(p.partials), outs.c_str());
     return g_fail;
 }
 

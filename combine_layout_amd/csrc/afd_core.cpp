@@ -250,7 +250,7 @@ void record_info(afd_ctx *c)
         i.tile_tokens = p.tile;
     }
     if (p.ntok > 0) {
-        i.combine_kernels = p.combine == AFD_COMBINE_ONCE ? 1 : p.F + 1;
+        i.combine_kernels = p.combine == AFD_COMBINE_ONCE ? 1 : p.F;
     }
 }
 
@@ -534,10 +534,13 @@ afd_status afd_worker_reply(afd_ctx *c, int32_t f, const void *reply, int64_t re
     c->plan.reply[f] = reply;
     const bool staged = c->cfg.combine != AFD_COMBINE_ONCE;
     const bool last = c->nreplied + 1 == c->cfg.num_partitions;
-    // per-stage: every reply runs its partition's stage one; once: the last
-    // reply runs the whole combine
+    // per-stage: every reply runs its partition's stage one, the last one
+    // together with stage two for every source; once: the last reply runs
+    // the whole combine
     if (c->plan.ntok > 0 && (staged || last)) {
-        const int rc = staged ? be_launch_partial(c->plan, f, stream) : be_launch_combine(c->plan, stream);
+        const int rc = !staged ? be_launch_combine(c->plan, stream)
+                       : last  ? be_launch_last(c->plan, f, stream)
+                               : be_launch_partial(c->plan, f, stream);
         if (rc != 0) {
             c->plan.reply[f] = nullptr;
             return AFD_E_HIP;
@@ -560,10 +563,6 @@ afd_status afd_source_collect(afd_ctx *c, int32_t s, int32_t view, const void **
     if (c->collected[s]) return AFD_E_ORDER;
     const void *res;
     if (g.num_partitions > 1) {
-        // per-stage: the round's first collect runs stage two for every source
-        if (g.combine != AFD_COMBINE_ONCE && c->ncollected == 0 && c->plan.ntok > 0 &&
-            be_launch_final(c->plan, stream) != 0)
-            return AFD_E_HIP;
         res = c->out_user[s];
     } else if (view) {
         res = inbox_of(c, s);

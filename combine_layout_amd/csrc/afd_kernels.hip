@@ -42,10 +42,10 @@
 //             stores it, or its FP8 form (codes plus one power-of-two scale
 //             byte per 128 elements, found with a 16-lane max), into the
 //             source's partial rows in the workspace.
-//   k_final   per-stage combine, stage two (at the round's first collect, for
-//             every source): adds each token's partials in float32,
-//             partitions in ascending order of their last live top-k lane,
-//             and rounds once to BF16.
+//   k_last    per-stage combine at the round's last reply: that partition's
+//             stage one as in k_partial, then stage two for every source:
+//             adds each token's partials in float32, partitions in ascending
+//             order of their last live top-k lane, and rounds once to BF16.
 //
 // Nothing here uses MFMA: the round is data movement plus one multiply-add
 // per reply element, bound by HBM bandwidth.  Expanded rows are written and
@@ -1580,28 +1580,19 @@ __device__ __forceinline__ int fp8_group_exponent(uint32_t amax_bits)
     return e < -117 ? -117 : e;
 }
 
-// Stage one of the per-stage combine for partition a.f: one wavefront per
-// (token, segment of 64 * VPL 16-byte columns).  A token has about K/F live
-// rows in one partition, so a wavefront takes VPL columns per lane to keep
-// as many row loads in flight as the single-rounding combine does.
+// Stage one of the per-stage combine for partition a.f, one token and one
+// segment of 64 * VPL 16-byte columns: the token's live rows of f (lanes
+// with `mine`) weighted and summed in ascending k in FP32, rounded once and
+// stored as the token's partial row.  ys/sfs return each column group as
+// stored, in the form load_partial reads it back (the FP8 codes with the
+// group's scale byte), so a caller can add the partial without reloading
+// it.  Every lane of the wavefront takes part (the FP8 group maximum is a
+// cross-lane reduction).
 template <bool FP8, int VPL>
-__global__ __launch_bounds__(256) void k_partial(StageArgs a)
+__device__ __forceinline__ void stage_one(const StageArgs &a, int lane, int seg, int2 sl, bool mine, uint8_t *row,
+                                          u32x4 (&ys)[VPL], uint32_t (&sfs)[VPL])
 {
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x & (kWave - 1);
-    const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / a.nseg;
-    const int seg = gw - g * a.nseg;
-    if (g >= a.ntok) return;
-    int2 sl;
-    sl.x = -1;
-    sl.y = 0;
-    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
-    const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
-    if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
-    int t0;
-    const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
-    const int t = g - t0;
     const int nvec = a.nvec;
     const int c0 = seg * kWave * VPL + lane;
     uint64_t raddr = 0;
@@ -1643,7 +1634,6 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
             }
         }
     }
-    uint8_t *row = a.partials + ((int64_t(a.f) * a.N + s) * a.capacity + t) * a.prow;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = c0 + i * kWave;
@@ -1651,14 +1641,14 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
 #pragma unroll
         for (int j = 0; j < 8; ++j) b[j] = bf16_rne_bits(acc[i][j]);
         if (!FP8) {
-            if (c < nvec) {
-                u32x4 r;
-                r.x = b[0] | (b[1] << 16);
-                r.y = b[2] | (b[3] << 16);
-                r.z = b[4] | (b[5] << 16);
-                r.w = b[6] | (b[7] << 16);
-                reinterpret_cast<u32x4 *>(row)[c] = r;
-            }
+            u32x4 r;
+            r.x = b[0] | (b[1] << 16);
+            r.y = b[2] | (b[3] << 16);
+            r.z = b[4] | (b[5] << 16);
+            r.w = b[6] | (b[7] << 16);
+            if (c < nvec) reinterpret_cast<u32x4 *>(row)[c] = r;
+            ys[i] = r;
+            sfs[i] = 0;
             continue;
         }
         // FP8: a group of 128 elements is 16 lanes; amax over the magnitudes
@@ -1693,6 +1683,8 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
             reinterpret_cast<uint2 *>(row)[c] = v2;
             if ((lane & 15) == 0) row[a.H + c / 16] = uint8_t(127 + e);
         }
+        ys[i] = u32x4{lo, hi, 0u, 0u};
+        sfs[i] = uint32_t(127 + e);
     }
     if (FP8) {
         const int G = a.H / 128;
@@ -1701,14 +1693,34 @@ __global__ __launch_bounds__(256) void k_partial(StageArgs a)
     }
 }
 
-// Stage two of the per-stage combine, for every source at once (the round's
-// first collect): one wavefront per (token, column segment).  A partition's
-// partial row is added when no later live top-k lane of the token maps to
-// that partition, so partitions are visited in ascending order of their last
-// live lane.  The address of a partial row does not depend on the slot map,
-// so with at most four partitions the rows of every partition are requested
-// together with the token's slots (rows of partitions without a live choice
-// are loaded but never added), and the wavefront waits on memory once.
+// Stage one of the per-stage combine for partition a.f: one wavefront per
+// (token, segment of 64 * VPL 16-byte columns).  A token has about K/F live
+// rows in one partition, so a wavefront may take VPL columns per lane to
+// keep more row loads in flight.
+template <bool FP8, int VPL>
+__global__ __launch_bounds__(256) void k_partial(StageArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gw = blockIdx.x * 4 + wave_id();
+    const int g = gw / a.nseg;
+    const int seg = gw - g * a.nseg;
+    if (g >= a.ntok) return;
+    int2 sl;
+    sl.x = -1;
+    sl.y = 0;
+    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
+    const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
+    if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
+    int t0;
+    const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
+    const int t = g - t0;
+    uint8_t *row = a.partials + ((int64_t(a.f) * a.N + s) * a.capacity + t) * a.prow;
+    u32x4 ys[VPL];
+    uint32_t sfs[VPL];
+    stage_one<FP8, VPL>(a, lane, seg, sl, mine, row, ys, sfs);
+}
+
+// One partial row segment added into a stage-two accumulator.
 template <bool FP8>
 __device__ __forceinline__ void add_partial(float (&acc)[8], const u32x4 &y, uint32_t sf)
 {
@@ -1751,8 +1763,20 @@ __device__ __forceinline__ void load_partial(const uint8_t *row, int c, int H, u
     }
 }
 
+// The round's last reply: partition a.f's stage one and stage two for every
+// source in one launch, one wavefront per (token, 64-column segment).  The
+// wavefront computes and stores the token's partial of a.f as k_partial
+// does, then adds the token's partials: a partition's partial is added when
+// no later live top-k lane of the token maps to that partition, so
+// partitions are visited in ascending order of their last live lane.  The
+// term of a.f is its partial as stored (for FP8 the decoded codes), taken
+// from registers instead of being read back, so the sum is the same as with
+// every partial reloaded.  A partial row's address does not depend on the
+// slot map: with at most four partitions the other partitions' rows are
+// requested before the reply rows, all in flight together (rows of a
+// partition without a live choice of the token are loaded but never added).
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_final(StageArgs a)
+__global__ __launch_bounds__(256) void k_last(StageArgs a)
 {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & (kWave - 1);
@@ -1760,19 +1784,18 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     const int g = gw / a.nseg;
     const int seg = gw - g * a.nseg;
     if (g >= a.ntok) return;
+    int2 sl;
+    sl.x = -1;
+    sl.y = 0;
+    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
+    const int part = sl.x >= 0 ? (sl.x >> 24) : -1;
     int t0;
     const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
     const int t = g - t0;
-    const int nvec = a.nvec;
     const int c = seg * kWave + lane;
-    const bool col = c < nvec;
+    const bool col = c < a.nvec;
     const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
-    const uint8_t *base = a.partials + (int64_t(s) * a.capacity + t) * a.prow;
-    int part = -1;
-    if (lane < a.K) {
-        const int sx = a.slot[(int64_t(g) * a.K + lane) * 2];
-        part = sx >= 0 ? (sx >> 24) : -1;
-    }
+    uint8_t *base = a.partials + (int64_t(s) * a.capacity + t) * a.prow;
     constexpr int SPEC = 4;
     const bool spec = a.F <= SPEC;
     u32x4 ys[SPEC];
@@ -1781,7 +1804,17 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
     for (int i = 0; i < SPEC; ++i) {
         ys[i] = u32x4{0u, 0u, 0u, 0u};
         sfs[i] = 127u;
-        if (spec && i < a.F && col) load_partial<FP8>(base + i * fstride, c, a.H, ys[i], sfs[i]);
+        if (spec && i < a.F && i != a.f && col) load_partial<FP8>(base + i * fstride, c, a.H, ys[i], sfs[i]);
+    }
+    const bool mine = part == a.f;
+    u32x4 yf = u32x4{0u, 0u, 0u, 0u};
+    uint32_t sff = 127u;
+    if (__ballot(mine) != 0) {
+        u32x4 y1[1];
+        uint32_t s1[1];
+        stage_one<FP8, 1>(a, lane, seg, sl, mine, base + a.f * fstride, y1, s1);
+        yf = y1[0];
+        sff = s1[0];
     }
     bool last = part >= 0;
     for (int j = 0; j < a.K; ++j) {
@@ -1804,11 +1837,12 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
                 y = f == i ? ys[i] : y;
                 sf = f == i ? sfs[i] : sf;
             }
+            y = f == a.f ? yf : y;
+            sf = f == a.f ? sff : sf;
             add_partial<FP8>(acc, y, sf);
         }
     } else {
         while (lm != 0) {
-            // up to four partials per batch, all loads issued before the adds
             u32x4 y[4];
             uint32_t sf[4];
             int n = 0;
@@ -1819,8 +1853,13 @@ __global__ __launch_bounds__(256) void k_final(StageArgs a)
                 if (lm != 0) {
                     const int k = __builtin_ctzll(lm);
                     lm &= lm - 1;
-                    if (col) load_partial<FP8>(base + int64_t(__builtin_amdgcn_readlane(part, k)) * fstride, c, a.H,
-                                               y[i], sf[i]);
+                    const int f = __builtin_amdgcn_readlane(part, k);
+                    if (f == a.f) {
+                        y[i] = yf;
+                        sf[i] = sff;
+                    } else if (col) {
+                        load_partial<FP8>(base + int64_t(f) * fstride, c, a.H, y[i], sf[i]);
+                    }
                     n = i + 1;
                 }
             }
@@ -2128,16 +2167,18 @@ int be_launch_partial(const RoundPlan &p, int f, void *stream)
     return launched_ok();
 }
 
-int be_launch_final(const RoundPlan &p, void *stream)
+int be_launch_last(const RoundPlan &p, int f, void *stream)
 {
     StageArgs a = make_stage_args(p);
+    a.f = f;
+    a.reply = static_cast<const uint16_t *>(p.reply[f]);
     for (int s = 0; s < p.N; ++s) a.outs[s] = static_cast<uint16_t *>(p.out[s]);
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     if (waves == 0) return 0;
     dim3 grid(unsigned((waves + 3) / 4));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_final<true>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(k_final<false>, grid, dim3(256), 0, st, a);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_last<true>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_last<false>, grid, dim3(256), 0, st, a);
     return launched_ok();
 }
 

@@ -168,7 +168,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream);
 int be_read_ends(const RoundPlan &p, void *stream, int32_t *host_ends, uint64_t *err_word);
 int be_launch_combine(const RoundPlan &p, void *stream);
 int be_launch_partial(const RoundPlan &p, int f, void *stream);   // per-stage combine, stage one
-int be_launch_final(const RoundPlan &p, void *stream);            // per-stage combine, stage two (every source)
+int be_launch_last(const RoundPlan &p, int f, void *stream);      // per-stage: the last reply's stage one + stage two
 int be_launch_copy(const void *src, void *dst, int64_t bytes, void *stream);
 int be_read_error(uint64_t *dev_err, void *stream, int clear, uint64_t *word);
 // The one-launch dispatch's gave-up flag (and clears it when asked).

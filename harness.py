@@ -86,9 +86,10 @@ class GpuRound:
 
 
 def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, keep_arrays=True, pad_value=NAN_BF16,
-              outs=None, cached=False):
+              outs=None, cached=False, reply_order=None):
     """One round through the binding; cached=True dispatches without ids,
-    reusing the buffer's last layout."""
+    reusing the buffer's last layout; reply_order lists the partitions in
+    the order they reply (default ascending)."""
     cfg = inst.cfg
     buf = buf or make_buffer(inst)
     dev = dev or upload(inst)
@@ -99,8 +100,8 @@ def run_round(inst, buf=None, dev=None, *, bucket=None, rhc=False, view=False, k
                             cached=cached)
     recs = [buf.worker_receive(f, bucket=bucket, read_host_counts=rhc) for f in range(cfg.F)]
     replies = [identity_replies(cfg, rec, f, pad_value) for f, rec in enumerate(recs)]
-    for f, rec in enumerate(recs):
-        buf.worker_reply(f, replies[f], rec.receipt)
+    for f in (range(cfg.F) if reply_order is None else reply_order):
+        buf.worker_reply(f, replies[f], recs[f].receipt)
     outs_t = [buf.source_collect(s, view=view) for s in range(cfg.N)]
     torch.cuda.synchronize()
     r = read_round(cfg, recs, replies, outs_t, keep_arrays)

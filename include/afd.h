@@ -69,11 +69,12 @@ typedef enum { AFD_BF16 = 0, AFD_FP8_E4M3 = 1 } afd_dtype;
  *                              worker_reply(f) reduces partition f's live
  *                              rows of every token into one BF16 partial
  *                              (float32 sum in ascending k, one rounding);
- *                              source_collect(s) sums source s's partials in
+ *                              stage two sums each token's partials in
  *                              float32, partitions ordered by the last live
  *                              top-k lane that maps to them, and rounds once
- *                              (the round's first source_collect runs this
- *                              stage for every source, in one launch).
+ *                              (on one GPU the round's last worker_reply
+ *                              runs its own stage one and this stage for
+ *                              every source, in one launch).
  *   AFD_COMBINE_PER_STAGE_FP8  as AFD_COMBINE_PER_STAGE, but each partial
  *                              is carried as E4M3 codes with one
  *                              power-of-two scale per 128 elements: e is the
@@ -298,7 +299,10 @@ afd_status afd_worker_receive(afd_ctx *ctx, int32_t f, int32_t bucket, int32_t r
  * read.  AFD_COMBINE_ONCE: the round's last reply enqueues the combine for
  * every source on `stream`; every reply must be complete in `stream` order
  * by then.  Per-stage modes: each reply enqueues partition f's stage one
- * (its partials, from its own reply only) on `stream`.
+ * (its partials, from its own reply only) on `stream`; the round's last
+ * reply enqueues its stage one and stage two for every source as one
+ * launch (every earlier reply's stage one must be complete in `stream`
+ * order by then).
  * Errors: AFD_E_ORDER (not received, already replied, or a receipt of
  * another round or partition), AFD_E_ARG.
  */
@@ -309,11 +313,8 @@ afd_status afd_worker_reply(afd_ctx *ctx, int32_t f, const void *reply_bf16, int
  * afd_source_collect (contract page: source_collect(view)).  Needs every
  * partition replied.  *result is device BF16 [T, H] in token order with row
  * stride *row_stride elements.
- *   F > 1, AFD_COMBINE_ONCE: the source's out_bf16 (nothing is enqueued).
- *   F > 1, per-stage modes: the round's first collect enqueues stage two
- *          for every source on `stream` (every partition's stage one must be
- *          complete in `stream` order; every source's result is complete in
- *          that stream's order); *result is out_bf16.
+ *   F > 1: the source's out_bf16, complete in the order of the stream of
+ *          the round's last reply (nothing is enqueued).
  *   F = 1, view = 1: a read-only view of the source's combine inbox in the
  *          workspace, valid until the next afd_source_dispatch (design page
  *          section 13); nothing is enqueued.
@@ -375,7 +376,7 @@ typedef struct {
     int32_t dispatch_path;     /* afd_dispatch_path */
     int32_t dispatch_kernels;  /* kernels the round's dispatch launched */
     int32_t combine_kernels;   /* kernels its combine launches: 1 (AFD_COMBINE_ONCE
-                                  with tokens), F + 1 (per stage, with tokens), 0 */
+                                  with tokens), F (per stage, with tokens), 0 */
     int32_t tokens;            /* tokens over every source */
     int32_t layout_tiles;      /* AFD_PATH_TILED: layout workgroups; else 0 */
     int32_t tile_tokens;       /* AFD_PATH_TILED: token slots per layout tile; else 0 */

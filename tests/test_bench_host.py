@@ -18,7 +18,7 @@ def test_dominant_kernel_follows_the_reported_path():
     small = {"dispatch": 5, "combine": 9, "total": 14}
     assert bench.dominant_kernel({"dispatch_path": "one_kernel"}, small, False, "once") == ("combine", "k_combine")
     assert bench.dominant_kernel({"dispatch_path": "tiled"}, nb, False, "per_stage") == \
-        ("combine", "k_partial+k_final")
+        ("combine", "k_partial+k_last")
 
 
 def _fake_run(us, hot, disp, comb):

@@ -201,6 +201,28 @@ def test_staged_parity_many_partitions(case, mode):
     check_staged(inst, g, mode)
 
 
+# (seed, F, E, K, T, reply order): the last reply is a low or middle
+# partition, with at most four partitions and with more
+ORDERS = [(0, 2, 16, 8, [300, 41], [1, 0]), (1, 3, 24, 8, [129, 0, 64], [2, 0, 1]),
+          (2, 4, 32, 6, [500], [3, 1, 0, 2]), (3, 6, 48, 12, [77, 90], [5, 0, 4, 1, 3, 2]),
+          (4, 8, 64, 32, [40, 3], [7, 6, 5, 4, 3, 2, 1, 0])]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", ORDERS, ids=lambda c: f"F{c[1]}_last{c[5][-1]}")
+def test_staged_reply_order(case, mode):
+    """Whichever partition replies last runs its stage one together with
+    stage two: partial rows of every partition (the last one's included)
+    and outputs equal the oracle's whatever the order."""
+    h = _gpu()
+    i, F, E, K, T, order = case
+    inst = gen.random_small(1200 + i, N=len(T), F=F, E=E, K=K, alpha=8, T=T, H=1024 if i % 2 else 512,
+                            p_skip=0.1, dtype="fp8" if i % 2 else "bf16", bucket=max(T))
+    print(f"[staged order] F={F} order={order} T={T} {mode}", flush=True)
+    g = h.run_round(inst, h.make_buffer(inst, combine=mode), reply_order=order)
+    check_staged(inst, g, mode)
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_staged_with_invalid_routes(mode):
     """Invalid ids are skipped in both stages: partial rows and outputs equal

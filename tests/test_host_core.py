@@ -556,8 +556,8 @@ def test_hip_failure_leaves_state(lib):
 @pytest.mark.parametrize("mode", [1, 2])
 def test_per_stage_round_launches(lib, mode):
     """Per-stage combine: each reply runs its partition's stage one, the
-    round's first collect stage two for every source; nothing runs at the
-    last reply or at the other collects."""
+    round's last reply (whichever partition it is) its own stage one and
+    stage two for every source in one launch; collects enqueue nothing."""
     c = cfg(N=2, F=3, E=6, K=2, H=512, cap=16, combine=mode)
     _, ws_once, _ = query(lib, cfg(N=2, F=3, E=6, K=2, H=512, cap=16), 16)
     x = Ctx(lib, c)
@@ -574,10 +574,11 @@ def test_per_stage_round_launches(lib, mode):
     assert FAKE_WS < base < FAKE_WS + x.ws
     assert x.reply(0, recs[0]) == 0 and log(lib)[0].startswith("partial f=0")
     assert x.collect(0)[0] == nat.AFD_E_ORDER                    # partition 1 has not replied
-    assert x.reply(1, recs[1]) == 0 and log(lib)[0].startswith("partial f=1")
+    assert x.reply(1, recs[1]) == 0
+    assert log(lib) == [f"last f=1 ntok=9 prow={prow} base={lg[0].split('base=')[1]} out=0x7000000,0x7100000"]
     st, res, stride = x.collect(1)
     assert st == 0 and res == 0x7100000 and stride == 512
-    assert log(lib) == ["final ntok=9 out=0x7000000,0x7100000"]
+    assert log(lib) == []
     assert x.collect(0)[0] == 0 and log(lib) == []
     # where source s's rows from partition f live
     ptr, rb = ctypes.c_void_p(), ctypes.c_int64()
@@ -586,14 +587,16 @@ def test_per_stage_round_launches(lib, mode):
         assert rb.value == prow and ptr.value == base + ((f_ * 2 + s_) * 16) * prow
     assert lib.afd_get_partials(x.ctx, 2, 0, ctypes.byref(ptr), None) == nat.AFD_E_ARG
     assert lib.afd_get_partials(x.ctx, 0, 3, ctypes.byref(ptr), None) == nat.AFD_E_ARG
-    # stage two runs once, at the first collect, whichever source it is
+    # stage two runs once, with the last reply's stage one
     assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 3) == 0
     recs = [x.receive(f)[1] for f in range(3)]
-    for f in range(3):
-        assert x.reply(f, recs[f]) == 0
     log(lib)
-    assert x.collect(0)[0] == 0 and log(lib) == ["final ntok=3 out=(nil),0x7000000"]
-    assert x.collect(1)[0] == 0 and log(lib) == []
+    for f in (1, 2, 0):
+        assert x.reply(f, recs[f]) == 0
+    lg = log(lib)
+    assert [m.split(" ")[:2] for m in lg] == [["partial", "f=1"], ["partial", "f=2"], ["last", "f=0"]]
+    assert lg[2].endswith(" out=(nil),0x7000000")
+    assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0 and log(lib) == []
     # a round without tokens runs none
     assert x.dispatch(0, 0, out=0) == 0 and x.dispatch(1, 0, out=0) == 0
     recs = [x.receive(f)[1] for f in range(3)]
@@ -621,12 +624,14 @@ def test_per_stage_failed_launches_leave_state(lib):
         assert x.reply(0, recs[0]) == nat.AFD_E_HIP               # stage one failed: reply not recorded
     finally:
         lib.afd_fake_set_fail(0)
-    assert x.reply(0, recs[0]) == 0 and x.reply(1, recs[1]) == 0
+    assert x.reply(0, recs[0]) == 0
     lib.afd_fake_set_fail(1)
     try:
-        assert x.collect(0)[0] == nat.AFD_E_HIP                   # stage two failed: not collected
+        assert x.reply(1, recs[1]) == nat.AFD_E_HIP               # stage one + two failed: not recorded
     finally:
         lib.afd_fake_set_fail(0)
+    assert x.collect(0)[0] == nat.AFD_E_ORDER
+    assert x.reply(1, recs[1]) == 0
     assert x.collect(0)[0] == 0 and x.collect(1)[0] == 0
     x.destroy()
 
@@ -711,7 +716,7 @@ def test_round_info_names_the_dispatch_path(lib):
     y = Ctx(lib, cfg(E=8, K=2, cap=16, combine=2))
     y.full_round(T=(4, 0))
     ri = _info(lib, y)
-    assert ri.combine_kernels == 2 + 1                        # two stage-one launches, one stage two
+    assert ri.combine_kernels == 2                            # a stage one, then stage one + stage two
     y.destroy()
 
 
