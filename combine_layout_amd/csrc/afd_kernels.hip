@@ -402,6 +402,40 @@ __device__ __forceinline__ uint32_t classify_token(const int (&ev)[KMAX], int E,
     return live;
 }
 
+// The route check's common case without pairwise compares: at most eight
+// ids per token and E <= 248.  The ids go into two 32-bit words, one byte
+// each, a skipped choice (-1) as byte 248 + k, which equals neither an id
+// nor another skip; two equal ids are then a zero byte in the XOR of a word
+// with a byte rotation of itself or of the other word (eight such XORs
+// cover all 28 pairs).  Returns true, with the live set, when every id is
+// in [-1, E) and no id repeats; otherwise classify_token decides.  As SGPR
+// lane masks the 28 compares form a dependent chain of scalar ORs; here it
+// is about forty independent vector operations.
+template <int KMAX>
+__device__ __forceinline__ bool routes_plain(const int (&ev)[KMAX], int E, uint32_t &live)
+{
+    if (KMAX != 8 || E > 248) return false;
+    // e + 1 is 0 for a skip and in [1, E] for a valid id; anything else
+    // (below -1 or at least E) makes the largest e + 1 exceed E
+    uint32_t w0 = 0, w1 = 0, lv = 0, mx = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const uint32_t e1 = uint32_t(ev[k]) + 1u;
+        mx = e1 > mx ? e1 : mx;
+        lv |= e1 != 0u ? (1u << k) : 0u;
+        const uint32_t b = (e1 != 0u ? e1 - 1u : 248u + uint32_t(k)) << (8 * (k & 3));
+        if (k < 4) w0 |= b;
+        else w1 |= b;
+    }
+    const uint32_t odd = mx > uint32_t(E) ? 1u : 0u;
+    auto rot = [](uint32_t v, int r) { return (v << r) | (v >> (32 - r)); };
+    auto zb = [](uint32_t v) { return (v - 0x01010101u) & ~v & 0x80808080u; };   // nonzero iff a byte is 0
+    const uint32_t z = zb(w0 ^ rot(w0, 8)) | zb(w0 ^ rot(w0, 16)) | zb(w1 ^ rot(w1, 8)) | zb(w1 ^ rot(w1, 16)) |
+                       zb(w0 ^ w1) | zb(w0 ^ rot(w1, 8)) | zb(w0 ^ rot(w1, 16)) | zb(w0 ^ rot(w1, 24));
+    live = lv;
+    return (z | odd) == 0;
+}
+
 // ------------------------------------------------------------- kernels ----
 
 // Dispatch in one kernel for small rounds (at most kFusedMaxTokens tokens,
@@ -503,12 +537,15 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
                 ev[k] = k < K ? val : -1;
             }
         }
-        int ss = 0, tt = 0;
-        if (blockIdx.x == 0) {
-            ss = src_of_lds(s_off, N, gg);
-            tt = gg - s_off[ss];
+        uint32_t live;
+        if (!routes_plain<KMAX>(ev, E, live)) {
+            int ss = 0, tt = 0;
+            if (blockIdx.x == 0) {
+                ss = src_of_lds(s_off, N, gg);
+                tt = gg - s_off[ss];
+            }
+            live = classify_token<KMAX>(ev, E, ss, tt, err);
         }
-        const uint32_t live = classify_token<KMAX>(ev, E, ss, tt, err);
         const int inc = gg < g ? 0x10001 : 1;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
@@ -656,7 +693,8 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     uint32_t live = 0;
     {
         uint64_t err = kNoError;
-        live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);   // token index used only for an error
+        if (!routes_plain<KMAX>(ev, E, live))
+            live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);   // token index used only for an error
         if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // mark the token's lane bit per live expert (others into the spare slot E)
         unsigned long long *mrow = mask + size_t(wave) * (E + 1);
@@ -1012,7 +1050,8 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
         {
             uint64_t err = kNoError;
             const int g = int(tr.z) + tid;
-            const uint32_t live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);
+            uint32_t live;
+            if (!routes_plain<KMAX>(ev, E, live)) live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);
             if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], 1);
@@ -1095,7 +1134,7 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
     uint32_t live;
     {
         uint64_t err_unused = kNoError;
-        live = classify_token<KMAX>(ev, E, 0, 0, err_unused);
+        if (!routes_plain<KMAX>(ev, E, live)) live = classify_token<KMAX>(ev, E, 0, 0, err_unused);
         unsigned long long *mrow = mask + size_t(wave) * (E + 1);
         const unsigned long long bit = 1ull << lane;
 #pragma unroll

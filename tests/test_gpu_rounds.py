@@ -186,6 +186,73 @@ def test_invalid_routes_sticky_first_offender(case):
     assert buf.get_error()[0] == 0
 
 
+def _crafted_ids(ids, E, rng):
+    """Overwrite the first rows of a [T, 8] id array with cases aimed at the
+    route check's compare-free form (at most eight ids, E <= 248, one byte
+    per id, a skip as byte 248 + k): a repeat at each of the 28 position
+    pairs, runs of skips, ids at E - 1 and E, ids whose low byte equals an
+    id or a skip byte, negatives below -1.  Returns the number of rows set."""
+    K = ids.shape[1]
+
+    def distinct():
+        return rng.permutation(E)[:K].astype(np.int32)
+
+    rows = []
+    for i in range(K):
+        for j in range(i + 1, K):
+            r = distinct()
+            r[j] = r[i]
+            rows.append(r)
+    for m in range(1, K + 1):                     # m skips at varying places
+        r = distinct()
+        r[rng.permutation(K)[:m]] = -1
+        rows.append(r)
+    r = distinct()
+    r[3] = E - 1 if E - 1 not in r else r[3]
+    rows.append(r)
+    for bad in (E, 248, 248 + 5, 256 + int(ids[0, 0] % E), 255, -2, -257, 2 ** 31 - 1, -2 ** 31):
+        r = distinct()
+        r[5] = bad
+        r[2] = -1
+        rows.append(r)
+    r = distinct()                                 # two skips and a repeat after them
+    r[0] = r[1] = -1
+    r[7] = r[4]
+    rows.append(r)
+    n = min(len(rows), ids.shape[0])
+    ids[:n] = np.stack(rows[:n])
+    return n
+
+
+# (E, F, tokens, dispatch): E = 248 takes the compare-free check, 249 and 256
+# the pairwise one; small rounds run the one-kernel dispatch, larger ones the
+# layout kernel, and the one-launch dispatch its counting workgroups
+ROUTE_BYTES = [(248, 2, 120, "auto"), (249, 3, 120, "auto"), (8, 2, 90, "auto"), (248, 2, 700, "auto"),
+               (249, 3, 700, "auto"), (256, 4, 700, "auto"), (248, 4, 700, "one_launch")]
+
+
+@pytest.mark.parametrize("case", ROUTE_BYTES, ids=lambda c: f"E{c[0]}-T{c[2]}-{c[3]}")
+def test_route_check_crafted_ids(case):
+    """Both forms of the route check agree with the oracle: the live set of
+    every token (so ends, rows, slots and the combine) and the first
+    offender of the round."""
+    h = _gpu()
+    E, F, T, dispatch = case
+    rng = np.random.default_rng(E * 7 + T)
+    inst = gen.random_small(1300 + E + T, N=1, F=F, E=E, K=8, alpha=4, T=[T], H=256, p_skip=0.0, bucket=T)
+    n = _crafted_ids(inst.sources[0].ids, E, rng)
+    cfg = inst.cfg
+    lay = oracle.layout(cfg.T, inst.sources[0].ids, cfg.E, cfg.F, cfg.K, cfg.alpha)
+    assert lay.err[0] != 0 and n > 40
+    buf = h.make_buffer(inst, dispatch=dispatch)
+    print(f"[route bytes] E={E} T={T} {dispatch}", flush=True)
+    g = h.run_round(inst, buf)
+    want = {"auto": "one_kernel" if T <= 512 else "tiled", "one_launch": "one_launch"}[dispatch]
+    assert buf.round_info()["dispatch_path"] == want
+    assert _check(inst, g, oracle.run_round(inst, rows_cap=g.receive_rows)) == 0
+    assert buf.get_error(clear=True) == lay.err
+
+
 def test_invalid_routes_reported_by_host_count_receive():
     h = _gpu()
     from combine_layout_amd import AfdError
