@@ -382,6 +382,28 @@ def copy_bandwidth(nbytes=1 << 30, reps=20):
     return 2 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
 
 
+def one_way_bandwidth(nbytes, reps=10):
+    """A read-only pass (a sum over int32 words) and a write-only pass (a
+    fill), each `reps` times over `nbytes`: with the copy, the counter
+    calibration's three kernels of known traffic."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    out = []
+    for op in (lambda: a.sum(), lambda: b.fill_(7)):
+        op()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            op()
+        t1.record()
+        torch.cuda.synchronize()
+        out.append(nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9)
+    return out[0], out[1]
+
+
 # ---------------------------------------------------------- CPU baseline ----
 
 def cpu_baseline(inst, budget_s, parallel=False, ref=None):
@@ -706,8 +728,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip launch-floor and copy probes")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (read + write) ten times; used to "
-                         "calibrate the HBM byte counters")
+                    help="only run a plain device copy of MIB MiB (read + write), a read-only sum and a "
+                         "write-only fill of MIB MiB, ten times each; used to calibrate the HBM byte counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -728,7 +750,9 @@ def main(argv=None):
         import torch
         torch.cuda.set_device(0)
         gbps = copy_bandwidth(args.copy_only << 20, reps=10)
-        print(json.dumps({"copy_mib": args.copy_only, "copy_gbps": round(gbps, 1)}), flush=True)
+        read_gbps, write_gbps = one_way_bandwidth(args.copy_only << 20, reps=10)
+        print(json.dumps({"copy_mib": args.copy_only, "copy_gbps": round(gbps, 1), "read_gbps": round(read_gbps, 1),
+                          "write_gbps": round(write_gbps, 1)}), flush=True)
         return 0
     if args.child or args.processes == 0:
         res = measure(names, args)
