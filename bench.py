@@ -13,21 +13,26 @@ workload carries the same figures.  Rounds are captured in HIP graphs and
 replayed.  "cold" rounds rotate over enough independent input/arena/reply
 sets to push every round's bytes through HBM past the on-package cache
 (round i on set i mod S, so a block's rounds use distinct sets); "hot"
-rounds reuse one set.  The timed rounds are split into five blocks; a
-workload's figure is the median block, and the median of that over fresh
-processes (three by default).  `value` is the cold whole-round algorithmic
-throughput:
+rounds reuse one set.  The timed rounds (--steps after --warmup) run in
+graphs of at most 64 rounds, in blocks of at least 64 (one block at 20
+steps, since every graph launch has a fixed device-side cost); beside them
+the five-block figure runs five blocks of 256 rounds and takes the median
+block.  Each figure is the median over fresh processes (three by default).
+`value` is the timed rounds' cold whole-round algorithmic throughput:
 
   per token       : H*b_x (+4*H/128 FP8 scales) read x, 2*H write the output,
                     8*K read ids+weights, 8*K write + 8*K read the slot map
   per live choice : H*b_x (+ scales) write its row, 2*H read its reply,
                     4 write its row weight
 
-Prints one JSON line.
+With the CPU baseline (the default), each workload's results are also
+compared bit for bit with the oracle's (`parity_vs_oracle`, SHA-256 of the
+BF16 outputs).  Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -118,10 +123,18 @@ class RoundSet:
         self.replies = [h.identity_replies(self.cfg, r, f) for f, r in enumerate(recs)]
         for f, r in enumerate(recs):
             self.buf.worker_reply(f, self.replies[f], r.receipt)
-        for s in range(self.cfg.N):
-            self.buf.source_collect(s, view=view)
+        self.results = [self.buf.source_collect(s, view=view) for s in range(self.cfg.N)]
         torch.cuda.synchronize()
         self.cached = cached
+
+    def output_sha256(self):
+        """SHA-256 of the BF16 bits of every source's result in source order
+        (after a synchronisation; every round of a set writes the same)."""
+        import torch
+        h = hashlib.sha256()
+        for r in self.results:
+            h.update(r.contiguous().view(torch.int16).cpu().numpy().tobytes())
+        return h.hexdigest()[:16]
 
     def dispatch_phase(self):
         """Every source dispatch and worker receive of a round (the receive
@@ -473,7 +486,6 @@ def kernel_digest():
     """First 16 hex digits of the SHA-256 of the kernel source's code: the
     text of combine_layout_amd/csrc/afd_kernels.hip with // comments,
     trailing blanks and empty lines removed, so comment edits keep it."""
-    import hashlib
     import re
     src = os.path.join(ROOT, "combine_layout_amd", "csrc", "afd_kernels.hip")
     lines = []
@@ -593,6 +605,8 @@ def measure_workload(name, args):
                      "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": kern[dom]},
         "inputs_sha256": inst.digests(),
     }
+    torch.cuda.synchronize()
+    res["output_sha256"] = sets[0].output_sha256()
     del sets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -663,6 +677,7 @@ def aggregate(runs, names, args):
             "config": first["config"],
             "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
             "inputs_sha256": first["inputs_sha256"],
+            "output_sha256": [r.get("output_sha256") for r in rs],
         }
         if name in GATED and args.combine == "once" and not args.cached:
             budget = nb / (GATE_FRAC * PEAK_HBM_GBPS * 1e9) * 1e6
@@ -799,6 +814,12 @@ def main(argv=None):
         for name in names:
             inst = gen.instance_by_name(name)
             ref = oracle.run_round(inst)
+            # the measured rounds' results against the oracle's, bit for bit
+            want = oracle.run_round(inst, combine_mode=args.combine) if args.combine != "once" else ref
+            want_sha = hashlib.sha256(np.ascontiguousarray(want.out).tobytes()).hexdigest()[:16]
+            got = per[name]["output_sha256"]
+            per[name]["parity_vs_oracle"] = {"oracle_sha256": want_sha,
+                                             "bit_exact": all(g == want_sha for g in got)}
             budget = args.cpu_budget if name == headline else args.cpu_budget_other
             figs = {}
             for par in (False, True):
@@ -817,6 +838,8 @@ def main(argv=None):
                               f"row copy and combine on {th} OpenMP threads, counting and slots serial) on {model}; "
                               f"single-threaded: {n1} rounds, {t1 * 1e3:.3f} ms/round, "
                               f"{nb / t1 / 1e9:.4f} GB/s"}
+        line["parity_vs_oracle"] = {"bit_exact": all(per[n]["parity_vs_oracle"]["bit_exact"] for n in names),
+                                    "workloads": len(names)}
     print(json.dumps(line), flush=True)
     return 0
 
