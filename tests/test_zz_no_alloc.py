@@ -40,13 +40,13 @@ def _same(inst, a, b):
         assert np.array_equal(a.out[s], b.out[s]), f"output of source {s}"
 
 
-def _rounds(base, smaller, view=False):
+def _rounds(base, smaller, view=False, dispatch="auto", path=None):
     h = _gpu()
     from combine_layout_amd import AfdError
     from tests.test_gpu_parity import check_round
     c = base.cfg
-    ref_buf = h.make_buffer(base)
-    st_buf = h.make_buffer(base, static_workspace=True)
+    ref_buf = h.make_buffer(base, dispatch=dispatch)
+    st_buf = h.make_buffer(base, static_workspace=True, dispatch=dispatch)
     try:
         assert st_buf.workspace is None
         with pytest.raises(AfdError):               # one static context per device at a time
@@ -56,6 +56,8 @@ def _rounds(base, smaller, view=False):
             dev = h.upload(inst)
             g_ref = h.run_round(inst, ref_buf, dev, view=view)
             g_st = h.run_round(inst, st_buf, dev, view=view)
+            if path is not None:
+                assert st_buf.round_info()["dispatch_path"] == path
             _same(inst, g_st, g_ref)
             assert check_round(inst, g_st, oracle.run_round(inst, rows_cap=g_st.receive_rows)) == 0
             if view:
@@ -84,3 +86,12 @@ def test_static_context_single_partition_view():
     base = gen.random_small(1400, N=3, F=1, E=12, K=4, alpha=8, T=[600, 0, 333], H=512, p_skip=0.1, bucket=600)
     smaller = gen.generate(dataclasses.replace(base.cfg, T=[20, 5, 0], seed=1401))
     _rounds(base, smaller, view=True)
+
+
+def test_static_context_one_launch_dispatch():
+    """The one-launch dispatch keeps its launch counter and tagged tile
+    counts in the workspace, so on the static scratch as well: two tiled
+    rounds in a row, the second with fewer tiles."""
+    base = gen.instance_by_name("2a2f_skew_h4096")
+    smaller = gen.generate(dataclasses.replace(base.cfg, T=[512, 140], seed=34))
+    _rounds(base, smaller, dispatch="one_launch", path="one_launch")
