@@ -438,6 +438,31 @@ __device__ __forceinline__ bool routes_plain(const int (&ev)[KMAX], int E, uint3
 
 // ------------------------------------------------------------- kernels ----
 
+// Token gg's KMAX ids from the round's id array in LDS (entries past K are
+// -1); one 16-byte read per four ids when K is a multiple of four, since a
+// token's ids are then 16-byte aligned.
+template <int KMAX>
+__device__ __forceinline__ void token_ids_lds(const int *sids, int gg, int K, int (&ev)[KMAX])
+{
+    if ((K & 3) == 0) {
+#pragma unroll
+        for (int q = 0; q < KMAX / 4; ++q) {
+            u32x4 v4 = u32x4{~0u, ~0u, ~0u, ~0u};
+            if (4 * q < K) v4 = reinterpret_cast<const u32x4 *>(sids + gg * K)[q];
+            ev[4 * q] = int(v4.x);
+            ev[4 * q + 1] = int(v4.y);
+            ev[4 * q + 2] = int(v4.z);
+            ev[4 * q + 3] = int(v4.w);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int val = sids[gg * K + (k < K ? k : K - 1)];
+            ev[k] = k < K ? val : -1;
+        }
+    }
+}
+
 // Dispatch in one kernel for small rounds (at most kFusedMaxTokens tokens,
 // kFusedMaxIds ids, kFusedMaxExperts experts).  Block g scatters token g,
 // each thread holding up to VMAX 16-byte columns of the row.  The row, the
@@ -456,7 +481,7 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
     const Hdr h = load_hdr(a);
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
-    __shared__ uint32_t s_live;
+    __shared__ uint32_t s_live, s_slow;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int E = h.E, K = h.K, ntok = h.ntok, G = h.G, N = h.N;
     int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (first: 16-byte aligned)
@@ -513,46 +538,51 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
             for (int q = 0; q <= N; ++q) s_off[q] = a.tok_off[q];
     }
     for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
+    if (tid == 0) s_slow = 0u;
     __syncthreads();
 
     // 2. route check and the two histograms (choices that are not live
-    // count into the spare slot at index E)
-    uint64_t err = kNoError;
-    for (int gg = tid; gg < ntok; gg += 256) {
+    // count into the spare slot at index E).  Tokens that pass the
+    // compare-free check count at once; the others (repeats, invalid ids,
+    // E > 248) are counted in a second pass that only a block holding such
+    // a token runs, so the common round carries none of its code.
+    uint32_t failed = 0;             // bit i: this thread's i-th token needs the second pass
+    for (int gg = tid, i = 0; gg < ntok; gg += 256, ++i) {
         int ev[KMAX];
-        if ((K & 3) == 0) {         // a token's ids are then 16-byte aligned in LDS
-#pragma unroll
-            for (int q = 0; q < KMAX / 4; ++q) {
-                u32x4 v4 = u32x4{~0u, ~0u, ~0u, ~0u};
-                if (4 * q < K) v4 = reinterpret_cast<const u32x4 *>(sids + gg * K)[q];
-                ev[4 * q] = int(v4.x);
-                ev[4 * q + 1] = int(v4.y);
-                ev[4 * q + 2] = int(v4.z);
-                ev[4 * q + 3] = int(v4.w);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                const int val = sids[gg * K + (k < K ? k : K - 1)];
-                ev[k] = k < K ? val : -1;
-            }
-        }
+        token_ids_lds<KMAX>(sids, gg, K, ev);
         uint32_t live;
-        if (!routes_plain<KMAX>(ev, E, live)) {
+        if (routes_plain<KMAX>(ev, E, live)) {
+            const int inc = gg < g ? 0x10001 : 1;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
+            if (gg == g) s_live = live;
+        } else {
+            failed |= 1u << i;
+        }
+    }
+    if (failed != 0) s_slow = 1u;
+    lds_barrier();
+    if (s_slow != 0u) {
+        uint64_t err = kNoError;
+        for (int gg = tid, i = 0; gg < ntok; gg += 256, ++i) {
+            if (((failed >> i) & 1u) == 0u) continue;
+            int ev[KMAX];
+            token_ids_lds<KMAX>(sids, gg, K, ev);
             int ss = 0, tt = 0;
             if (blockIdx.x == 0) {
                 ss = src_of_lds(s_off, N, gg);
                 tt = gg - s_off[ss];
             }
-            live = classify_token<KMAX>(ev, E, ss, tt, err);
-        }
-        const int inc = gg < g ? 0x10001 : 1;
+            const uint32_t live = classify_token<KMAX>(ev, E, ss, tt, err);
+            const int inc = gg < g ? 0x10001 : 1;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
-        if (gg == g) s_live = live;
+            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
+            if (gg == g) s_live = live;
+        }
+        if (blockIdx.x == 0 && err != kNoError)
+            __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lds_barrier();
     }
-    if (blockIdx.x == 0 && err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
     // partitions); expert e starts at pfx[e] - pfx[first expert of its part].
