@@ -46,6 +46,13 @@
 //             stage one as in k_partial, then stage two for every source:
 //             adds each token's partials in float32, partitions in ascending
 //             order of their last live top-k lane, and rounds once to BF16.
+//   k_dispatch1  the dispatch as one launch (AFD_DISPATCH_ONE_LAUNCH): the
+//             first 32 workgroups count one tile each and publish tagged
+//             counts; every other workgroup ranks its own tokens, waits (a
+//             bounded poll) for the counts of this launch, and scatters as
+//             k_scatter does (design page, section 16: counts first, then
+//             the expansion).
+//   k_zero_ends, k_init_ws  a round without tokens; a fresh static workspace.
 //
 // Nothing here uses MFMA: the round is data movement plus one multiply-add
 // per reply element, bound by HBM bandwidth.  Expanded rows are written and
