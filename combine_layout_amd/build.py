@@ -23,6 +23,9 @@ HIP_FLAGS = [
     "-ffp-contract=off",
     # no packed-FP32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel-argument preloading: a kernel's leading scalar arguments (up to
+    # nine, as many as the user SGPRs hold) arrive in SGPRs at wave launch
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     "-Wall", "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

@@ -481,49 +481,30 @@ __device__ __forceinline__ void token_ids_lds(const int *sids, int gg, int K, in
 // a token holds an expert at most once):
 //   row(g, e) = start_e + #{live choices of e in tokens before g}.
 // Both are kept in one LDS word per expert (all tokens in the low 16 bits,
-// earlier tokens in the high 16), so each choice costs one atomic.
-template <int VMAX, int KMAX>
-__global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
+// earlier tokens in the high 16), so each choice costs one atomic.  The
+// leading scalar arguments (the first two sources' rows, ids and token
+// counts, K and nvec) are preloaded into SGPRs by the hardware; rounds of at
+// most two sources (FEW) address the row and the ids from them alone.
+template <int VMAX, int KMAX, bool FEW>
+__global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t *px1, const int32_t *pids0,
+                                               const int32_t *pids1, int pT0, int pT1, int pK, int pnvec,
+                                               DispatchArgs a)
 {
-    const Hdr h = load_hdr(a);
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ uint32_t s_live, s_slow;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
-    const int E = h.E, K = h.K, ntok = h.ntok, G = h.G, N = h.N;
     int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (first: 16-byte aligned)
-    int *hist = sids + ntok * K;                // [E + 1] per expert (+ spare): all | before << 16
-    int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
-
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
-    const bool mine = g < ntok;
-    int t0;
-    const int s = source_of(load_offsets(a.tok_off), h.N, mine ? g : 0, t0);
-    const SourceRec src = load_source(a, s);
-    const int t = g - t0;
 
-    // 1. request every load: row, weights, scales, all ids
-    u32x4 v[VMAX];
-    if (mine) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
-#pragma unroll
-        for (int i = 0; i < VMAX; ++i) {
-            const int c = tid + i * 256;
-            if (c < h.nvec) v[i] = xs[c];
-        }
-    }
-    float wk = 0.0f;
-    if (mine && tid < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + tid];
-    float scv = 0.0f;
-    const bool myscale = mine && h.fp8 && tid < G;
-    if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
-    for (int q = 0; q < N; ++q) {
-        const SourceRec rq = load_source(a, q);
-        const int lo = rq.off * K;
-        const int n = rq.T * K;
-        const gptr<const int32_t> src = (gptr<const int32_t>)rq.ids;
-        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(rq.ids) & 15u) == 0) {
+    // 1. request every load: row, weights, scales, all ids.  With at most
+    // two sources (FEW) the row and the ids are addressed from the preloaded
+    // arguments alone, so they are requested before any load from the
+    // argument block returns.
+    auto ids_to_lds = [&](const int32_t *qids, int lo, int n, int K) {
+        const gptr<const int32_t> src = (gptr<const int32_t>)qids;
+        if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(qids) & 15u) == 0) {
             // 16 bytes per lane: a wavefront moves 256 ids per instruction
             for (int base = wave * 4 * kWave; base < n; base += 16 * kWave)
                 if (base + 4 * lane < n)
@@ -534,6 +515,48 @@ __global__ __launch_bounds__(256) void k_fused(DispatchArgs a)
                 if (base + lane < n)
                     __builtin_amdgcn_global_load_lds((gptr<void>)(src + base + lane), (lptr<void>)(sids + lo + base), 4,
                                                      0, 0);
+        }
+    };
+    auto row_loads = [&](u32x4 (&v)[VMAX], const uint8_t *xrow, int nvec) {
+        const gptr<const u32x4> xs = (gptr<const u32x4>)xrow;
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i) {
+            const int c = tid + i * 256;
+            if (c < nvec) v[i] = xs[c];
+        }
+    };
+    u32x4 v[VMAX];
+    int s, t0;
+    bool mine;
+    if constexpr (FEW) {
+        mine = g < pT0 + pT1;
+        s = g < pT0 ? 0 : 1;
+        t0 = s ? pT0 : 0;
+        if (mine) row_loads(v, (s ? px1 : px0) + int64_t(g - t0) * pnvec * 16, pnvec);
+        ids_to_lds(pids0, 0, pT0 * pK, pK);
+        if (pT1 > 0) ids_to_lds(pids1, pT0 * pK, pT1 * pK, pK);
+    }
+    const Hdr h = load_hdr(a);
+    const int E = h.E, K = h.K, ntok = h.ntok, G = h.G, N = h.N;
+    int *hist = sids + ntok * K;                // [E + 1] per expert (+ spare): all | before << 16
+    int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
+    if constexpr (!FEW) {
+        mine = g < ntok;
+        s = source_of(load_offsets(a.tok_off), N, mine ? g : 0, t0);
+        const SourceRec sx = load_source(a, s);
+        if (mine) row_loads(v, sx.x + int64_t(g - t0) * h.row_bytes, h.nvec);
+    }
+    const SourceRec src = load_source(a, s);
+    const int t = g - t0;
+    float wk = 0.0f;
+    if (mine && tid < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + tid];
+    float scv = 0.0f;
+    const bool myscale = mine && h.fp8 && tid < G;
+    if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
+    if constexpr (!FEW) {
+        for (int q = 0; q < N; ++q) {
+            const SourceRec rq = load_source(a, q);
+            ids_to_lds(rq.ids, rq.off * K, rq.T * K, K);
         }
     }
     // pointer tables, one per wavefront (lane 0)
@@ -1506,27 +1529,30 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 
 // Combine: one wavefront per (token, segment of 64*VPL 16-byte columns).
 // The token's slots arrive as wave-uniform values, one 64-byte scalar load
-// per eight choices (the slot map does not change during the kernel).  With
-// at most NB = 2 or 4 partitions each choice's reply base is selected from
-// the ones that came with the scalars, so the chain before the row loads is
-// two scalar round trips: arguments, slots (the two-way select is the
+// per eight choices (the slot map does not change during the kernel).  The
+// slot map's address, the sizes and the first two reply bases are leading
+// scalar arguments, which the hardware preloads into SGPRs, so the slot
+// load is the first memory request.  With at most NB = 2 or 4 partitions
+// each choice's reply base is selected from those (the third and fourth
+// from the argument block, loaded alongside the slots), so the only round
+// trip before the row loads is the slots' (the two-way select is the
 // cheaper one, which shows at decode).  With more partitions (NB = 0) the
 // bases are looked up in the kernel arguments by partition number, all
-// eight requested before one wait (a third round trip).  The token offsets are read only for
-// the output address.  The wavefront then issues every live row's loads
-// before it accumulates, in ascending k, with a float32 multiply and a
-// separate add.
+// eight requested before one wait.  The token offsets are read only for the
+// output address.  The wavefront then issues every live row's loads before
+// it accumulates, in ascending k, with a float32 multiply and a separate
+// add.
 template <int VPL, int NB>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
+__global__ __launch_bounds__(256) void k_combine(const int32_t *slot, int ntok, int K, int H, int nseg, uint64_t rb0,
+                                                 uint64_t rb1, CombineArgs a)
 {
 #pragma clang fp contract(off)
     static_assert(offsetof(CombineArgs, reply4) == 32 && offsetof(CombineArgs, tok_off) == 64,
                   "scalars and four bases in the first 64 bytes, offsets at byte 64");
     const u32x16 hv = *reinterpret_cast<const u32x16 *>(&a);
-    const int32_t *slot = reinterpret_cast<const int32_t *>((uint64_t(hv[1]) << 32) | uint64_t(hv[0]));
-    const int N = int(hv[2]), ntok = int(hv[3]), K = int(hv[4]), H = int(hv[5]), nvec = int(hv[6]), nseg = int(hv[7]);
+    const int N = int(hv[2]), nvec = H >> 3;
     auto base4 = [&](uint32_t q) { return (uint64_t(hv[9 + 2 * q]) << 32) | uint64_t(hv[8 + 2 * q]); };
-    const uint64_t rb0 = base4(0), rb1 = base4(1), rb2 = base4(2), rb3 = base4(3);
+    const uint64_t rb2 = base4(2), rb3 = base4(3);
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
     const int g = gw / nseg;
@@ -2043,11 +2069,49 @@ int vmax_for(int nvec)
 
 int launched_ok() { return hipGetLastError() == hipSuccess ? 0 : 1; }
 
+// The first two sources of a round as leading scalar kernel arguments.  The
+// library is built with kernel-argument preloading, so the hardware places
+// a kernel's leading scalar arguments in SGPRs before its waves start; for
+// rounds of at most two sources the one-kernel dispatch addresses its first
+// loads (the row and every id) from these alone, with no fetch from the
+// argument block in front of them.
+struct FirstSources {
+    bool two = false;          // the round has at most two sources
+    const uint8_t *x0 = nullptr, *x1 = nullptr;
+    const int32_t *ids0 = nullptr, *ids1 = nullptr;
+    int T0 = 0, T1 = 0;
+};
+
+FirstSources first_sources(const DispatchArgs &a)
+{
+    FirstSources f;
+    f.two = a.h.N <= 2;
+    f.x0 = a.src[0].x;
+    f.ids0 = a.src[0].ids;
+    f.T0 = a.src[0].T;
+    if (a.h.N >= 2) {
+        f.x1 = a.src[1].x;
+        f.ids1 = a.src[1].ids;
+        f.T1 = a.src[1].T;
+    }
+    return f;
+}
+
 template <int VMAX>
 int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipStream_t st)
 {
-    if (k32) hipLaunchKernelGGL((k_fused<VMAX, 32>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((k_fused<VMAX, 8>), grid, dim3(256), lds, st, a);
+    const FirstSources f = first_sources(a);
+#define AFD_FUSED(KM, FW)                                                                                          \
+    hipLaunchKernelGGL((k_fused<VMAX, KM, FW>), grid, dim3(256), lds, st, f.x0, f.x1, f.ids0, f.ids1, f.T0, f.T1,     \
+                       a.h.K, a.h.nvec, a)
+    if (k32) {
+        if (f.two) AFD_FUSED(32, true);
+        else AFD_FUSED(32, false);
+    } else {
+        if (f.two) AFD_FUSED(8, true);
+        else AFD_FUSED(8, false);
+    }
+#undef AFD_FUSED
     return launched_ok();
 }
 
@@ -2222,9 +2286,12 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     a.nseg = (a.nvec + kWave - 1) / kWave;
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
-    if (p.F <= 2) hipLaunchKernelGGL((k_combine<1, 2>), grid, dim3(256), 0, st, a);
-    else if (p.F <= 4) hipLaunchKernelGGL((k_combine<1, 4>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_combine<1, 0>), grid, dim3(256), 0, st, a);
+    const uint64_t rb0 = reinterpret_cast<uint64_t>(a.reply4[0]), rb1 = reinterpret_cast<uint64_t>(a.reply4[1]);
+#define AFD_COMBINE(NB) hipLaunchKernelGGL((k_combine<1, NB>), grid, dim3(256), 0, st, a.slot, a.ntok, a.K, a.H, a.nseg, rb0, rb1, a)
+    if (p.F <= 2) AFD_COMBINE(2);
+    else if (p.F <= 4) AFD_COMBINE(4);
+    else AFD_COMBINE(0);
+#undef AFD_COMBINE
     return launched_ok();
 }
 
