@@ -1401,45 +1401,62 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
 // (column i * LPT + lane of its token); longer rows loop over chunks.  Every
 // wavefront of a token reads the token's K slots itself (no hand-off between
 // wavefronts); the token's first wavefront also writes the new weights into
-// the slot map and the row weights.
-template <int VMAX>
-__global__ __launch_bounds__(256) void k_scatter_cached(DispatchArgs a, int lpt)
+// the slot map and the row weights.  The leading scalar arguments (lanes
+// per token, the slot map's address, the first two sources' rows, their
+// token counts as T0 | T1 << 16, and K | nvec << 8) are preloaded into SGPRs
+// by the hardware; rounds of at most two sources (FEW) address the row and
+// the slots from them alone, ahead of any load from the argument block.
+template <int VMAX, bool FEW>
+__global__ __launch_bounds__(256) void k_scatter_cached(int lpt, const int32_t *pslot, const uint8_t *px0,
+                                                        const uint8_t *px1, int pT01, int pKnv, DispatchArgs a)
 {
-    u32x16 r0, r1;
-    const Hdr h = load_hdr(a, r0, r1);
-    const u32x16 to = load_offsets(a.tok_off);
-    // both header halves, the offsets and lpt in one batch of scalar loads
-    // (left alone, the compiler requests each where it is first used and
-    // waits for it there: three dependent round trips before the record)
-    asm volatile("" ::"s"(r0), "s"(r1), "s"(to), "s"(lpt));
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
     const int wpt = lpt / kWave;                          // wavefronts per token
     const int g = blockIdx.x * (256 / lpt) + wave / wpt;
     const int tl = (wave % wpt) * kWave + lane;           // lane within the token
-    const bool have = g < h.ntok;
-    const int K = h.K, nvec = h.nvec;
-    int t0;
-    const int s = source_of(to, h.N, have ? g : 0, t0);
-    const SourceRec src = load_source(a, s);
-    const int t = (have ? g : 0) - t0;
     u32x4 v[VMAX];
     i32x2 sl;
     sl.x = -1;
     sl.y = 0;
-    float wk = 0.0f;
-    float scv = 0.0f;                                     // FP8: scale of block `lane` (first wavefront)
-    if (have) {
-        const gptr<const u32x4> xs = (gptr<const u32x4>)(src.x + int64_t(t) * h.row_bytes);
+    auto row_and_slots = [&](const uint8_t *x, int t, int K, int nvec) {
+        const gptr<const u32x4> xs = (gptr<const u32x4>)(x + int64_t(t) * nvec * 16);
 #pragma unroll
         for (int i = 0; i < VMAX; ++i) {
             const int c = i * lpt + tl;
             v[i] = xs[c < nvec ? c : 0];
         }
-        if (lane < K) {
-            sl = ((gptr<const i32x2>)h.slot)[int64_t(g) * K + lane];
-            wk = ((gptr<const float>)src.w)[int64_t(t) * K + lane];
-        }
+        if (lane < K) sl = ((gptr<const i32x2>)pslot)[int64_t(g) * K + lane];
+    };
+    int s = 0, t0 = 0;
+    bool have = false;
+    if constexpr (FEW) {
+        const int T0 = pT01 & 0xFFFF, T1 = pT01 >> 16;
+        have = g < T0 + T1;
+        s = g < T0 ? 0 : 1;
+        t0 = s ? T0 : 0;
+        if (have) row_and_slots(s ? px1 : px0, g - t0, pKnv & 0xFF, pKnv >> 8);
+    }
+    u32x16 r0, r1;
+    const Hdr h = load_hdr(a, r0, r1);
+    const int K = h.K, nvec = h.nvec;
+    if constexpr (!FEW) {
+        const u32x16 to = load_offsets(a.tok_off);
+        // both header halves, the offsets and lpt in one batch of scalar loads
+        // (left alone, the compiler requests each where it is first used and
+        // waits for it there: three dependent round trips before the record)
+        asm volatile("" ::"s"(r0), "s"(r1), "s"(to), "s"(lpt));
+        have = g < h.ntok;
+        s = source_of(to, h.N, have ? g : 0, t0);
+        const SourceRec rx = load_source(a, s);
+        if (have) row_and_slots(rx.x, g - t0, K, nvec);
+    }
+    const SourceRec src = load_source(a, s);
+    const int t = (have ? g : 0) - t0;
+    float wk = 0.0f;
+    float scv = 0.0f;                                     // FP8: scale of block `lane` (first wavefront)
+    if (have) {
+        if (lane < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + lane];
         if (h.fp8 && tl < kWave && tl < h.G) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tl) * src.ssg];
     }
     if (lane == 0) {
@@ -2133,7 +2150,18 @@ template <int VMAX>
 int launch_cached_v(const DispatchArgs &a, int lpt, hipStream_t st)
 {
     const int tpb = 256 / lpt;
-    hipLaunchKernelGGL(k_scatter_cached<VMAX>, dim3((a.h.ntok + tpb - 1) / tpb), dim3(256), 0, st, a, lpt);
+    const dim3 grid((a.h.ntok + tpb - 1) / tpb);
+    const int T1 = a.h.N >= 2 ? a.src[1].T : 0;
+    const bool few = a.h.N <= 2 && a.src[0].T <= 0xFFFF && T1 <= 0x7FFF && a.h.nvec <= 0x7FFFFF;
+    const int T01 = few ? a.src[0].T | (T1 << 16) : 0;
+    const int Knv = a.h.K | ((a.h.nvec & 0x7FFFFF) << 8);
+    const uint8_t *x1 = a.h.N >= 2 ? a.src[1].x : nullptr;
+    if (few)
+        hipLaunchKernelGGL((k_scatter_cached<VMAX, true>), grid, dim3(256), 0, st, lpt, a.h.slot, a.src[0].x, x1, T01,
+                           Knv, a);
+    else
+        hipLaunchKernelGGL((k_scatter_cached<VMAX, false>), grid, dim3(256), 0, st, lpt, a.h.slot, a.src[0].x, x1, T01,
+                           Knv, a);
     return launched_ok();
 }
 
