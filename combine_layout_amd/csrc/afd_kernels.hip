@@ -1699,7 +1699,7 @@ __device__ __forceinline__ int fp8_group_exponent(uint32_t amax_bits)
     return e < -117 ? -117 : e;
 }
 
-// Stage one of the per-stage combine for partition a.f, one token and one
+// Stage one of the per-stage combine for partition f, one token and one
 // segment of 64 * VPL 16-byte columns: the token's live rows of f (lanes
 // with `mine`) weighted and summed in ascending k in FP32, rounded once and
 // stored as the token's partial row.  ys/sfs return each column group as
@@ -1708,21 +1708,21 @@ __device__ __forceinline__ int fp8_group_exponent(uint32_t amax_bits)
 // it.  Every lane of the wavefront takes part (the FP8 group maximum is a
 // cross-lane reduction).
 template <bool FP8, int VPL>
-__device__ __forceinline__ void stage_one(const StageArgs &a, int lane, int seg, int2 sl, bool mine, uint8_t *row,
-                                          u32x4 (&ys)[VPL], uint32_t (&sfs)[VPL])
+__device__ __forceinline__ void stage_one(const uint16_t *reply, int H, int K, int64_t prow, int lane, int seg, int2 sl,
+                                          bool mine, uint8_t *row, u32x4 (&ys)[VPL], uint32_t (&sfs)[VPL])
 {
 #pragma clang fp contract(off)
-    const int nvec = a.nvec;
+    const int nvec = H >> 3;
     const int c0 = seg * kWave * VPL + lane;
     uint64_t raddr = 0;
-    if (mine) raddr = reinterpret_cast<uint64_t>(a.reply) + uint64_t(sl.x & 0xFFFFFF) * uint64_t(a.H) * 2u;
+    if (mine) raddr = reinterpret_cast<uint64_t>(reply) + uint64_t(sl.x & 0xFFFFFF) * uint64_t(H) * 2u;
     const int rlo = int(uint32_t(raddr)), rhi = int(uint32_t(raddr >> 32));
     float acc[VPL][8];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
-    for (int k0 = 0; k0 < a.K; k0 += 8) {
+    for (int k0 = 0; k0 < K; k0 += 8) {
         u32x4 y[8][VPL];
         uint64_t rk[8];
 #pragma unroll
@@ -1800,43 +1800,46 @@ __device__ __forceinline__ void stage_one(const StageArgs &a, int lane, int seg,
             v2.x = lo;
             v2.y = hi;
             reinterpret_cast<uint2 *>(row)[c] = v2;
-            if ((lane & 15) == 0) row[a.H + c / 16] = uint8_t(127 + e);
+            if ((lane & 15) == 0) row[H + c / 16] = uint8_t(127 + e);
         }
         ys[i] = u32x4{lo, hi, 0u, 0u};
         sfs[i] = uint32_t(127 + e);
     }
     if (FP8) {
-        const int G = a.H / 128;
-        const int pad = int(a.prow) - a.H - G;
-        if (seg == 0 && lane < pad) row[a.H + G + lane] = 0;
+        const int G = H / 128;
+        const int pad = int(prow) - H - G;
+        if (seg == 0 && lane < pad) row[H + G + lane] = 0;
     }
 }
 
-// Stage one of the per-stage combine for partition a.f: one wavefront per
+// Stage one of the per-stage combine for partition f: one wavefront per
 // (token, segment of 64 * VPL 16-byte columns).  A token has about K/F live
 // rows in one partition, so a wavefront may take VPL columns per lane to
-// keep more row loads in flight.
+// keep more row loads in flight.  The slot map's and the reply's addresses,
+// K, H, the segment count, the token count and f are leading scalar
+// arguments, preloaded into SGPRs, so the slot load is the first request.
 template <bool FP8, int VPL>
-__global__ __launch_bounds__(256) void k_partial(StageArgs a)
+__global__ __launch_bounds__(256) void k_partial(const int32_t *pslot, const uint16_t *preply, int pK, int pH,
+                                                 int pnseg, int pntok, int pf, StageArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / a.nseg;
-    const int seg = gw - g * a.nseg;
-    if (g >= a.ntok) return;
+    const int g = gw / pnseg;
+    const int seg = gw - g * pnseg;
+    if (g >= pntok) return;
     int2 sl;
     sl.x = -1;
     sl.y = 0;
-    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
-    const bool mine = sl.x >= 0 && (sl.x >> 24) == a.f;
+    if (lane < pK) sl = reinterpret_cast<const int2 *>(pslot)[int64_t(g) * pK + lane];
+    const bool mine = sl.x >= 0 && (sl.x >> 24) == pf;
     if (__ballot(mine) == 0) return;                 // no live choice of g in f: no partial
     int t0;
     const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
     const int t = g - t0;
-    uint8_t *row = a.partials + ((int64_t(a.f) * a.N + s) * a.capacity + t) * a.prow;
+    uint8_t *row = a.partials + ((int64_t(pf) * a.N + s) * a.capacity + t) * a.prow;
     u32x4 ys[VPL];
     uint32_t sfs[VPL];
-    stage_one<FP8, VPL>(a, lane, seg, sl, mine, row, ys, sfs);
+    stage_one<FP8, VPL>(preply, pH, pK, a.prow, lane, seg, sl, mine, row, ys, sfs);
 }
 
 // One partial row segment added into a stage-two accumulator.
@@ -1882,37 +1885,38 @@ __device__ __forceinline__ void load_partial(const uint8_t *row, int c, int H, u
     }
 }
 
-// The round's last reply: partition a.f's stage one and stage two for every
+// The round's last reply: partition f's stage one and stage two for every
 // source in one launch, one wavefront per (token, 64-column segment).  The
-// wavefront computes and stores the token's partial of a.f as k_partial
+// wavefront computes and stores the token's partial of f as k_partial
 // does, then adds the token's partials: a partition's partial is added when
 // no later live top-k lane of the token maps to that partition, so
 // partitions are visited in ascending order of their last live lane.  The
-// term of a.f is its partial as stored (for FP8 the decoded codes), taken
+// term of f is its partial as stored (for FP8 the decoded codes), taken
 // from registers instead of being read back, so the sum is the same as with
 // every partial reloaded.  A partial row's address does not depend on the
 // slot map: with at most four partitions the other partitions' rows are
 // requested before the reply rows, all in flight together (rows of a
 // partition without a live choice of the token are loaded but never added).
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_last(StageArgs a)
+__global__ __launch_bounds__(256) void k_last(const int32_t *pslot, const uint16_t *preply, int pK, int pH, int pnseg,
+                                              int pntok, int pf, StageArgs a)
 {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / a.nseg;
-    const int seg = gw - g * a.nseg;
-    if (g >= a.ntok) return;
+    const int g = gw / pnseg;
+    const int seg = gw - g * pnseg;
+    if (g >= pntok) return;
     int2 sl;
     sl.x = -1;
     sl.y = 0;
-    if (lane < a.K) sl = reinterpret_cast<const int2 *>(a.slot)[int64_t(g) * a.K + lane];
+    if (lane < pK) sl = reinterpret_cast<const int2 *>(pslot)[int64_t(g) * pK + lane];
     const int part = sl.x >= 0 ? (sl.x >> 24) : -1;
     int t0;
     const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
     const int t = g - t0;
     const int c = seg * kWave + lane;
-    const bool col = c < a.nvec;
+    const bool col = c < (pH >> 3);
     const int64_t fstride = int64_t(a.N) * a.capacity * a.prow;
     uint8_t *base = a.partials + (int64_t(s) * a.capacity + t) * a.prow;
     constexpr int SPEC = 4;
@@ -1923,20 +1927,20 @@ __global__ __launch_bounds__(256) void k_last(StageArgs a)
     for (int i = 0; i < SPEC; ++i) {
         ys[i] = u32x4{0u, 0u, 0u, 0u};
         sfs[i] = 127u;
-        if (spec && i < a.F && i != a.f && col) load_partial<FP8>(base + i * fstride, c, a.H, ys[i], sfs[i]);
+        if (spec && i < a.F && i != pf && col) load_partial<FP8>(base + i * fstride, c, pH, ys[i], sfs[i]);
     }
-    const bool mine = part == a.f;
+    const bool mine = part == pf;
     u32x4 yf = u32x4{0u, 0u, 0u, 0u};
     uint32_t sff = 127u;
     if (__ballot(mine) != 0) {
         u32x4 y1[1];
         uint32_t s1[1];
-        stage_one<FP8, 1>(a, lane, seg, sl, mine, base + a.f * fstride, y1, s1);
+        stage_one<FP8, 1>(preply, pH, pK, a.prow, lane, seg, sl, mine, base + pf * fstride, y1, s1);
         yf = y1[0];
         sff = s1[0];
     }
     bool last = part >= 0;
-    for (int j = 0; j < a.K; ++j) {
+    for (int j = 0; j < pK; ++j) {
         const int pj = __builtin_amdgcn_readlane(part, j);
         last = last && !(j > lane && pj == part);
     }
@@ -1956,8 +1960,8 @@ __global__ __launch_bounds__(256) void k_last(StageArgs a)
                 y = f == i ? ys[i] : y;
                 sf = f == i ? sfs[i] : sf;
             }
-            y = f == a.f ? yf : y;
-            sf = f == a.f ? sff : sf;
+            y = f == pf ? yf : y;
+            sf = f == pf ? sff : sf;
             add_partial<FP8>(acc, y, sf);
         }
     } else {
@@ -1973,11 +1977,11 @@ __global__ __launch_bounds__(256) void k_last(StageArgs a)
                     const int k = __builtin_ctzll(lm);
                     lm &= lm - 1;
                     const int f = __builtin_amdgcn_readlane(part, k);
-                    if (f == a.f) {
+                    if (f == pf) {
                         y[i] = yf;
                         sf[i] = sff;
                     } else if (col) {
-                        load_partial<FP8>(base + int64_t(f) * fstride, c, a.H, y[i], sf[i]);
+                        load_partial<FP8>(base + int64_t(f) * fstride, c, pH, y[i], sf[i]);
                     }
                     n = i + 1;
                 }
@@ -2333,8 +2337,10 @@ int be_launch_partial(const RoundPlan &p, int f, void *stream)
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL((k_partial<true, VPL>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((k_partial<false, VPL>), grid, dim3(256), 0, st, a);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8)
+        hipLaunchKernelGGL((k_partial<true, VPL>), grid, dim3(256), 0, st, a.slot, a.reply, a.K, a.H, a.nseg, a.ntok, a.f, a);
+    else
+        hipLaunchKernelGGL((k_partial<false, VPL>), grid, dim3(256), 0, st, a.slot, a.reply, a.K, a.H, a.nseg, a.ntok, a.f, a);
     return launched_ok();
 }
 
@@ -2348,8 +2354,10 @@ int be_launch_last(const RoundPlan &p, int f, void *stream)
     if (waves == 0) return 0;
     dim3 grid(unsigned((waves + 3) / 4));
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.combine == AFD_COMBINE_PER_STAGE_FP8) hipLaunchKernelGGL(k_last<true>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(k_last<false>, grid, dim3(256), 0, st, a);
+    if (p.combine == AFD_COMBINE_PER_STAGE_FP8)
+        hipLaunchKernelGGL(k_last<true>, grid, dim3(256), 0, st, a.slot, a.reply, a.K, a.H, a.nseg, a.ntok, a.f, a);
+    else
+        hipLaunchKernelGGL(k_last<false>, grid, dim3(256), 0, st, a.slot, a.reply, a.K, a.H, a.nseg, a.ntok, a.f, a);
     return launched_ok();
 }
 
