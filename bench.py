@@ -556,7 +556,7 @@ def measure_workload(name, args):
           f"dtype={cfg.dtype} L={L} bytes/round={nb['total']} cold sets={S}", file=sys.stderr, flush=True)
     sets = [RoundSet(inst, view, args.combine, args.cached, args.dispatch)]
     info = sets[0].buf.round_info()
-    # the survey's protocol beside the timed steps: five blocks of
+    # the five-block protocol beside the timed steps: five blocks of
     # protocol_block rounds after 64 warmup rounds
     (hot_us, hot_blocks), (prot_hot_us, _) = time_rounds(sets, 1, args.steps, args.warmup,
                                                          5 * args.protocol_block, gmax=gmax)
