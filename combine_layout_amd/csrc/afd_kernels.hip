@@ -473,35 +473,52 @@ __device__ __forceinline__ void token_ids_lds(const int *sids, int gg, int K, in
 // Dispatch in one kernel for small rounds (at most kFusedMaxTokens tokens,
 // kFusedMaxIds ids, kFusedMaxExperts experts).  Block g scatters token g,
 // each thread holding up to VMAX 16-byte columns of the row.  The row, the
-// token's weights and scales and every id of the round (copied straight
-// into LDS) are requested at entry, so a block waits on memory once before
-// its stores.  The block then needs two histograms of the round's live
-// choices: over all tokens (for the aligned starts of every expert) and over
-// the tokens before g (the rank of g's row inside each of its experts, since
-// a token holds an expert at most once):
+// token's weights and scales and every id of the round are requested at
+// entry.  The block then needs two histograms of the round's live choices:
+// over all tokens (for the aligned starts of every expert) and over the
+// tokens before g (the rank of g's row inside each of its experts, since a
+// token holds an expert at most once):
 //   row(g, e) = start_e + #{live choices of e in tokens before g}.
 // Both are kept in one LDS word per expert (all tokens in the low 16 bits,
 // earlier tokens in the high 16), so each choice costs one atomic.  The
 // leading scalar arguments (the first two sources' rows, ids and token
-// counts, K and nvec) are preloaded into SGPRs by the hardware; rounds of at
-// most two sources (FEW) address the row and the ids from them alone.
-template <int VMAX, int KMAX, bool FEW>
+// counts, K and nvec) are preloaded into SGPRs by the hardware.  Three forms:
+//   kFusedAny  any number of sources: every id of the round is copied
+//              straight into LDS (global_load_lds) after the row, and the
+//              first barrier waits for every load;
+//   kFusedFew  at most two sources: the same, with the row and the ids
+//              addressed from the preloaded arguments alone, so they are
+//              requested before any load from the argument block returns;
+//   kFusedReg  at most two sources, K = 8 and 16-byte aligned ids: every
+//              thread loads its two tokens' ids (tid and tid + 256, clamped
+//              to the round) into registers and lane k of every wavefront
+//              loads token g's id k, so no id passes through LDS.  Every
+//              load is unconditional, with in-bounds indices, so the
+//              counting waits for the ids alone, not for the row or the
+//              weights (whose address comes from the argument block), and
+//              the barriers order LDS only.
+constexpr int kFusedAny = 0, kFusedFew = 1, kFusedReg = 2;
+
+template <int VMAX, int KMAX, int MODE>
 __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t *px1, const int32_t *pids0,
                                                const int32_t *pids1, int pT0, int pT1, int pK, int pnvec,
                                                DispatchArgs a)
 {
+    constexpr bool FEW = MODE != kFusedAny, REG = MODE == kFusedReg;
+    static_assert(!REG || KMAX == 8, "register ids: eight per token");
+    static_assert(kFusedMaxTokens == 512, "register ids: two tokens per thread");
     extern __shared__ __align__(16) unsigned char lds[];
     __shared__ int s_off[kMaxSources + 1];
     __shared__ uint32_t s_live, s_slow;
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
-    int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (first: 16-byte aligned)
+    // per expert (+ spare): all | before << 16; aligned counts, then their
+    // exclusive prefix
+    __shared__ int hist[kFusedMaxExperts + 1], pfx[kFusedMaxExperts];
+    int *sids = reinterpret_cast<int *>(lds);   // [ntok * K] (not REG; first: 16-byte aligned)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const int g = blockIdx.x;
 
-    // 1. request every load: row, weights, scales, all ids.  With at most
-    // two sources (FEW) the row and the ids are addressed from the preloaded
-    // arguments alone, so they are requested before any load from the
-    // argument block returns.
+    // 1. request every load: ids, row, weights, scales
     auto ids_to_lds = [&](const int32_t *qids, int lo, int n, int K) {
         const gptr<const int32_t> src = (gptr<const int32_t>)qids;
         if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(qids) & 15u) == 0) {
@@ -528,18 +545,40 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
     u32x4 v[VMAX];
     int s, t0;
     bool mine;
+    int ev0[KMAX], ev1[KMAX];                   // REG: tokens tid and tid + 256
+    int eg = -1;                                // REG: token g's id `lane` (lanes < 8)
     if constexpr (FEW) {
         mine = g < pT0 + pT1;
         s = g < pT0 ? 0 : 1;
         t0 = s ? pT0 : 0;
-        if (mine) row_loads(v, (s ? px1 : px0) + int64_t(g - t0) * pnvec * 16, pnvec);
-        ids_to_lds(pids0, 0, pT0 * pK, pK);
-        if (pT1 > 0) ids_to_lds(pids1, pT0 * pK, pT1 * pK, pK);
+        if constexpr (REG) {
+            // one block per token of the round (mine), K = 8
+            const int nt = pT0 + pT1;
+            auto tok = [&](int gg) {
+                return (gptr<const u32x4>)((gg < pT0 ? pids0 + int64_t(gg) * 8 : pids1 + int64_t(gg - pT0) * 8));
+            };
+            const gptr<const u32x4> p0 = tok(tid < nt ? tid : nt - 1);
+            const gptr<const u32x4> p1 = tok(tid + 256 < nt ? tid + 256 : nt - 1);
+            const u32x4 a0 = p0[0], a1 = p0[1], b0 = p1[0], b1 = p1[1];
+            eg = ((gptr<const int32_t>)tok(g))[lane < 8 ? lane : 0];
+            ev0[0] = int(a0.x), ev0[1] = int(a0.y), ev0[2] = int(a0.z), ev0[3] = int(a0.w);
+            ev0[4] = int(a1.x), ev0[5] = int(a1.y), ev0[6] = int(a1.z), ev0[7] = int(a1.w);
+            ev1[0] = int(b0.x), ev1[1] = int(b0.y), ev1[2] = int(b0.z), ev1[3] = int(b0.w);
+            ev1[4] = int(b1.x), ev1[5] = int(b1.y), ev1[6] = int(b1.z), ev1[7] = int(b1.w);
+            const gptr<const u32x4> xs = (gptr<const u32x4>)((s ? px1 : px0) + int64_t(g - t0) * pnvec * 16);
+#pragma unroll
+            for (int i = 0; i < VMAX; ++i) {
+                const int c = tid + i * 256;
+                v[i] = xs[c < pnvec ? c : 0];
+            }
+        } else {
+            if (mine) row_loads(v, (s ? px1 : px0) + int64_t(g - t0) * pnvec * 16, pnvec);
+            ids_to_lds(pids0, 0, pT0 * pK, pK);
+            if (pT1 > 0) ids_to_lds(pids1, pT0 * pK, pT1 * pK, pK);
+        }
     }
     const Hdr h = load_hdr(a);
     const int E = h.E, K = h.K, ntok = h.ntok, G = h.G, N = h.N;
-    int *hist = sids + ntok * K;                // [E + 1] per expert (+ spare): all | before << 16
-    int *pfx = hist + E + 1;                    // [E] aligned counts, then their exclusive prefix
     if constexpr (!FEW) {
         mine = g < ntok;
         s = source_of(load_offsets(a.tok_off), N, mine ? g : 0, t0);
@@ -549,10 +588,21 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
     const SourceRec src = load_source(a, s);
     const int t = g - t0;
     float wk = 0.0f;
-    if (mine && tid < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + tid];
     float scv = 0.0f;
     const bool myscale = mine && h.fp8 && tid < G;
-    if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
+    if constexpr (REG) {
+        // unconditional, in bounds: BF16 rounds point the scale load at the
+        // token's weights, whose value is not used
+        wk = ((gptr<const float>)src.w)[int64_t(t) * K + (tid < K ? tid : 0)];
+        const bool fp8 = h.fp8 != 0;
+        const float *sbase = fp8 ? src.scale : src.w;
+        const int64_t sst = fp8 ? src.sst : int64_t(K);
+        const int64_t sgl = fp8 ? int64_t(tid < G ? tid : 0) * src.ssg : 0;
+        scv = ((gptr<const float>)sbase)[int64_t(t) * sst + sgl];
+    } else {
+        if (mine && tid < K) wk = ((gptr<const float>)src.w)[int64_t(t) * K + tid];
+        if (myscale) scv = ((gptr<const float>)src.scale)[int64_t(t) * src.sst + int64_t(tid) * src.ssg];
+    }
     if constexpr (!FEW) {
         for (int q = 0; q < N; ++q) {
             const SourceRec rq = load_source(a, q);
@@ -569,25 +619,38 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
     }
     for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
     if (tid == 0) s_slow = 0u;
-    __syncthreads();
+    if constexpr (REG) lds_barrier();
+    else __syncthreads();
 
     // 2. route check and the two histograms (choices that are not live
     // count into the spare slot at index E).  Tokens that pass the
     // compare-free check count at once; the others (repeats, invalid ids,
     // E > 248) are counted in a second pass that only a block holding such
     // a token runs, so the common round carries none of its code.
-    uint32_t failed = 0;             // bit i: this thread's i-th token needs the second pass
-    for (int gg = tid, i = 0; gg < ntok; gg += 256, ++i) {
-        int ev[KMAX];
-        token_ids_lds<KMAX>(sids, gg, K, ev);
-        uint32_t live;
-        if (routes_plain<KMAX>(ev, E, live)) {
-            const int inc = gg < g ? 0x10001 : 1;
+    auto count = [&](int gg, const int (&e)[KMAX], uint32_t live) {
+        const int inc = gg < g ? 0x10001 : 1;
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
-            if (gg == g) s_live = live;
-        } else {
-            failed |= 1u << i;
+        for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? e[k] : E], inc);
+        if (gg == g) s_live = live;
+    };
+    uint32_t failed = 0;             // bit i: this thread's i-th token needs the second pass
+    if constexpr (REG) {
+        uint32_t live;
+        if (tid < ntok) {
+            if (routes_plain<KMAX>(ev0, E, live)) count(tid, ev0, live);
+            else failed = 1u;
+        }
+        if (tid + 256 < ntok) {
+            if (routes_plain<KMAX>(ev1, E, live)) count(tid + 256, ev1, live);
+            else failed |= 2u;
+        }
+    } else {
+        for (int gg = tid, i = 0; gg < ntok; gg += 256, ++i) {
+            int e[KMAX];
+            token_ids_lds<KMAX>(sids, gg, K, e);
+            uint32_t live;
+            if (routes_plain<KMAX>(e, E, live)) count(gg, e, live);
+            else failed |= 1u << i;
         }
     }
     if (failed != 0) s_slow = 1u;
@@ -596,18 +659,19 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
         uint64_t err = kNoError;
         for (int gg = tid, i = 0; gg < ntok; gg += 256, ++i) {
             if (((failed >> i) & 1u) == 0u) continue;
-            int ev[KMAX];
-            token_ids_lds<KMAX>(sids, gg, K, ev);
+            int e[KMAX];
+            if constexpr (REG) {
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) e[k] = i == 0 ? ev0[k] : ev1[k];
+            } else {
+                token_ids_lds<KMAX>(sids, gg, K, e);
+            }
             int ss = 0, tt = 0;
             if (blockIdx.x == 0) {
                 ss = src_of_lds(s_off, N, gg);
                 tt = gg - s_off[ss];
             }
-            const uint32_t live = classify_token<KMAX>(ev, E, ss, tt, err);
-            const int inc = gg < g ? 0x10001 : 1;
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], inc);
-            if (gg == g) s_live = live;
+            count(gg, e, classify_token<KMAX>(e, E, ss, tt, err));
         }
         if (blockIdx.x == 0 && err != kNoError)
             __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -616,16 +680,22 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
 
     // 3. aligned starts: pfx[e] = sum of aligned counts of experts < e (all
     // partitions); expert e starts at pfx[e] - pfx[first expert of its part].
-    // Wavefront 0 aligns and scans in one pass (E <= 256: at most 4 experts
-    // per lane), then one barrier.
-    if (tid < kWave) {
+    // Wavefront 0 reads the counts in one batch (in-bounds indices, E <= 256:
+    // at most 4 experts per lane), aligns them (a mask for a power-of-two
+    // alignment) and scans them, then one barrier.
+    if (wave == 0) {
         const int per = (E + kWave - 1) / kWave;
         const int lo = lane * per;
         int c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = hist[lo + i < E ? lo + i : E] & 0xFFFF;
+        const int al = h.alpha;
+        const bool pow2 = (al & (al - 1)) == 0;
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            c[i] = i < per && lo + i < E ? align_up_i(hist[lo + i] & 0xFFFF, h.alpha) : 0;
+            const int up = pow2 ? (c[i] + al - 1) & -al : align_up_i(c[i], al);
+            c[i] = i < per && lo + i < E ? up : 0;
             sum += c[i];
         }
         int run = wave_inclusive_scan(sum) - sum;
@@ -646,7 +716,7 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
     uint64_t d = 0, ds = 0;
     int packed = -1;
     if (lane < K && ((s_live >> lane) & 1u)) {
-        const int e = sids[g * K + lane];
+        const int e = REG ? eg : sids[g * K + lane];
         const int row = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] >> 16);
         const int part = e / h.E_loc;
         packed = (part << 24) | row;
@@ -2098,6 +2168,7 @@ int launched_ok() { return hipGetLastError() == hipSuccess ? 0 : 1; }
 // argument block in front of them.
 struct FirstSources {
     bool two = false;          // the round has at most two sources
+    bool reg = false;          // and eight ids per token, 16-byte aligned: ids in registers
     const uint8_t *x0 = nullptr, *x1 = nullptr;
     const int32_t *ids0 = nullptr, *ids1 = nullptr;
     int T0 = 0, T1 = 0;
@@ -2115,6 +2186,8 @@ FirstSources first_sources(const DispatchArgs &a)
         f.ids1 = a.src[1].ids;
         f.T1 = a.src[1].T;
     }
+    f.reg = f.two && a.h.K == 8 &&
+            ((reinterpret_cast<uintptr_t>(f.ids0) | reinterpret_cast<uintptr_t>(f.ids1)) & 15u) == 0;
     return f;
 }
 
@@ -2126,11 +2199,12 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
     hipLaunchKernelGGL((k_fused<VMAX, KM, FW>), grid, dim3(256), lds, st, f.x0, f.x1, f.ids0, f.ids1, f.T0, f.T1,     \
                        a.h.K, a.h.nvec, a)
     if (k32) {
-        if (f.two) AFD_FUSED(32, true);
-        else AFD_FUSED(32, false);
+        if (f.two) AFD_FUSED(32, kFusedFew);
+        else AFD_FUSED(32, kFusedAny);
     } else {
-        if (f.two) AFD_FUSED(8, true);
-        else AFD_FUSED(8, false);
+        if (f.reg) AFD_FUSED(8, kFusedReg);
+        else if (f.two) AFD_FUSED(8, kFusedFew);
+        else AFD_FUSED(8, kFusedAny);
     }
 #undef AFD_FUSED
     return launched_ok();
@@ -2258,7 +2332,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
         // one block per token; 256 threads hold the row, VMAX columns each
         const int per = (a.h.nvec + 255) / 256;
         const int vm_f = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
-        const size_t lds = size_t(p.E + 1) * 4 + size_t(p.E) * 4 + size_t(p.ntok) * p.K * 4;
+        const size_t lds = size_t(p.ntok) * p.K * 4;
         dim3 grid(p.ntok);
         switch (vm_f) {
         case 1: return launch_fused_v<1>(a, k32, grid, lds, st);

@@ -225,9 +225,11 @@ def _crafted_ids(ids, E, rng):
 
 
 # (E, F, tokens, dispatch): E = 248 takes the compare-free check, 249 and 256
-# the pairwise one; small rounds run the one-kernel dispatch, larger ones the
-# layout kernel, and the one-launch dispatch its counting workgroups
-ROUTE_BYTES = [(248, 2, 120, "auto"), (249, 3, 120, "auto"), (8, 2, 90, "auto"), (248, 2, 700, "auto"),
+# the pairwise one; small rounds run the one-kernel dispatch (above 256
+# tokens with two tokens per thread), larger ones the layout kernel, and the
+# one-launch dispatch its counting workgroups
+ROUTE_BYTES = [(248, 2, 120, "auto"), (249, 3, 120, "auto"), (8, 2, 90, "auto"), (248, 2, 400, "auto"),
+               (249, 3, 450, "auto"), (248, 2, 700, "auto"),
                (249, 3, 700, "auto"), (256, 4, 700, "auto"), (248, 4, 700, "one_launch")]
 
 
