@@ -314,6 +314,16 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ int align_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
+// Partition of expert e, 0 <= e < 2^16, with E_loc experts per partition,
+// without an integer division.  (e + 1/2) / E_loc lies at least 1/(2 E_loc)
+// from every integer; the float product with the hardware reciprocal (1 ulp)
+// is off by less than (e + 1/2) / E_loc * 2^-21, which is smaller for
+// e < 2^19, so truncating it gives floor(e / E_loc).
+__device__ __forceinline__ int part_of(int e, int E_loc)
+{
+    return int((float(e) + 0.5f) * __builtin_amdgcn_rcpf(float(E_loc)));
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() is a full
 // workgroup fence: it waits for every outstanding global load and store of
 // the wave (the vector-memory counter), which would stall on row loads and
@@ -706,9 +716,7 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
         }
     }
     lds_barrier();
-    if (blockIdx.x == 0)
-        for (int e = tid; e < E; e += 256) h.ends[e] = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] & 0xFFFF);
-    if (!mine) return;
+    if (!mine) return;                          // (never block 0: a round here has a token)
 
     // 4. slot of choice k: lane k of every wavefront computes it (those of
     // wavefront 0 also write the slot map and the row weight); the stores
@@ -717,8 +725,8 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
     int packed = -1;
     if (lane < K && ((s_live >> lane) & 1u)) {
         const int e = REG ? eg : sids[g * K + lane];
-        const int row = pfx[e] - pfx[(e / h.E_loc) * h.E_loc] + (hist[e] >> 16);
-        const int part = e / h.E_loc;
+        const int part = part_of(e, h.E_loc);
+        const int row = pfx[e] - pfx[part * h.E_loc] + (hist[e] >> 16);
         packed = (part << 24) | row;
         d = s_prow[part] + uint64_t(row) * uint64_t(h.row_bytes);
         ds = s_ps[part] + uint64_t(row) * uint64_t(G) * 4u;
@@ -750,6 +758,10 @@ __global__ __launch_bounds__(256) void k_fused(const uint8_t *px0, const uint8_t
             ((gptr<float>)sk)[tid] = scv;
         }
     }
+    // ends, once the rows are on their way (nothing in this kernel waits
+    // for them)
+    if (blockIdx.x == 0)
+        for (int e = tid; e < E; e += 256) h.ends[e] = pfx[e] - pfx[part_of(e, h.E_loc) * h.E_loc] + (hist[e] & 0xFFFF);
 }
 
 // Tile histogram of larger rounds.  Block = NW wavefronts = one tile of
