@@ -314,11 +314,18 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ int align_up_i(int v, int a) { return (v + a - 1) / a * a; }
 
-// Partition of expert e, 0 <= e < 2^16, with E_loc experts per partition,
-// without an integer division.  (e + 1/2) / E_loc lies at least 1/(2 E_loc)
-// from every integer; the float product with the hardware reciprocal (1 ulp)
-// is off by less than (e + 1/2) / E_loc * 2^-21, which is smaller for
-// e < 2^19, so truncating it gives floor(e / E_loc).
+// x / d for x >= 0, d >= 1, with a shift when d is a power of two (the
+// common case for the wave-uniform sizes it divides)
+__device__ __forceinline__ int div_pow2_or(int x, int d)
+{
+    return (d & (d - 1)) == 0 ? x >> __builtin_ctz(uint32_t(d)) : x / d;
+}
+
+// Partition of expert e (0 <= e < 2^19; experts number at most 512) with
+// E_loc experts per partition, without an integer division.  (e + 1/2) /
+// E_loc lies at least 1/(2 E_loc) from every integer; the float product with
+// the hardware reciprocal (1 ulp) is off by less than (e + 1/2) / E_loc *
+// 2^-21, which is smaller, so truncating it gives floor(e / E_loc).
 __device__ __forceinline__ int part_of(int e, int E_loc)
 {
     return int((float(e) + 0.5f) * __builtin_amdgcn_rcpf(float(E_loc)));
@@ -1654,7 +1661,7 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t *slot, int ntok, 
     const uint64_t rb2 = base4(2), rb3 = base4(3);
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / nseg;
+    const int g = div_pow2_or(gw, nseg);
     const int seg = gw - g * nseg;
     if (g >= ntok) return;
     const int c0 = seg * kWave * VPL + lane;
@@ -1906,7 +1913,7 @@ __global__ __launch_bounds__(256) void k_partial(const int32_t *pslot, const uin
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / pnseg;
+    const int g = div_pow2_or(gw, pnseg);
     const int seg = gw - g * pnseg;
     if (g >= pntok) return;
     int2 sl;
@@ -1986,7 +1993,7 @@ __global__ __launch_bounds__(256) void k_last(const int32_t *pslot, const uint16
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & (kWave - 1);
     const int gw = blockIdx.x * 4 + wave_id();
-    const int g = gw / pnseg;
+    const int g = div_pow2_or(gw, pnseg);
     const int seg = gw - g * pnseg;
     if (g >= pntok) return;
     int2 sl;
