@@ -144,7 +144,9 @@ WorkspacePlan plan_workspace(const afd_config &c)
     if (c.combine != AFD_COMBINE_ONCE)
         off += a(size_t(c.num_partitions) * ntok * size_t(partial_row_bytes(c.combine, c.hidden)));
     w.tcount = off;
-    off += a(size_t(kLayoutMaxTiles) * c.num_experts * 4);
+    off += a(size_t(kLayoutMaxTiles) * tcount_pitch(c.num_experts) * 4);
+    w.ready = off;
+    off += a(size_t(kReadyCopies + kDoneGroups) * kReadyStride * 4);
     w.total = off;
     return w;
 }
@@ -217,6 +219,7 @@ void build_plan(afd_ctx *c, bool cached)
     p.slot = reinterpret_cast<int32_t *>(c->ws + c->wp.slot);
     p.partials = g.combine != AFD_COMBINE_ONCE ? reinterpret_cast<uint8_t *>(c->ws + c->wp.partials) : nullptr;
     p.tcount = reinterpret_cast<uint32_t *>(c->ws + c->wp.tcount);
+    p.ready = reinterpret_cast<uint32_t *>(c->ws + c->wp.ready);
     p.sync = reinterpret_cast<uint32_t *>(c->ws + kSyncOffset);
 }
 

@@ -120,10 +120,11 @@ struct DispatchHdr {
     uint64_t *err;           // sticky route-error word
     int64_t row_bytes;
     int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
-    uint32_t *tcount;        // one-launch dispatch: [E][kLayoutMaxTiles] tagged tile counts
+    uint32_t *tcount;        // one-launch dispatch: [kLayoutMaxTiles][tcount_pitch(E)] tagged tile counts
     uint32_t *sync;          // one-launch dispatch: launch counter, finished workgroups, gave-up flag
     int wait_polls;          // one-launch dispatch: polls before giving up
-    int pad[3];
+    int pad;
+    uint32_t *ready;         // one-launch dispatch: ready flag copies
 };
 
 // Layout tile record, 16 bytes, for rounds of at most kLayoutMaxTiles tiles:
@@ -155,7 +156,7 @@ struct Hdr {
     gptr<unsigned long long> err;
     int64_t row_bytes;
     int N, ntok, K, E, E_loc, alpha, nblk, cpitch, nvec, G, fp8, tile;
-    gptr<uint32_t> tcount, sync;
+    gptr<uint32_t> tcount, sync, ready;
     int wait_polls;
 };
 
@@ -187,6 +188,7 @@ __device__ __forceinline__ Hdr load_hdr(const DispatchArgs &a, u32x16 &r0, u32x1
     h.tcount = (gptr<uint32_t>)((uint64_t(r1[9]) << 32) | uint64_t(r1[8]));
     h.sync = (gptr<uint32_t>)((uint64_t(r1[11]) << 32) | uint64_t(r1[10]));
     h.wait_polls = int(r1[12]);
+    h.ready = (gptr<uint32_t>)((uint64_t(r1[15]) << 32) | uint64_t(r1[14]));
     return h;
 }
 
@@ -789,8 +791,12 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
     extern __shared__ __align__(16) unsigned char lds[];
     const int E = h.E, K = h.K;
     constexpr int TILE = NW * kWave;
-    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 1]
-    int *pre = reinterpret_cast<int *>(mask + size_t(NW) * (E + 1));          // [NW][E]
+    // per wavefront, a lane mask per expert and one spare word per lane
+    // (choices that are not live mark their lane's own spare, so they never
+    // contend for one address)
+    const int MS = E + kWave;
+    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);  // [NW][E + 64]
+    int *pre = reinterpret_cast<int *>(mask + size_t(NW) * MS);               // [NW][E]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     // the tile lies in one source's span of the tiled token space: its
     // first token's ids, its token count and its first token in the round
@@ -837,7 +843,7 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
             }
         }
     }
-    for (int i = tid; i < NW * (E + 1); i += TILE) mask[i] = 0ull;
+    for (int i = tid; i < NW * MS; i += TILE) mask[i] = 0ull;
     lds_barrier();
     uint32_t live = 0;
     {
@@ -845,11 +851,11 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
         if (!routes_plain<KMAX>(ev, E, live))
             live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);   // token index used only for an error
         if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // mark the token's lane bit per live expert (others into the spare slot E)
-        unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        // mark the token's lane bit per live expert (others into the lane's spare)
+        unsigned long long *mrow = mask + size_t(wave) * MS;
         const unsigned long long bit = 1ull << lane;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E], bit);
+        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E + lane], bit);
     }
     lds_barrier();
     for (int e = tid; e < E; e += TILE) {
@@ -857,14 +863,14 @@ __global__ __launch_bounds__(NW * 64) void k_layout(DispatchArgs a)
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             pre[w * E + e] = run;
-            run += __popcll(mask[w * (E + 1) + e]);
+            run += __popcll(mask[w * MS + e]);
         }
         h.blkcnt[e * h.cpitch + blockIdx.x] = run;
     }
     lds_barrier();
     if (have) {
         const unsigned long long below = (1ull << lane) - 1ull;
-        const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        const unsigned long long *mrow = mask + size_t(wave) * MS;
         const gptr<int32_t> pk = h.packed + int64_t(g) * K;
         int vals[KMAX];
 #pragma unroll
@@ -1107,43 +1113,68 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 //
 // Counts first, then the expansion, in one launch (design page, section 16)
 // for rounds of at most kLayoutMaxTiles layout tiles and 256 experts.
-// Workgroups 0 .. kLayoutMaxTiles - 1 each count the live choices of one
-// layout tile per expert and publish them as tagged words (tag << 9 |
-// count; a tile holds at most 256 tokens) with device-scope stores; a
-// counting workgroup past the round's last tile publishes zeros, so every
-// launch rewrites every word and a stale word always carries the previous
-// launch's tag, and then add one to the arrival counter.
+// Workgroups of five wavefronts.  Workgroups 0 .. kLayoutMaxTiles - 1 each
+// count the live choices of one layout tile per expert and publish them as
+// tagged words (tag << 9 | count; a tile holds at most 256 tokens) with
+// device-scope stores; a counting workgroup past the round's last tile
+// publishes zeros, so every launch rewrites every word and a stale word
+// always carries another launch's tag.  Each then adds one to the arrival
+// counter; the one that completes it writes the launch's tag into every
+// copy of the ready flag.
 // Every other workgroup scatters TB slots of the tiled token space as
-// k_scatter does, but ranks its tokens' choices inside their tile itself
-// (lane masks over the tile's tokens up to its own, as k_layout builds them)
-// and takes the tile counts from the published words: one lane polls the
-// arrival counter until every counting workgroup has published, then the
-// workgroup reads the words once with device-scope loads (and checks their
-// tags, reading again if one is stale): the one hand-off between
-// workgroups.  The counting workgroups have the lowest
-// indices and never wait, so the hand-off completes whatever number of
-// workgroups is resident at once.  The wait is bounded: past h.wait_polls
-// polls a workgroup sets the sticky gave-up flag, marks its tokens' choices
-// skipped in the slot map (the combine then reads nothing for them), clears
-// ends[] if it is the first, stores no row and exits.  The tag is one more
-// than the launch counter; the last workgroup to finish advances the
-// counter and clears the arrival counter, and stream order shows the next
-// launch the new values.
+// k_scatter does with its first four wavefronts, which rank their tokens'
+// choices inside their tile themselves (lane masks over the tile's tokens
+// up to their own, as k_layout builds them).  Its fifth wavefront holds no
+// row loads, so its polls are not queued behind them: it polls one copy of
+// the ready flag (eight or so workgroups per copy) until it reads a tag,
+// the one hand-off between workgroups.  The workgroup then reads the
+// tagged words through the caches (a cache holds no copy from before the
+// words were final: kernels start with invalidated caches and no workgroup
+// reads a word before the flag is set), checks every tag against the
+// flag's, and reads again at device scope if one differs.
+// The counting workgroups have the lowest indices and never wait, so the
+// hand-off completes whatever number of workgroups is resident at once.
+// The wait is bounded: past h.wait_polls polls a workgroup sets the sticky
+// gave-up flag, marks its tokens' choices skipped in the slot map (the
+// combine then reads nothing for them), clears ends[] if it is the first,
+// stores no row and exits.  Every workgroup counts itself finished once it
+// no longer reads the counters (a scatter workgroup right after its
+// hand-off, while its stores proceed), in one of several group counters;
+// the last one advances the launch counter and clears the counters and the
+// flags, and stream order shows the next launch the new values.
+// Choices that are not live mark a spare word of their own lane, in the
+// counting histogram as in the rank masks, so idle lanes past a tile's
+// tokens never contend for one LDS address.
 
 constexpr int kTagShift = 9;
 constexpr uint32_t kTagMask = 0x7FFFFFu;
+constexpr int kD1Waves = 5;                    // four scatter wavefronts and the hand-off wavefront
+constexpr int kD1Threads = kD1Waves * kWave;
 
-__device__ __forceinline__ void onepass_finish(const Hdr &h, uint32_t launch)
+// Tag of the launch whose counter reads `launch`: never 0 (the value of a
+// cleared word and of a flag not yet set), and different for consecutive
+// launches, also where the 32-bit counter wraps.
+__device__ __forceinline__ uint32_t launch_tag(uint32_t launch) { return launch % kTagMask + 1u; }
+
+// One lane: this workgroup no longer reads the launch's counters or flags.
+// It counts itself in its group's counter; the last of a group counts the
+// group, and the last group clears everything for the next launch and
+// advances the launch counter.  (Counters per group, each on its own line,
+// keep the grid's finishing workgroups from queueing on one address.)
+__device__ __forceinline__ void onepass_done(const Hdr &h)
 {
-    lds_barrier();
-    if (threadIdx.x == 0) {
-        const uint32_t n = __hip_atomic_fetch_add(&h.sync[kSyncDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (n + 1u == gridDim.x) {
-            __hip_atomic_store(&h.sync[kSyncDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&h.sync[kSyncArrive], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&h.sync[0], launch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    const int grp = int(blockIdx.x) % kDoneGroups;
+    const uint32_t gsize = (gridDim.x - uint32_t(grp) + kDoneGroups - 1u) / kDoneGroups;
+    const gptr<uint32_t> gc = h.ready + (kReadyCopies + grp) * kReadyStride;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u != gsize) return;
+    const uint32_t ngroups = gridDim.x < uint32_t(kDoneGroups) ? gridDim.x : uint32_t(kDoneGroups);
+    if (__hip_atomic_fetch_add(&h.sync[kSyncDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u != ngroups)
+        return;
+    for (int c = 0; c < kReadyCopies + kDoneGroups; ++c)
+        __hip_atomic_store(&h.ready[c * kReadyStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&h.sync[kSyncDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&h.sync[kSyncArrive], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&h.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Ids of the token in tile slot `slot` (-1 past K or when `have` is false).
@@ -1174,57 +1205,79 @@ __device__ __forceinline__ void load_token_ids(const int32_t *ids_first, int slo
 }
 
 template <int KMAX, int VMAX>
-__global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
+__global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
 {
-    static_assert(kLayoutMaxTiles == 32, "tile counts polled into 32 registers");
+    static_assert(kLayoutMaxTiles == 32, "tile counts read into 32 registers");
     const u32x4 tr = reinterpret_cast<const u32x4 *>(a.tiles)[blockIdx.x < kLayoutMaxTiles ? blockIdx.x : 0];
     const Hdr h = load_hdr(a);
-    const uint32_t launch = __hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t tag = (launch + 1u) & kTagMask;
     extern __shared__ __align__(16) unsigned char lds[];
     const int E = h.E, K = h.K, nblk = h.nblk;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
 
     if (blockIdx.x < kLayoutMaxTiles) {
         // ---- counting workgroup of tile b: route check, count, publish
-        int *hist = reinterpret_cast<int *>(lds);          // [E + 1] (spare slot E for choices not live)
+        const uint32_t tag =
+            launch_tag(__hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        // a count per expert, then one spare per lane for choices that are
+        // not live (so they never contend for one address)
+        int *hist = reinterpret_cast<int *>(lds);          // [E + 64]
         const int b = blockIdx.x;
-        for (int i = tid; i < E + 1; i += 256) hist[i] = 0;
+        for (int i = tid; i < E + kWave; i += kD1Threads) hist[i] = 0;
         const int n_tile = b < nblk ? int(tr.w & 0xFFFFu) : 0;
         const int s = int(tr.w >> 16);
         const int32_t *ids_first = reinterpret_cast<const int32_t *>((uint64_t(tr.y) << 32) | uint64_t(tr.x));
         int ev[KMAX];
         load_token_ids<KMAX>(ids_first, tid, K, tid < n_tile, ev);
         lds_barrier();
-        {
+        if (wave * kWave < n_tile) {     // wavefronts past the tile's tokens count nothing
             uint64_t err = kNoError;
             const int g = int(tr.z) + tid;
             uint32_t live;
             if (!routes_plain<KMAX>(ev, E, live)) live = classify_token<KMAX>(ev, E, s, g - a.tok_off[s], err);
             if (err != kNoError) __hip_atomic_fetch_min(h.err, err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E], 1);
+            for (int k = 0; k < KMAX; ++k) atomicAdd(&hist[((live >> k) & 1u) ? ev[k] : E + lane], 1);
         }
         lds_barrier();
-        for (int e = tid; e < E; e += 256)
-            __hip_atomic_store(&h.tcount[e * kLayoutMaxTiles + b], (tag << kTagShift) | uint32_t(hist[e]),
+        // tile-major, one run of whole 128-byte lines per tile, so every
+        // line is written by one workgroup only
+        for (int e = tid; e < E; e += kD1Threads)
+            __hip_atomic_store(&h.tcount[b * tcount_pitch(E) + e], (tag << kTagShift) | uint32_t(hist[e]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every thread's count stores acknowledged (the barrier waits for them)
-        // before the arrival; readers check the tags anyway, so no release
-        // fence (an L2 write-back) is needed
-        __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        onepass_finish(h, launch);
+        // every wavefront's count stores acknowledged, then the barrier: the
+        // workgroup's counts are in memory before its arrival (readers check
+        // the tags anyway, so no release fence, an L2 write-back, is needed)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        lds_barrier();
+        if (wave == 0) {
+            uint32_t r = 0;
+            if (lane == 0)
+                r = __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r = uint32_t(__builtin_amdgcn_readfirstlane(int(r)));
+            if (r + 1u == uint32_t(kLayoutMaxTiles)) {
+                // the last arrival: every tile's counts are in memory, so set
+                // every copy of the ready flag to this launch's tag, and wait
+                // for those stores before counting this workgroup finished
+                for (int c = lane; c < kReadyCopies; c += kWave)
+                    __hip_atomic_store(&h.ready[c * kReadyStride], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+            if (lane == 0) onepass_done(h);
+        }
         return;
     }
 
-    // ---- scatter workgroup: W tokens per wavefront, TB per workgroup
+    // ---- scatter workgroup: wavefronts 0-3 hold W tokens each, TB in all;
+    // wavefront 4 makes the hand-off
     constexpr int W = VMAX >= 4 ? 1 : 4 / VMAX;
     constexpr int TB = 4 * W;
+    constexpr int HW = kD1Waves - 1;             // the hand-off wavefront
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     __shared__ int s_gaveup;
-    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);   // [4][E + 1]
-    int *pre = reinterpret_cast<int *>(mask + 4 * (E + 1));                   // [4][E]
+    __shared__ uint32_t s_tag;
+    const int MS = E + kWave;                    // lane masks per expert, then a spare per lane
+    unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);   // [4][E + 64]
+    int *pre = reinterpret_cast<int *>(mask + 4 * MS);                        // [4][E]
     int *pkl = pre + 4 * E;                                                   // [TB][K] (expert << 16 | rank), -1
     int *base = pkl + TB * K;                                                 // [E]
     int *A = base + E;                                                        // [E]
@@ -1239,9 +1292,10 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
     const int g_src = src.off;
 
     // 1. the ids of the tile's tokens up to this workgroup's last slot
-    // (thread = slot of the tile), then the rows, weights and scales of this
-    // wavefront's tokens: loads complete in issue order, so the ids (needed
-    // first, for the ranks) go ahead of the rows
+    // (thread = slot of the tile, so wavefronts 0-3), then the rows,
+    // weights and scales of the scatter wavefronts' tokens: loads complete
+    // in issue order, so the ids (needed first, for the ranks) go ahead of
+    // the rows.  The hand-off wavefront loads nothing here.
     const int o = v_first - tile * h.tile;       // this workgroup's first slot inside its tile
     const int tt0 = tile * h.tile - src.voff;    // source token of the tile's first slot
     int ev[KMAX];
@@ -1250,7 +1304,7 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
     u32x4 v[W][VMAX];
     float wk[W];
     float scv[W];
-    {
+    if (wave < HW) {
         const int kl = lane < K ? lane : 0;
         const bool fp8 = h.fp8 != 0;
         const float *sbase = fp8 ? src.scale : src.w;
@@ -1275,33 +1329,33 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
         if (wave == 2) table_to_lds(s_ps, a.scales);
         if (wave == 3) s_gaveup = 0;
     }
-    for (int i = tid; i < 4 * (E + 1); i += 256) mask[i] = 0ull;
+    for (int i = tid; i < 4 * MS; i += kD1Threads) mask[i] = 0ull;
     lds_barrier();
 
     // 2. in-tile ranks of this workgroup's tokens (route errors are recorded
     // by the counting workgroups)
-    uint32_t live;
-    {
+    uint32_t live = 0;
+    if (wave < HW && wave * kWave < o + TB) {    // wavefronts past this workgroup's slots mark nothing
         uint64_t err_unused = kNoError;
         if (!routes_plain<KMAX>(ev, E, live)) live = classify_token<KMAX>(ev, E, 0, 0, err_unused);
-        unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        unsigned long long *mrow = mask + size_t(wave) * MS;
         const unsigned long long bit = 1ull << lane;
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E], bit);
+        for (int k = 0; k < KMAX; ++k) atomicOr(&mrow[((live >> k) & 1u) ? ev[k] : E + lane], bit);
     }
     lds_barrier();
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += kD1Threads) {
         int run = 0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             pre[w * E + e] = run;
-            run += __popcll(mask[w * (E + 1) + e]);
+            run += __popcll(mask[w * MS + e]);
         }
     }
     lds_barrier();
     if (tid >= o && tid < o + TB) {
         const unsigned long long below = (1ull << lane) - 1ull;
-        const unsigned long long *mrow = mask + size_t(wave) * (E + 1);
+        const unsigned long long *mrow = mask + size_t(wave) * MS;
         int *dst = pkl + (tid - o) * K;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
@@ -1311,71 +1365,81 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
         }
     }
 
-    // 3. the published tile counts: one lane polls the arrival counter until
-    // every counting workgroup has published (bounded); then thread e reads
-    // expert e's run of words (expert-major, two tiles per 8-byte
-    // device-scope load) and checks that every one of the round's tiles
-    // carries this launch's tag, reading again if not (bounded)
-    if (tid == 0) {
-        for (int it = 0;; ++it) {
-            if (it > h.wait_polls) {
-                s_gaveup = 1;
-                break;
-            }
-            if (__hip_atomic_load(&h.sync[kSyncArrive], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-                uint32_t(kLayoutMaxTiles))
-                break;
-            __builtin_amdgcn_s_sleep(2);
+    // 3. the hand-off: wavefront 4, which has no loads of its own in flight
+    // (its polls do not queue behind the rows), polls this workgroup's copy
+    // of the ready flag until it holds a launch's tag (bounded; every lane
+    // reads the same word, one request per poll)
+    if (wave == HW) {
+        const gptr<uint32_t> rf = h.ready + (jb % kReadyCopies) * kReadyStride;
+        uint32_t tg = 0;
+        for (int it = 0; it <= h.wait_polls; ++it) {
+            tg = __hip_atomic_load(rf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (tg != 0u) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        tg = uint32_t(__builtin_amdgcn_readfirstlane(int(tg)));
+        if (lane == 0) {
+            s_tag = tg;
+            if (tg == 0u) s_gaveup = 1;
         }
     }
-    // (no acquire fence: on this GPU it invalidates the XCD's L2, which
-    // measured far slower than device-scope reads of the words, whose tags
-    // show whether they are this launch's)
     lds_barrier();
+    // nothing below is moved above the hand-off
+    asm volatile("" ::: "memory");
+    // thread e reads expert e's word of every tile through the caches (a
+    // wavefront's lanes read consecutive words; no cache holds a copy from
+    // before the words were final) and checks that every one of the round's
+    // tiles carries the flag's tag; otherwise it reads them again at device
+    // scope (bounded)
     uint32_t cw[kLayoutMaxTiles];
+    const uint32_t tag = s_tag;
     if (tid < E && !s_gaveup) {
-        const gptr<unsigned long long> run = (gptr<unsigned long long>)(h.tcount + tid * kLayoutMaxTiles);
-        for (int it = 0;; ++it) {
+        const int pitch = tcount_pitch(E);
+        const gptr<const uint32_t> col = (gptr<const uint32_t>)h.tcount + tid;
+#pragma unroll
+        for (int b = 0; b < kLayoutMaxTiles; ++b) cw[b] = col[b * pitch];
+        bool fresh = true;
+#pragma unroll
+        for (int b = 0; b < kLayoutMaxTiles; ++b) fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
+        for (int it = 0; !fresh; ++it) {
             if (it > h.wait_polls) {
                 s_gaveup = 1;
                 break;
             }
-#pragma unroll
-            for (int q = 0; q < kLayoutMaxTiles / 2; ++q) {
-                const unsigned long long two = __hip_atomic_load(&run[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                cw[2 * q] = uint32_t(two);
-                cw[2 * q + 1] = uint32_t(two >> 32);
-            }
-            bool fresh = true;
-#pragma unroll
-            for (int b = 0; b < kLayoutMaxTiles; ++b) fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
-            if (fresh) break;
             __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+            for (int b = 0; b < kLayoutMaxTiles; ++b)
+                cw[b] = __hip_atomic_load(&h.tcount[b * pitch + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            fresh = true;
+#pragma unroll
+            for (int b = 0; b < kLayoutMaxTiles; ++b)
+                fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
         }
     }
     lds_barrier();
     if (s_gaveup) {
         // no counts: this workgroup's choices are skipped, nothing is stored
-        __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (wave < HW) {
 #pragma unroll
-        for (int j = 0; j < W; ++j) {
-            const int t = t_first + j;
-            if (t < T_s && lane < K) {
-                i32x2 sl;
-                sl.x = -1;
-                sl.y = __float_as_int(wk[j]);
-                ((gptr<i32x2>)h.slot)[int64_t(g_src + t) * K + lane] = sl;
+            for (int j = 0; j < W; ++j) {
+                const int t = t_first + j;
+                if (t < T_s && lane < K) {
+                    i32x2 sl;
+                    sl.x = -1;
+                    sl.y = __float_as_int(wk[j]);
+                    ((gptr<i32x2>)h.slot)[int64_t(g_src + t) * K + lane] = sl;
+                }
             }
         }
         if (jb == 0)
-            for (int e = tid; e < E; e += 256) h.ends[e] = 0;
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        onepass_finish(h, launch);
+            for (int e = tid; e < E; e += kD1Threads) h.ends[e] = 0;
+        if (wave == HW && lane == 0) onepass_done(h);
         return;
     }
 
     // 4. this tile's first row of every expert (as k_scatter)
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += kD1Threads) {
         int C = 0, before = 0;
 #pragma unroll
         for (int b = 0; b < kLayoutMaxTiles; ++b) {
@@ -1389,14 +1453,19 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
     }
     lds_barrier();
     block_exclusive_scan(A, E);
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += kD1Threads) {
         const int start = A[e] - A[(e / h.E_loc) * h.E_loc];
         base[e] += start;
         if (jb == 0) h.ends[e] = start + Cs[e];
     }
     lds_barrier();
-    // every row, weight and scale load (and every poll) has been waited for
-    // here, once, before the first store (see k_scatter)
+    if (wave == HW) {
+        // the counters and flags are no longer read by this workgroup
+        if (lane == 0) onepass_done(h);
+        return;
+    }
+    // every row, weight and scale load has been waited for here, once,
+    // before the first store (see k_scatter)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // 5. slots and stores, token by token (as k_scatter)
@@ -1482,7 +1551,6 @@ __global__ __launch_bounds__(256) void k_dispatch1(DispatchArgs a)
             }
         }
     }
-    onepass_finish(h, launch);
 }
 
 // Dispatch of a cached round.  Block = 256 threads = 256 / LPT tokens, LPT
@@ -2157,6 +2225,7 @@ DispatchArgs make_dispatch_args(const RoundPlan &p)
     a.h.slot = p.slot;
     a.h.tcount = p.tcount;
     a.h.sync = p.sync;
+    a.h.ready = p.ready;
     a.h.wait_polls = p.wait_polls;
     TileRec tr[kLayoutMaxTiles];
     const int ntr = layout_tiles(p, tr);
@@ -2235,11 +2304,11 @@ template <int VMAX>
 int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 4 ? 1 : 4 / VMAX);
-    const size_t scatter_lds = size_t(4) * (E + 1) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(3) * E * 4;
-    const size_t lds = scatter_lds > size_t(E + 1) * 4 ? scatter_lds : size_t(E + 1) * 4;
+    const size_t scatter_lds = size_t(4) * (E + kWave) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(3) * E * 4;
+    const size_t lds = scatter_lds > size_t(E + kWave) * 4 ? scatter_lds : size_t(E + kWave) * 4;
     const dim3 grid(kLayoutMaxTiles + nslots / TB);
-    if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(256), lds, st, a);
+    if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(kD1Threads), lds, st, a);
+    else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     return launched_ok();
 }
 
@@ -2363,7 +2432,7 @@ int be_launch_dispatch(const RoundPlan &p, void *stream)
     {
         // one workgroup per tile of 64, 128 or 256 tokens, one lane per token
         const int nw = p.tile / kWave;
-        const size_t lds = size_t(nw) * (p.E + 1) * 8 + size_t(nw) * p.E * 4;
+        const size_t lds = size_t(nw) * (p.E + kWave) * 8 + size_t(nw) * p.E * 4;
         const dim3 grid(p.nblk), blk(p.tile);
         if (nw == 1) {
             if (k32) hipLaunchKernelGGL((k_layout<32, 1>), grid, blk, lds, st, a);

@@ -39,13 +39,29 @@ constexpr uint64_t kNoError = ~0ull;
 
 // The workspace's first 256 bytes: the route-error word at 0, and the
 // one-launch dispatch's words (uint32) at byte 64: launch counter at index
-// 0, finished workgroups at 16, the sticky gave-up flag at 32, published
-// tiles at 40.
+// 0, finished workgroup groups at 16, the sticky gave-up flag at 32,
+// published tiles at 40.
 constexpr size_t kSyncOffset = 64;
 constexpr int kSyncDone = 16;
 constexpr int kSyncStall = 32;
 constexpr int kSyncArrive = 40;
 constexpr int kDefaultWaitPolls = 1000000;
+// The one-launch dispatch's ready flag, in this many copies one 128-byte
+// line apart, so that the scatter workgroups' polls spread over many lines
+// instead of all reading one word.
+constexpr int kReadyCopies = 64;
+constexpr int kReadyStride = 32;   // uint32 words between copies (and between group counters)
+// Finished workgroups of a one-launch dispatch are counted in this many
+// group counters (workgroup b in group b % kDoneGroups), each on a line of
+// its own after the flag copies; the last of a group counts the group in
+// the workspace's finished-group word.
+constexpr int kDoneGroups = 16;
+// Words between consecutive tiles' runs of the one-launch dispatch's tile
+// counts (tile-major, each run on whole 128-byte lines).
+#ifdef __HIPCC__
+__host__ __device__
+#endif
+inline int tcount_pitch(int E) { return (E + 31) / 32 * 32; }
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -83,7 +99,9 @@ struct WorkspacePlan {
                            // bytes of slack (the combine reads slots 64 bytes at a time)
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
     size_t partials = 0;   // per-stage combine: [F][N][capacity] rows of partial_row_bytes
-    size_t tcount = 0;     // one-launch dispatch: uint32 [E][kLayoutMaxTiles] tagged tile counts
+    size_t tcount = 0;     // one-launch dispatch: uint32 [kLayoutMaxTiles][tcount_pitch(E)] tagged tile counts
+    size_t ready = 0;      // one-launch dispatch: uint32 ready flag, kReadyCopies copies kReadyStride apart,
+                           // then kDoneGroups finished-workgroup counters at the same stride
     size_t total = 0;
     int nblk_max = 0;
 };
@@ -128,7 +146,8 @@ struct RoundPlan {
     // per-stage combine: row (f, s, t) at partials + ((f * N + s) * capacity + t) * prow
     uint8_t *partials = nullptr;
     // one-launch dispatch
-    uint32_t *tcount = nullptr;   // [E][kLayoutMaxTiles]
+    uint32_t *tcount = nullptr;   // [kLayoutMaxTiles][tcount_pitch(E)]
+    uint32_t *ready = nullptr;    // [(kReadyCopies + kDoneGroups) * kReadyStride]
     uint32_t *sync = nullptr;     // launch counter, finished workgroups, gave-up flag
     int wait_polls = kDefaultWaitPolls;
 };
