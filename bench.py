@@ -17,8 +17,15 @@ rounds reuse one set.  The timed rounds (--steps after --warmup) run in
 graphs of at most 64 rounds, in blocks of at least 64 (one block at 20
 steps, since every graph launch has a fixed device-side cost); beside them
 the five-block figure runs five blocks of 256 rounds and takes the median
-block.  Each figure is the median over fresh processes (three by default).
-`value` is the timed rounds' cold whole-round algorithmic throughput:
+block.  The timed rounds are measured on the GPU's own constant-rate clock,
+stamped by tiny kernels captured in the same graph before the first round
+and after the last; HIP events around the graph launch are reported beside
+them (`us_per_round_events`), since they also hold the graph launch's and
+the events' fixed cost (about 12 us per graph here, 0.6 us per round at 20
+rounds).  The five-block figure is timed with events (its blocks of 256
+rounds spread that cost thin).  Each figure is the median over fresh
+processes (three by default).  `value` is the timed rounds' cold
+whole-round algorithmic throughput:
 
   per token       : H*b_x (+4*H/128 FP8 scales) read x, 2*H write the output,
                     8*K read ids+weights, 8*K write + 8*K read the slot map
@@ -162,8 +169,37 @@ class RoundSet:
         self.combine_phase(self.dispatch_phase())
 
 
-def capture(sets, order):
-    """A graph of one round of each set index in `order`, in that order."""
+class Clock:
+    """The GPU's constant-rate real-time counter, stamped by a one-wavefront
+    kernel (combine_layout_amd/_lib/libafd_clock.so) that a captured graph
+    can hold: timing events cannot be recorded inside a capture, and an
+    event pair around a graph launch also measures the launch's fixed cost
+    (about 8 us per graph launch and 4 us per event pair here, which at 20
+    rounds per graph is 0.6 us per round that no round spends)."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "combine_layout_amd", "_lib", "libafd_clock.so")
+        self.lib = ctypes.CDLL(path)
+        self.lib.afd_clock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.afd_clock_hz.argtypes = [ctypes.POINTER(ctypes.c_longlong)]
+        hz = ctypes.c_longlong(0)
+        if self.lib.afd_clock_hz(ctypes.byref(hz)) != 0:
+            raise RuntimeError("afd_clock_hz failed")
+        self.hz = float(hz.value)
+
+    def stamp(self, addr):
+        """Enqueue a stamp of the counter into the device word at `addr` on
+        the current stream."""
+        import torch
+        if self.lib.afd_clock_stamp(addr, torch.cuda.current_stream().cuda_stream) != 0:
+            raise RuntimeError("afd_clock_stamp failed")
+
+
+def capture(sets, order, stamps=None):
+    """A graph of one round of each set index in `order`, in that order.
+    stamps = (clock, addr0, addr1): the graph also stamps the device clock
+    into addr0 before its first round and into addr1 after its last."""
     import torch
     g = torch.cuda.CUDAGraph()
     stream = torch.cuda.Stream()
@@ -174,8 +210,12 @@ def capture(sets, order):
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
+        if stamps is not None:
+            stamps[0].stamp(stamps[1])
         for i in order:
             sets[i].round()
+        if stamps is not None:
+            stamps[0].stamp(stamps[2])
     torch.cuda.synchronize()
     return g
 
@@ -189,30 +229,50 @@ class RoundPlan:
     as graphs of at most `gmax` rounds (cached in `graphs` by starting set
     and length).  Every graph launch has a fixed device-side cost (HIP timing
     events cannot be recorded inside a graph on this runtime), so a block has
-    at least 64 rounds: fewer steps make fewer blocks (one, at 20 steps)."""
+    at least 64 rounds: fewer steps make fewer blocks (one, at 20 steps).
+    HIP events bracket every block.  With a `clock`, the blocks' graphs are
+    captured for this plan alone with a device clock stamp before their
+    first round and after their last, and a block's stamped time is the sum
+    over its graphs of the stamped spans: the rounds themselves, without the
+    graph launches and event records in between (each span also holds the
+    first stamp's own short kernel)."""
 
-    def __init__(self, sets, S, first, steps, warmup, graphs, blocks=5, gmax=64):
+    def __init__(self, sets, S, first, steps, warmup, graphs, blocks=5, gmax=64, clock=None):
         import torch
 
-        def chunks(start, n):
+        def chunks(start, n, stamped=False):
             out = []
             while n > 0:
                 m = min(n, gmax)
-                key = (start % S, m)
-                if key not in graphs:
-                    graphs[key] = capture(sets, [(start + j) % S for j in range(m)])
-                out.append(graphs[key])
+                order = [(start + j) % S for j in range(m)]
+                if stamped:
+                    k = len(self.spans)
+                    self.spans.append(k)
+                    base = self.stamp_buf.data_ptr() + 16 * k
+                    out.append(capture(sets, order, (clock, base, base + 8)))
+                else:
+                    key = (start % S, m)
+                    if key not in graphs:
+                        graphs[key] = capture(sets, order)
+                    out.append(graphs[key])
                 start += m
                 n -= m
             return out
 
         blocks = max(1, min(blocks, steps // 64))
         self.per = [steps // blocks + (1 if b < steps % blocks else 0) for b in range(blocks)]
+        self.clock = clock
+        self.spans = []
+        ngraphs = sum((n + gmax - 1) // gmax for n in self.per)
+        self.stamp_buf = torch.zeros((max(1, ngraphs), 2), dtype=torch.int64, device="cuda")
         self.warm = chunks(first, warmup)
         self.blocks = []
+        self.block_spans = []
         i = first + warmup
         for n in self.per:
-            self.blocks.append(chunks(i, n))
+            k0 = len(self.spans)
+            self.blocks.append(chunks(i, n, stamped=clock is not None))
+            self.block_spans.append(list(range(k0, len(self.spans))))
             i += n
         self.end = i
         self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
@@ -227,12 +287,20 @@ class RoundPlan:
             self.ev[b + 1].record()
 
     def result(self):
-        """Median block µs per round and every block's value (after a sync)."""
+        """Median block µs per round and every block's value (after a sync),
+        from the HIP events."""
         us = [self.ev[b].elapsed_time(self.ev[b + 1]) * 1e3 / n for b, n in enumerate(self.per)]
         return float(np.median(us)), us
 
+    def result_stamped(self):
+        """The same from the device clock stamps (plans with a clock)."""
+        t = self.stamp_buf.cpu().numpy()
+        us = [float(sum(t[k, 1] - t[k, 0] for k in ks)) / self.clock.hz * 1e6 / n
+              for ks, n in zip(self.block_spans, self.per)]
+        return float(np.median(us)), us
 
-def time_rounds(sets, S, steps, warmup, protocol_steps, protocol_warmup=64, gmax=64):
+
+def time_rounds(sets, S, steps, warmup, protocol_steps, protocol_warmup=64, gmax=64, clock=None):
     """The timed steps and the five-block protocol figure on one rotation.
 
     Every graph is captured first; then the protocol's rounds and, right
@@ -240,17 +308,18 @@ def time_rounds(sets, S, steps, warmup, protocol_steps, protocol_warmup=64, gmax
     enqueued back to back, so the timed steps run on a GPU that has been
     busy for milliseconds (as in a serving loop) rather than one waking from
     the host's capture work, and HIP events between blocks bracket device
-    work.  Returns ((median, blocks) of the timed steps, (median, blocks) of
-    the protocol)."""
+    work.  The timed steps' graphs also carry device clock stamps (`clock`).
+    Returns ((median, blocks) of the timed steps from the stamps, the same
+    from the events, (median, blocks) of the protocol from the events)."""
     import torch
     graphs = {}
     prot = RoundPlan(sets, S, 0, protocol_steps, protocol_warmup, graphs, gmax=gmax)
-    timed = RoundPlan(sets, S, prot.end, steps, warmup, graphs, gmax=gmax)
+    timed = RoundPlan(sets, S, prot.end, steps, warmup, graphs, gmax=gmax, clock=clock)
     torch.cuda.synchronize()
     prot.enqueue()
     timed.enqueue()
     torch.cuda.synchronize()
-    out = timed.result(), prot.result()
+    out = timed.result_stamped(), timed.result(), prot.result()
     del graphs
     return out
 
@@ -542,7 +611,7 @@ def dominant_kernel(info, nb, cached, combine):
     return "combine", "k_combine"
 
 
-def measure_workload(name, args):
+def measure_workload(name, args, clock):
     """Every GPU figure of one workload, measured in this process."""
     import torch
     inst = gen.instance_by_name(name)
@@ -558,15 +627,16 @@ def measure_workload(name, args):
     info = sets[0].buf.round_info()
     # the five-block protocol beside the timed steps: five blocks of
     # protocol_block rounds after 64 warmup rounds
-    (hot_us, hot_blocks), (prot_hot_us, _) = time_rounds(sets, 1, args.steps, args.warmup,
-                                                         5 * args.protocol_block, gmax=gmax)
+    (hot_us, hot_blocks), (hot_ev_us, _), (prot_hot_us, _) = time_rounds(
+        sets, 1, args.steps, args.warmup, 5 * args.protocol_block, gmax=gmax, clock=clock)
     for _ in range(S - 1):
         sets.append(RoundSet(inst, view, args.combine, args.cached, args.dispatch))
-    (cold_us, cold_blocks), (prot_us, prot_blocks) = time_rounds(sets, S, args.steps, args.warmup,
-                                                                 5 * args.protocol_block, gmax=gmax)
-    print(f"[bench] {name}: cold {cold_us:.3f} us/round ({args.steps} rounds), hot {hot_us:.3f}; "
-          f"protocol cold {prot_us:.3f} (blocks {', '.join(f'{u:.3f}' for u in prot_blocks)}), "
-          f"hot {prot_hot_us:.3f}", file=sys.stderr, flush=True)
+    (cold_us, cold_blocks), (cold_ev_us, cold_ev_blocks), (prot_us, prot_blocks) = time_rounds(
+        sets, S, args.steps, args.warmup, 5 * args.protocol_block, gmax=gmax, clock=clock)
+    print(f"[bench] {name}: cold {cold_us:.3f} us/round ({args.steps} rounds; events around the graph "
+          f"{cold_ev_us:.3f}), hot {hot_us:.3f}; protocol cold {prot_us:.3f} "
+          f"(blocks {', '.join(f'{u:.3f}' for u in prot_blocks)}), hot {prot_hot_us:.3f}",
+          file=sys.stderr, flush=True)
     kern = time_kernels_live(sets)
     expert_us = time_identity_experts(sets[0])
     dom, dom_name = dominant_kernel(info, nb, args.cached, args.combine)
@@ -578,7 +648,10 @@ def measure_workload(name, args):
     res = {
         "us_per_round": cold_us,
         "us_per_round_blocks": cold_blocks,
+        "us_per_round_events": cold_ev_us,
+        "us_per_round_events_blocks": cold_ev_blocks,
         "us_per_round_hot": hot_us,
+        "us_per_round_hot_events": hot_ev_us,
         "us_per_round_hot_blocks": hot_blocks,
         "protocol_us_per_round": prot_us,
         "protocol_us_per_round_blocks": prot_blocks,
@@ -620,9 +693,10 @@ def measure(names, args):
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    out = {"workloads": {}}
+    clock = Clock()
+    out = {"workloads": {}, "clock_hz": clock.hz}
     for name in names:
-        out["workloads"][name] = measure_workload(name, args)
+        out["workloads"][name] = measure_workload(name, args, clock)
     if not args.no_extras:
         out["launch_floor_us_per_round"] = launch_floor()
         out["copy_gbps"] = copy_bandwidth()
@@ -644,6 +718,7 @@ def aggregate(runs, names, args):
         first = rs[0]
         nb = first["bytes_per_round"]
         cold = _median([r["us_per_round"] for r in rs])
+        cold_ev = _median([r["us_per_round_events"] for r in rs])
         hot = _median([r["us_per_round_hot"] for r in rs])
         kern = {k: _median([r["kernels_us"][k] for r in rs]) for k in first["kernels_us"]}
         roof = dict(first["roofline"])
@@ -658,6 +733,12 @@ def aggregate(runs, names, args):
             "us_per_round": round(cold, 3),
             "us_per_round_per_process": [round(r["us_per_round"], 3) for r in rs],
             "us_per_round_blocks": [[round(u, 3) for u in r["us_per_round_blocks"]] for r in rs],
+            # the same rounds timed by HIP events around their graph launch:
+            # also the launch's and the events' fixed cost, spread over the rounds
+            "us_per_round_events": round(cold_ev, 3),
+            "us_per_round_events_per_process": [round(r["us_per_round_events"], 3) for r in rs],
+            "events_minus_stamps_us_per_graph": round((cold_ev - cold) * args.steps /
+                                                      max(1, -(-args.steps // (args.graph_rounds or 64))), 2),
             "gbps": round(gbps, 2),
             "pct_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
             "us_per_round_hot": round(hot, 3),
@@ -796,6 +877,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": top["config"],
         "us_per_round": top["us_per_round"],
+        "us_per_round_events": top["us_per_round_events"],
         "pct_peak": top["pct_peak"],
         "us_per_round_hot": top["us_per_round_hot"],
         "protocol": top["protocol"],

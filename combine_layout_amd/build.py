@@ -3,6 +3,8 @@
   _lib/libafd.so           the library: host core + gfx950 kernels (hipcc)
   _lib/libafd_hostfake.so  the host core over a recording backend (g++), used
                            only by CPU tests of the state machine and checks
+  _lib/libafd_clock.so     device clock stamps for the benchmark's timing
+                           inside captured graphs (hipcc)
 """
 from __future__ import annotations
 
@@ -15,6 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libafd.so")
 FAKE_LIB = os.path.join(LIBDIR, "libafd_hostfake.so")
+CLOCK_LIB = os.path.join(LIBDIR, "libafd_clock.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -54,12 +57,22 @@ def build_fake():
     return FAKE_LIB
 
 
+def build_clock():
+    os.makedirs(LIBDIR, exist_ok=True)
+    tmp = CLOCK_LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, *HIP_FLAGS, os.path.join(CSRC, "afd_clock.hip"), "-o", tmp])
+    os.replace(tmp, CLOCK_LIB)
+    return CLOCK_LIB
+
+
 def build_all():
     build_fake()
     build_lib()
+    build_clock()
 
 
 if __name__ == "__main__":
     build_all()
     print(LIB)
     print(FAKE_LIB)
+    print(CLOCK_LIB)

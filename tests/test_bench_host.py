@@ -23,7 +23,8 @@ def test_dominant_kernel_follows_the_reported_path():
 
 def _fake_run(us, hot, disp, comb):
     return {"workloads": {"2a2f_decode": {
-        "us_per_round": us, "us_per_round_blocks": [us], "us_per_round_hot": hot, "bytes_per_round": 18931712,
+        "us_per_round": us, "us_per_round_blocks": [us], "us_per_round_events": us + 0.6,
+        "us_per_round_hot": hot, "bytes_per_round": 18931712,
         "protocol_us_per_round": us - 1.0, "protocol_us_per_round_blocks": [us - 1.0] * 5,
         "protocol_us_per_round_hot": hot - 1.0, "protocol_block_rounds": 256,
         "kernels_us": {"dispatch": disp, "combine": comb}, "identity_experts_us": 50.0, "dispatch_path": "one_kernel",
@@ -36,9 +37,14 @@ def test_aggregate_takes_medians_and_applies_the_gate():
     class A:
         combine = "once"
         cached = False
+        steps = 20
+        graph_rounds = 0
     runs = [_fake_run(12.0, 10.0, 6.0, 4.0), _fake_run(10.0, 9.0, 5.0, 4.5), _fake_run(11.0, 11.0, 7.0, 5.0)]
     w = bench.aggregate(runs, ["2a2f_decode"], A)["2a2f_decode"]
     assert w["us_per_round"] == 11.0 and w["us_per_round_hot"] == 10.0
+    # the event-timed figure beside the stamped one, and their difference
+    # per graph launch (20 rounds in one graph: 0.6 us per round is 12 us)
+    assert w["us_per_round_events"] == 11.6 and w["events_minus_stamps_us_per_graph"] == 12.0
     assert w["us_per_round_per_process"] == [12.0, 10.0, 11.0]
     assert w["kernels_us"] == {"dispatch": 6.0, "combine": 4.5}
     assert w["roofline"]["avg_launch_us"] == 6.0
