@@ -173,7 +173,7 @@ afd_status afd_query(const afd_config *cfg, int32_t bucket, size_t *workspace_by
 
 /*
  * afd_create (contract page: the Buffer, which owns the exchange's state and
- * storage; "Initialization and close() are ... outside CUDA capture"): make a
+ * storage, and whose set-up and close() happen outside graph capture): make a
  * context over a caller-owned device workspace of at least afd_query bytes
  * (256-byte aligned).  Initialises the workspace's error word and counters
  * with a synchronous device write, so it is not for a capturing stream.  The

@@ -99,7 +99,8 @@ def test_graph_replay_with_inputs_changed_in_place(name):
     replayed with payloads and ids changed in place, inactive choices as -1.
     Replays: two fresh instances; every choice -1; invalid ids (the
     sanitised result, and the sticky first offender); a clean replay (the
-    word stays set: "invalid routes ... including on graph replay"); after
+    word stays set: the contract page has invalid routes caught on graph
+    replays too); after
     clearing it, a clean replay leaves it clear.  Every replay is compared
     with the oracle on the same inputs."""
     import dataclasses
