@@ -144,7 +144,8 @@ WorkspacePlan plan_workspace(const afd_config &c)
     if (c.combine != AFD_COMBINE_ONCE)
         off += a(size_t(c.num_partitions) * ntok * size_t(partial_row_bytes(c.combine, c.hidden)));
     w.tcount = off;
-    off += a(size_t(kLayoutMaxTiles) * tcount_pitch(c.num_experts) * 4);
+    off += a(size_t(kLayoutMaxTiles) * tcount_pitch(c.num_experts) * 4 +
+             size_t(kLayoutMaxTiles + 1) * tcount_pitch(c.num_experts) * 8);
     w.ready = off;
     off += a(size_t(kReadyCopies + kDoneGroups) * kReadyStride * 4);
     w.total = off;
@@ -204,7 +205,7 @@ void build_plan(afd_ctx *c, bool cached)
     // the one-launch dispatch publishes at most kLayoutMaxTiles tile counts,
     // one expert per thread of a workgroup
     p.onepass = g.dispatch == AFD_DISPATCH_ONE_LAUNCH && !cached && !p.empty && !p.fused &&
-                p.nblk <= kLayoutMaxTiles && p.E <= 256;
+                p.nblk <= kLayoutMaxTiles && p.E <= kMaxExpertsOneLaunch;
     p.wait_polls = c->wait_polls;
     for (int s = 0; s < p.N; ++s) p.out[s] = p.F == 1 ? inbox_of(c, s) : c->out_user[s];
     for (int f = 0; f < p.F; ++f) {

@@ -1112,39 +1112,42 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 // ---------------------------------------------------- one-launch dispatch ----
 //
 // Counts first, then the expansion, in one launch (design page, section 16)
-// for rounds of at most kLayoutMaxTiles layout tiles and 256 experts.
-// Workgroups of five wavefronts.  Workgroups 0 .. kLayoutMaxTiles - 1 each
-// count the live choices of one layout tile per expert and publish them as
-// tagged words (tag << 9 | count; a tile holds at most 256 tokens) with
-// device-scope stores; a counting workgroup past the round's last tile
-// publishes zeros, so every launch rewrites every word and a stale word
-// always carries another launch's tag.  Each then adds one to the arrival
-// counter; the one that completes it writes the launch's tag into every
-// copy of the ready flag.
+// for rounds of at most kLayoutMaxTiles layout tiles and
+// kMaxExpertsOneLaunch experts.  Workgroups of five wavefronts.
+// Workgroups 0 .. kLayoutMaxTiles - 1 each count the live choices of one
+// layout tile per expert and publish them as tagged words (tag << 9 |
+// count; a tile holds at most 256 tokens) with device-scope stores,
+// tile-major, so every line is written by one workgroup; a counting
+// workgroup past the round's last tile publishes zeros, so every launch
+// rewrites every word and a stale word always carries another launch's
+// tag.  Each then adds one to an arrival counter.  The one that completes
+// it reads every tile's counts (checking the tags, reading a word again
+// while it is not yet this launch's), and computes every tile's first row
+// per expert (the aligned start of the expert plus its counts in earlier
+// tiles) and the ends, published as tagged 64-bit words; right behind
+// them it sets all copies of a ready flag to the launch's tag.
 // Every other workgroup scatters TB slots of the tiled token space as
 // k_scatter does with its first four wavefronts, which rank their tokens'
 // choices inside their tile themselves (lane masks over the tile's tokens
 // up to their own, as k_layout builds them).  Its fifth wavefront holds no
 // row loads, so its polls are not queued behind them: it polls one copy of
-// the ready flag (eight or so workgroups per copy) until it reads a tag,
-// the one hand-off between workgroups.  The workgroup then reads the
-// tagged words through the caches (a cache holds no copy from before the
-// words were final: kernels start with invalidated caches and no workgroup
-// reads a word before the flag is set), checks every tag against the
-// flag's, and reads again at device scope if one differs.
+// the flag (eight or so workgroups per copy) until it reads a tag, then
+// reads its tile's first rows (and the first workgroup the ends) through
+// the caches, reading a word again at device scope while its tag differs
+// from the flag's.
 // The counting workgroups have the lowest indices and never wait, so the
 // hand-off completes whatever number of workgroups is resident at once.
-// The wait is bounded: past h.wait_polls polls a workgroup sets the sticky
-// gave-up flag, marks its tokens' choices skipped in the slot map (the
-// combine then reads nothing for them), clears ends[] if it is the first,
-// stores no row and exits.  Every workgroup counts itself finished once it
-// no longer reads the counters (a scatter workgroup right after its
-// hand-off, while its stores proceed), in one of several group counters;
-// the last one advances the launch counter and clears the counters and the
-// flags, and stream order shows the next launch the new values.
-// Choices that are not live mark a spare word of their own lane, in the
-// counting histogram as in the rank masks, so idle lanes past a tile's
-// tokens never contend for one LDS address.
+// Every wait is bounded: past h.wait_polls polls a workgroup sets the
+// sticky gave-up flag, marks its tokens' choices skipped in the slot map
+// (the combine then reads nothing for them), clears ends[] if it is the
+// first, stores no row and exits.  Every workgroup counts itself finished
+// once it no longer reads the counters or flags (a scatter workgroup right
+// after its hand-off, while its stores proceed), in one of several group
+// counters; the last one advances the launch counter and clears the
+// counters and the flags, and stream order shows the next launch the new
+// values.  Choices that are not live mark a spare word of their own lane,
+// in the counting histogram as in the rank masks, so idle lanes past a
+// tile's tokens never contend for one LDS address.
 
 constexpr int kTagShift = 9;
 constexpr uint32_t kTagMask = 0x7FFFFFu;
@@ -1244,26 +1247,91 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
         for (int e = tid; e < E; e += kD1Threads)
             __hip_atomic_store(&h.tcount[b * tcount_pitch(E) + e], (tag << kTagShift) | uint32_t(hist[e]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every wavefront's count stores acknowledged, then the barrier: the
-        // workgroup's counts are in memory before its arrival (readers check
-        // the tags anyway, so no release fence, an L2 write-back, is needed)
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // every wavefront's count stores issued, then the arrival: the last
+        // arrival's reader checks every tag and reads a word that is not yet
+        // this launch's again, so neither a wait for the stores nor a
+        // release fence (an L2 write-back) is needed before it
         lds_barrier();
-        if (wave == 0) {
-            uint32_t r = 0;
-            if (lane == 0)
-                r = __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            r = uint32_t(__builtin_amdgcn_readfirstlane(int(r)));
-            if (r + 1u == uint32_t(kLayoutMaxTiles)) {
-                // the last arrival: every tile's counts are in memory, so set
-                // every copy of the ready flag to this launch's tag, and wait
-                // for those stores before counting this workgroup finished
+        __shared__ int s_last, s_bad;
+        if (tid == 0) {
+            const uint32_t r =
+                __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = r + 1u == uint32_t(kLayoutMaxTiles);
+            s_bad = 0;
+        }
+        lds_barrier();
+        if (s_last) {
+            // The last arrival: every tile's counts are in memory.  Thread e
+            // reads expert e's count in every tile through the caches
+            // (checking the tags; device scope again if one differs,
+            // bounded), and the workgroup turns them into every tile's first
+            // row per expert and the partition-local ends, published as
+            // tagged 64-bit words (tag << 32 | value) for the scatter
+            // workgroups; then the ready flag.
+            const int pitch = tcount_pitch(E);
+            int *A = hist + E + kWave;            // [E] aligned counts, then their exclusive prefix
+            uint32_t cw[kLayoutMaxTiles];
+            int C = 0;
+            if (tid < E) {
+                const gptr<const uint32_t> col = (gptr<const uint32_t>)h.tcount + tid;
+#pragma unroll
+                for (int bb = 0; bb < kLayoutMaxTiles; ++bb) cw[bb] = col[bb * pitch];
+                bool fresh = true;
+#pragma unroll
+                for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                    fresh = fresh && (bb >= nblk || (cw[bb] >> kTagShift) == tag);
+                for (int it = 0; !fresh; ++it) {
+                    if (it > h.wait_polls) {
+                        s_bad = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                    for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                        cw[bb] = __hip_atomic_load(&h.tcount[bb * pitch + tid], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    fresh = true;
+#pragma unroll
+                    for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                        fresh = fresh && (bb >= nblk || (cw[bb] >> kTagShift) == tag);
+                }
+#pragma unroll
+                for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                    C += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
+                A[tid] = align_up_i(C, h.alpha);
+            }
+            lds_barrier();
+            block_exclusive_scan(A, E);
+            if (tid < E && !s_bad) {
+                const gptr<unsigned long long> tb = (gptr<unsigned long long>)(h.tcount + kLayoutMaxTiles * pitch);
+                const int start = A[tid] - A[part_of(tid, h.E_loc) * h.E_loc];
+                const unsigned long long tg = uint64_t(tag) << 32;
+                int run = start;
+#pragma unroll
+                for (int bb = 0; bb < kLayoutMaxTiles; ++bb) {
+                    __hip_atomic_store(&tb[bb * pitch + tid], tg | uint32_t(run), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    run += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
+                }
+                __hip_atomic_store(&tb[kLayoutMaxTiles * pitch + tid], tg | uint32_t(start + C), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // the flag right behind the bases, without waiting for them: a
+            // scatter workgroup that reads a base before it lands sees
+            // another launch's tag and reads it again
+            if (s_bad) {
+                if (tid == 0)
+                    __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (wave == 0) {
                 for (int c = lane; c < kReadyCopies; c += kWave)
                     __hip_atomic_store(&h.ready[c * kReadyStride], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
-            if (lane == 0) onepass_done(h);
         }
+        // counted finished once its flag stores (if any) are acknowledged: the
+        // last finished workgroup clears the flags for the next launch, and a
+        // flag store still in flight must not land after that
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        if (wave == 0 && lane == 0) onepass_done(h);
         return;
     }
 
@@ -1274,14 +1342,12 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
     constexpr int HW = kD1Waves - 1;             // the hand-off wavefront
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     __shared__ int s_gaveup;
-    __shared__ uint32_t s_tag;
     const int MS = E + kWave;                    // lane masks per expert, then a spare per lane
     unsigned long long *mask = reinterpret_cast<unsigned long long *>(lds);   // [4][E + 64]
     int *pre = reinterpret_cast<int *>(mask + 4 * MS);                        // [4][E]
     int *pkl = pre + 4 * E;                                                   // [TB][K] (expert << 16 | rank), -1
-    int *base = pkl + TB * K;                                                 // [E]
-    int *A = base + E;                                                        // [E]
-    int *Cs = A + E;                                                          // [E]
+    int *base = pkl + TB * K;                                                 // [E] this tile's first row per expert
+    int *Cs = base + E;                                                       // [E] ends (first workgroup)
     const int nvec = h.nvec;
     const int jb = blockIdx.x - kLayoutMaxTiles;
     const int v_first = jb * TB;                 // first slot of the tiled token space
@@ -1368,7 +1434,12 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
     // 3. the hand-off: wavefront 4, which has no loads of its own in flight
     // (its polls do not queue behind the rows), polls this workgroup's copy
     // of the ready flag until it holds a launch's tag (bounded; every lane
-    // reads the same word, one request per poll)
+    // reads the same word, one request per poll), then reads this tile's
+    // first row of every expert (and, in the first workgroup, the ends)
+    // through the caches, lane l taking experts l, l + 64, ...; a word whose
+    // tag differs from the flag's is read again at device scope (bounded).
+    // No cache holds a copy from before the words were final: kernels start
+    // with invalidated caches and nothing reads a word before the flag.
     if (wave == HW) {
         const gptr<uint32_t> rf = h.ready + (jb % kReadyCopies) * kReadyStride;
         uint32_t tg = 0;
@@ -1378,47 +1449,47 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
             __builtin_amdgcn_s_sleep(1);
         }
         tg = uint32_t(__builtin_amdgcn_readfirstlane(int(tg)));
-        if (lane == 0) {
-            s_tag = tg;
-            if (tg == 0u) s_gaveup = 1;
+        bool gave = tg == 0u;
+        // nothing below is moved above the poll
+        asm volatile("" ::: "memory");
+        if (!gave) {
+            static_assert(kMaxExpertsOneLaunch <= 4 * kWave, "four experts per lane");
+            const int pitch = tcount_pitch(E);
+            const gptr<unsigned long long> tb = (gptr<unsigned long long>)(h.tcount + kLayoutMaxTiles * pitch);
+            const int nrow = jb == 0 ? 2 : 1;      // this tile's bases; the ends row for the first workgroup
+            unsigned long long w[2][4];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int e = q * kWave + lane < E ? q * kWave + lane : E - 1;
+                    const int row = r == 0 ? tile : kLayoutMaxTiles;
+                    w[r][q] = (r < nrow && q * kWave < E) ? ((gptr<const unsigned long long>)tb)[row * pitch + e] : 0ull;
+                }
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (r >= nrow || q * kWave >= E) continue;
+                    const int e = q * kWave + lane < E ? q * kWave + lane : E - 1;
+                    const int row = r == 0 ? tile : kLayoutMaxTiles;
+                    for (int it = 0; uint32_t(w[r][q] >> 32) != tg; ++it) {
+                        if (it > h.wait_polls) {
+                            gave = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                        w[r][q] = __hip_atomic_load(&tb[row * pitch + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    if (q * kWave + lane < E) (r == 0 ? base : Cs)[q * kWave + lane] = int(uint32_t(w[r][q]));
+                }
+            gave = __builtin_amdgcn_ballot_w64(gave) != 0;
         }
-    }
-    lds_barrier();
-    // nothing below is moved above the hand-off
-    asm volatile("" ::: "memory");
-    // thread e reads expert e's word of every tile through the caches (a
-    // wavefront's lanes read consecutive words; no cache holds a copy from
-    // before the words were final) and checks that every one of the round's
-    // tiles carries the flag's tag; otherwise it reads them again at device
-    // scope (bounded)
-    uint32_t cw[kLayoutMaxTiles];
-    const uint32_t tag = s_tag;
-    if (tid < E && !s_gaveup) {
-        const int pitch = tcount_pitch(E);
-        const gptr<const uint32_t> col = (gptr<const uint32_t>)h.tcount + tid;
-#pragma unroll
-        for (int b = 0; b < kLayoutMaxTiles; ++b) cw[b] = col[b * pitch];
-        bool fresh = true;
-#pragma unroll
-        for (int b = 0; b < kLayoutMaxTiles; ++b) fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
-        for (int it = 0; !fresh; ++it) {
-            if (it > h.wait_polls) {
-                s_gaveup = 1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-            for (int b = 0; b < kLayoutMaxTiles; ++b)
-                cw[b] = __hip_atomic_load(&h.tcount[b * pitch + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            fresh = true;
-#pragma unroll
-            for (int b = 0; b < kLayoutMaxTiles; ++b)
-                fresh = fresh && (b >= nblk || (cw[b] >> kTagShift) == tag);
-        }
+        if (lane == 0 && gave) s_gaveup = 1;
     }
     lds_barrier();
     if (s_gaveup) {
-        // no counts: this workgroup's choices are skipped, nothing is stored
+        // no bases: this workgroup's choices are skipped, nothing is stored
         if (tid == 0) __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (wave < HW) {
 #pragma unroll
@@ -1437,28 +1508,8 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
         if (wave == HW && lane == 0) onepass_done(h);
         return;
     }
-
-    // 4. this tile's first row of every expert (as k_scatter)
-    for (int e = tid; e < E; e += kD1Threads) {
-        int C = 0, before = 0;
-#pragma unroll
-        for (int b = 0; b < kLayoutMaxTiles; ++b) {
-            const int c = b < nblk ? int(cw[b] & ((1u << kTagShift) - 1u)) : 0;
-            C += c;
-            before += b < tile ? c : 0;
-        }
-        A[e] = align_up_i(C, h.alpha);
-        Cs[e] = C;
-        base[e] = before;
-    }
-    lds_barrier();
-    block_exclusive_scan(A, E);
-    for (int e = tid; e < E; e += kD1Threads) {
-        const int start = A[e] - A[(e / h.E_loc) * h.E_loc];
-        base[e] += start;
-        if (jb == 0) h.ends[e] = start + Cs[e];
-    }
-    lds_barrier();
+    if (jb == 0)
+        for (int e = tid; e < E; e += kD1Threads) h.ends[e] = Cs[e];
     if (wave == HW) {
         // the counters and flags are no longer read by this workgroup
         if (lane == 0) onepass_done(h);
@@ -2304,8 +2355,9 @@ template <int VMAX>
 int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 4 ? 1 : 4 / VMAX);
-    const size_t scatter_lds = size_t(4) * (E + kWave) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(3) * E * 4;
-    const size_t lds = scatter_lds > size_t(E + kWave) * 4 ? scatter_lds : size_t(E + kWave) * 4;
+    const size_t scatter_lds = size_t(4) * (E + kWave) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(2) * E * 4;
+    const size_t count_lds = size_t(2 * E + kWave) * 4;   // counts and lane spares, then the aligned scan
+    const size_t lds = scatter_lds > count_lds ? scatter_lds : count_lds;
     const dim3 grid(kLayoutMaxTiles + nslots / TB);
     if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(kD1Threads), lds, st, a);

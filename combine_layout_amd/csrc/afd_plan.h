@@ -56,6 +56,9 @@ constexpr int kReadyStride = 32;   // uint32 words between copies (and between g
 // its own after the flag copies; the last of a group counts the group in
 // the workspace's finished-group word.
 constexpr int kDoneGroups = 16;
+// Experts of a round the one-launch dispatch takes (its hand-off reads four
+// experts' words per lane of one wavefront).
+constexpr int kMaxExpertsOneLaunch = 256;
 // Words between consecutive tiles' runs of the one-launch dispatch's tile
 // counts (tile-major, each run on whole 128-byte lines).
 #ifdef __HIPCC__
@@ -99,7 +102,9 @@ struct WorkspacePlan {
                            // bytes of slack (the combine reads slots 64 bytes at a time)
     size_t inbox = 0;      // BF16 [N][capacity][H] (one partition only)
     size_t partials = 0;   // per-stage combine: [F][N][capacity] rows of partial_row_bytes
-    size_t tcount = 0;     // one-launch dispatch: uint32 [kLayoutMaxTiles][tcount_pitch(E)] tagged tile counts
+    size_t tcount = 0;     // one-launch dispatch: uint32 [kLayoutMaxTiles][tcount_pitch(E)] tagged tile counts,
+                           // then uint64 [kLayoutMaxTiles + 1][tcount_pitch(E)] tagged first rows per tile and
+                           // expert, and the ends
     size_t ready = 0;      // one-launch dispatch: uint32 ready flag, kReadyCopies copies kReadyStride apart,
                            // then kDoneGroups finished-workgroup counters at the same stride
     size_t total = 0;
