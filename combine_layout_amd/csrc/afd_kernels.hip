@@ -1117,15 +1117,14 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 // Workgroups 0 .. kLayoutMaxTiles - 1 each count the live choices of one
 // layout tile per expert and publish them as tagged words (tag << 9 |
 // count; a tile holds at most 256 tokens) with device-scope stores,
-// tile-major, so every line is written by one workgroup; a counting
-// workgroup past the round's last tile publishes zeros, so every launch
-// rewrites every word and a stale word always carries another launch's
-// tag.  Each then adds one to an arrival counter.  The one that completes
-// it reads every tile's counts (checking the tags, reading a word again
-// while it is not yet this launch's), and computes every tile's first row
-// per expert (the aligned start of the expert plus its counts in earlier
-// tiles) and the ends, published as tagged 64-bit words; right behind
-// them it sets all copies of a ready flag to the launch's tag.
+// tile-major; a counting workgroup past the round's last tile publishes
+// zeros, so every launch rewrites every word and a stale word always
+// carries another launch's tag.  Workgroup kLayoutMaxTiles, the finisher,
+// polls those words at device scope until every tile of the round carries
+// the launch's tag, computes every tile's first row per expert (the
+// aligned start of the expert plus its counts in earlier tiles) and the
+// ends, publishes them as tagged 64-bit words, and right behind them sets
+// all copies of a ready flag to the launch's tag.
 // Every other workgroup scatters TB slots of the tiled token space as
 // k_scatter does with its first four wavefronts, which rank their tokens'
 // choices inside their tile themselves (lane masks over the tile's tokens
@@ -1135,19 +1134,20 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 // reads its tile's first rows (and the first workgroup the ends) through
 // the caches, reading a word again at device scope while its tag differs
 // from the flag's.
-// The counting workgroups have the lowest indices and never wait, so the
-// hand-off completes whatever number of workgroups is resident at once.
-// Every wait is bounded: past h.wait_polls polls a workgroup sets the
-// sticky gave-up flag, marks its tokens' choices skipped in the slot map
-// (the combine then reads nothing for them), clears ends[] if it is the
-// first, stores no row and exits.  Every workgroup counts itself finished
-// once it no longer reads the counters or flags (a scatter workgroup right
-// after its hand-off, while its stores proceed), in one of several group
-// counters; the last one advances the launch counter and clears the
-// counters and the flags, and stream order shows the next launch the new
-// values.  Choices that are not live mark a spare word of their own lane,
-// in the counting histogram as in the rank masks, so idle lanes past a
-// tile's tokens never contend for one LDS address.
+// The counting workgroups have the lowest indices and never wait, and the
+// finisher waits only for them, so the hand-off completes whatever number
+// of workgroups is resident at once.  Every wait is bounded: past
+// h.wait_polls polls a workgroup sets the sticky gave-up flag, marks its
+// tokens' choices skipped in the slot map (the combine then reads nothing
+// for them), clears ends[] if it is the first, stores no row and exits.
+// Every workgroup counts itself finished once it no longer reads the
+// counters or flags (a scatter workgroup right after its hand-off, while
+// its stores proceed), in one of several group counters; the last one
+// advances the launch counter and clears the counters and the flags, and
+// stream order shows the next launch the new values.  Choices that are not
+// live mark a spare word of their own lane, in the counting histogram as
+// in the rank masks, so idle lanes past a tile's tokens never contend for
+// one LDS address.
 
 constexpr int kTagShift = 9;
 constexpr uint32_t kTagMask = 0x7FFFFFu;
@@ -1176,7 +1176,6 @@ __device__ __forceinline__ void onepass_done(const Hdr &h)
     for (int c = 0; c < kReadyCopies + kDoneGroups; ++c)
         __hip_atomic_store(&h.ready[c * kReadyStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&h.sync[kSyncDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&h.sync[kSyncArrive], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&h.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1247,89 +1246,79 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
         for (int e = tid; e < E; e += kD1Threads)
             __hip_atomic_store(&h.tcount[b * tcount_pitch(E) + e], (tag << kTagShift) | uint32_t(hist[e]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every wavefront's count stores issued, then the arrival: the last
-        // arrival's reader checks every tag and reads a word that is not yet
-        // this launch's again, so neither a wait for the stores nor a
-        // release fence (an L2 write-back) is needed before it
+        // counted finished right away: its stores land before the launch
+        // ends, and the finisher reads every word until it carries this
+        // launch's tag
+        if (wave == 0 && lane == 0) onepass_done(h);
+        return;
+    }
+
+    if (blockIdx.x == kLayoutMaxTiles) {
+        // ---- the finisher: thread e polls expert e's tagged word of every
+        // tile at device scope until all of the round's tiles carry this
+        // launch's tag (bounded), then the workgroup turns the counts into
+        // every tile's first row per expert (the expert's aligned start plus
+        // its counts in earlier tiles) and the partition-local ends,
+        // published as tagged 64-bit words (tag << 32 | value), and right
+        // behind them sets every copy of the ready flag to the tag
+        const uint32_t tag =
+            launch_tag(__hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        __shared__ int s_bad;
+        int *A = reinterpret_cast<int *>(lds);    // [E] aligned counts, then their exclusive prefix
+        if (tid == 0) s_bad = 0;
         lds_barrier();
-        __shared__ int s_last, s_bad;
-        if (tid == 0) {
-            const uint32_t r =
-                __hip_atomic_fetch_add(&h.sync[kSyncArrive], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_last = r + 1u == uint32_t(kLayoutMaxTiles);
-            s_bad = 0;
-        }
-        lds_barrier();
-        if (s_last) {
-            // The last arrival: every tile's counts are in memory.  Thread e
-            // reads expert e's count in every tile through the caches
-            // (checking the tags; device scope again if one differs,
-            // bounded), and the workgroup turns them into every tile's first
-            // row per expert and the partition-local ends, published as
-            // tagged 64-bit words (tag << 32 | value) for the scatter
-            // workgroups; then the ready flag.
-            const int pitch = tcount_pitch(E);
-            int *A = hist + E + kWave;            // [E] aligned counts, then their exclusive prefix
-            uint32_t cw[kLayoutMaxTiles];
-            int C = 0;
-            if (tid < E) {
-                const gptr<const uint32_t> col = (gptr<const uint32_t>)h.tcount + tid;
+        const int pitch = tcount_pitch(E);
+        uint32_t cw[kLayoutMaxTiles];
+        int C = 0;
+        if (tid < E) {
+            for (int it = 0;; ++it) {
+                if (it > h.wait_polls) {
+                    s_bad = 1;
+                    break;
+                }
 #pragma unroll
-                for (int bb = 0; bb < kLayoutMaxTiles; ++bb) cw[bb] = col[bb * pitch];
+                for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                    cw[bb] = __hip_atomic_load(&h.tcount[bb * pitch + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 bool fresh = true;
 #pragma unroll
                 for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
                     fresh = fresh && (bb >= nblk || (cw[bb] >> kTagShift) == tag);
-                for (int it = 0; !fresh; ++it) {
-                    if (it > h.wait_polls) {
-                        s_bad = 1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-                    for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
-                        cw[bb] = __hip_atomic_load(&h.tcount[bb * pitch + tid], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                    fresh = true;
-#pragma unroll
-                    for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
-                        fresh = fresh && (bb >= nblk || (cw[bb] >> kTagShift) == tag);
-                }
-#pragma unroll
-                for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
-                    C += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
-                A[tid] = align_up_i(C, h.alpha);
+                if (fresh) break;
+                __builtin_amdgcn_s_sleep(1);
             }
-            lds_barrier();
-            block_exclusive_scan(A, E);
-            if (tid < E && !s_bad) {
-                const gptr<unsigned long long> tb = (gptr<unsigned long long>)(h.tcount + kLayoutMaxTiles * pitch);
-                const int start = A[tid] - A[part_of(tid, h.E_loc) * h.E_loc];
-                const unsigned long long tg = uint64_t(tag) << 32;
-                int run = start;
 #pragma unroll
-                for (int bb = 0; bb < kLayoutMaxTiles; ++bb) {
-                    __hip_atomic_store(&tb[bb * pitch + tid], tg | uint32_t(run), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    run += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
-                }
-                __hip_atomic_store(&tb[kLayoutMaxTiles * pitch + tid], tg | uint32_t(start + C), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-            // the flag right behind the bases, without waiting for them: a
-            // scatter workgroup that reads a base before it lands sees
-            // another launch's tag and reads it again
-            if (s_bad) {
-                if (tid == 0)
-                    __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else if (wave == 0) {
-                for (int c = lane; c < kReadyCopies; c += kWave)
-                    __hip_atomic_store(&h.ready[c * kReadyStride], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            for (int bb = 0; bb < kLayoutMaxTiles; ++bb)
+                C += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
+            A[tid] = align_up_i(C, h.alpha);
         }
-        // counted finished once its flag stores (if any) are acknowledged: the
-        // last finished workgroup clears the flags for the next launch, and a
-        // flag store still in flight must not land after that
+        lds_barrier();
+        block_exclusive_scan(A, E);
+        if (tid < E && !s_bad) {
+            const gptr<unsigned long long> tb = (gptr<unsigned long long>)(h.tcount + kLayoutMaxTiles * pitch);
+            const int start = A[tid] - A[part_of(tid, h.E_loc) * h.E_loc];
+            const unsigned long long tg = uint64_t(tag) << 32;
+            int run = start;
+#pragma unroll
+            for (int bb = 0; bb < kLayoutMaxTiles; ++bb) {
+                __hip_atomic_store(&tb[bb * pitch + tid], tg | uint32_t(run), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                run += bb < nblk ? int(cw[bb] & ((1u << kTagShift) - 1u)) : 0;
+            }
+            __hip_atomic_store(&tb[kLayoutMaxTiles * pitch + tid], tg | uint32_t(start + C), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the flag right behind the bases, without waiting for them: a
+        // scatter workgroup that reads a base before it lands sees another
+        // launch's tag and reads it again
+        if (s_bad) {
+            if (tid == 0) __hip_atomic_store(&h.sync[kSyncStall], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (wave == 0) {
+            for (int c = lane; c < kReadyCopies; c += kWave)
+                __hip_atomic_store(&h.ready[c * kReadyStride], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // counted finished once its flag stores are acknowledged: the last
+        // finished workgroup clears the flags for the next launch, and a flag
+        // store still in flight must not land after that
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (wave == 0 && lane == 0) onepass_done(h);
         return;
@@ -1349,7 +1338,7 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
     int *base = pkl + TB * K;                                                 // [E] this tile's first row per expert
     int *Cs = base + E;                                                       // [E] ends (first workgroup)
     const int nvec = h.nvec;
-    const int jb = blockIdx.x - kLayoutMaxTiles;
+    const int jb = blockIdx.x - kLayoutMaxTiles - 1;
     const int v_first = jb * TB;                 // first slot of the tiled token space
     const int tile = v_first / h.tile;
     const SourceRec src = load_source(a, source_of_tiled(a, h.N, v_first));
@@ -2349,8 +2338,8 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
     return launched_ok();
 }
 
-// One-launch dispatch: kLayoutMaxTiles counting workgroups, then one
-// scatter workgroup per TB slots of the tiled token space.
+// One-launch dispatch: kLayoutMaxTiles counting workgroups, the finisher,
+// then one scatter workgroup per TB slots of the tiled token space.
 template <int VMAX>
 int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, hipStream_t st)
 {
@@ -2358,7 +2347,7 @@ int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, 
     const size_t scatter_lds = size_t(4) * (E + kWave) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(2) * E * 4;
     const size_t count_lds = size_t(2 * E + kWave) * 4;   // counts and lane spares, then the aligned scan
     const size_t lds = scatter_lds > count_lds ? scatter_lds : count_lds;
-    const dim3 grid(kLayoutMaxTiles + nslots / TB);
+    const dim3 grid(kLayoutMaxTiles + 1 + nslots / TB);
     if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     return launched_ok();

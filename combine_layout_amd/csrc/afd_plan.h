@@ -39,12 +39,10 @@ constexpr uint64_t kNoError = ~0ull;
 
 // The workspace's first 256 bytes: the route-error word at 0, and the
 // one-launch dispatch's words (uint32) at byte 64: launch counter at index
-// 0, finished workgroup groups at 16, the sticky gave-up flag at 32,
-// published tiles at 40.
+// 0, finished workgroup groups at 16, the sticky gave-up flag at 32.
 constexpr size_t kSyncOffset = 64;
 constexpr int kSyncDone = 16;
 constexpr int kSyncStall = 32;
-constexpr int kSyncArrive = 40;
 constexpr int kDefaultWaitPolls = 1000000;
 // The one-launch dispatch's ready flag, in this many copies one 128-byte
 // line apart, so that the scatter workgroups' polls spread over many lines
