@@ -2,8 +2,9 @@
 C ABI) against the CPU oracle.
 
 Counts first, then the expansion, in one launch (design page, section 16):
-the first 32 workgroups publish per-tile expert counts, the others rank
-their tokens inside their tile themselves and wait for the counts.  The
+the first 32 workgroups publish per-tile expert counts, a finisher turns
+them into every tile's first rows, and the others rank their tokens inside
+their tile themselves and wait for those rows.  The
 layout must be the same as the split path's: bit-exact ends, rows, scales,
 row weights, and the combine to the usual bar.  Also: route errors found by
 the counting workgroups, sequences of rounds whose tile counts change (every
@@ -51,19 +52,24 @@ def test_one_launch_workloads(name):
     assert buf.get_error(with_status=True)[1] == 0
 
 
-# (seed, tokens per source, H, K, dtype): tiles of 64, 128 and 256 tokens,
-# ragged and empty sources, top-k above 8, wide rows, FP8
+# (seed, tokens per source, H, K, dtype[, E, F]): tiles of 64, 128 and 256
+# tokens, ragged and empty sources, top-k above 8, wide rows, FP8; expert
+# counts that are not a multiple of the 32-word table pitch, and up to the
+# one-launch limit of 256 experts (the hand-off wavefront then reads four
+# experts' words per lane)
 CASES = [(0, [600, 0, 41], 512, 8, "bf16"), (1, [1000, 1000], 256, 12, "bf16"), (2, [513], 1024, 4, "fp8"),
          (3, [3000, 2000, 3000], 256, 2, "bf16"), (4, [700], 8448, 8, "bf16"), (5, [2048, 2048], 2048, 32, "fp8"),
-         (6, [4096, 4096], 256, 8, "bf16")]
+         (6, [4096, 4096], 256, 8, "bf16"), (7, [1500, 700], 512, 8, "bf16", 256, 4),
+         (8, [900, 37], 512, 6, "fp8", 200, 5)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"c{c[0]}")
 def test_one_launch_random(case):
     h = _gpu()
-    i, T, H, K, dtype = case
-    E = 64 if K <= 8 else 128
-    inst = gen.random_small(1500 + i, N=len(T), F=2 + i % 3, E=E - E % (2 + i % 3), K=K, alpha=[1, 16, 128][i % 3],
+    i, T, H, K, dtype = case[:5]
+    F = case[6] if len(case) > 5 else 2 + i % 3
+    E = case[5] if len(case) > 5 else (64 if K <= 8 else 128) - (64 if K <= 8 else 128) % F
+    inst = gen.random_small(1500 + i, N=len(T), F=F, E=E, K=K, alpha=[1, 16, 128][i % 3],
                             T=T, H=H, p_skip=0.1, dtype=dtype, bucket=max(T))
     buf = _buf(h, inst)
     print(f"[one launch] c{i} T={T} H={H} K={K} {dtype}", flush=True)
