@@ -97,13 +97,14 @@ typedef enum { AFD_COMBINE_ONCE = 0, AFD_COMBINE_PER_STAGE = 1, AFD_COMBINE_PER_
  *   AFD_DISPATCH_AUTO        the library chooses (currently AFD_DISPATCH_SPLIT)
  *   AFD_DISPATCH_SPLIT       a layout kernel over token tiles, then the scatter
  *   AFD_DISPATCH_ONE_LAUNCH  one launch: its first 32 workgroups count one
- *                            tile each and publish the counts; every other
- *                            workgroup ranks its tokens inside their tile
- *                            itself, waits for the published counts (the one
- *                            hand-off between workgroups, a bounded wait) and
- *                            scatters.  Applies to rounds of at most 32
- *                            tiles (8192 token slots) and 256 experts; other
- *                            rounds take the split path.
+ *                            tile each and publish the counts; the next one
+ *                            waits for them and publishes every tile's
+ *                            first row per expert; every other workgroup
+ *                            ranks its tokens inside their tile itself,
+ *                            waits for its tile's first rows (bounded waits
+ *                            throughout) and scatters.  Applies to rounds of
+ *                            at most 32 tiles (8192 token slots) and 256
+ *                            experts; other rounds take the split path.
  */
 typedef enum { AFD_DISPATCH_AUTO = 0, AFD_DISPATCH_SPLIT = 1, AFD_DISPATCH_ONE_LAUNCH = 2 } afd_dispatch_mode;
 
@@ -326,7 +327,8 @@ afd_status afd_source_collect(afd_ctx *ctx, int32_t s, int32_t view, const void 
 
 /*
  * afd_set_dispatch_wait: the number of polls a workgroup of a one-launch
- * dispatch makes for the published tile counts before it gives up (default
+ * dispatch makes for what another workgroup publishes (the tile counts, or
+ * its tile's first rows) before it gives up (default
  * 1,000,000, about a second; a negative value gives up at once).  A
  * workgroup that gives up stores no rows and marks its tokens' choices as
  * skipped, so the round's outputs are defined (its tokens' outputs are +0);
