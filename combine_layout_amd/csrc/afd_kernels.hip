@@ -1113,41 +1113,43 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a)
 //
 // Counts first, then the expansion, in one launch (design page, section 16)
 // for rounds of at most kLayoutMaxTiles layout tiles and
-// kMaxExpertsOneLaunch experts.  Workgroups of five wavefronts.
-// Workgroups 0 .. kLayoutMaxTiles - 1 each count the live choices of one
-// layout tile per expert and publish them as tagged words (tag << 9 |
-// count; a tile holds at most 256 tokens) with device-scope stores,
-// tile-major; a counting workgroup past the round's last tile publishes
-// zeros, so every launch rewrites every word and a stale word always
-// carries another launch's tag.  Workgroup kLayoutMaxTiles, the finisher,
-// polls those words at device scope until every tile of the round carries
-// the launch's tag, computes every tile's first row per expert (the
-// aligned start of the expert plus its counts in earlier tiles) and the
-// ends, publishes them as tagged 64-bit words, and right behind them sets
-// all copies of a ready flag to the launch's tag.
-// Every other workgroup scatters TB slots of the tiled token space as
-// k_scatter does with its first four wavefronts, which rank their tokens'
-// choices inside their tile themselves (lane masks over the tile's tokens
-// up to their own, as k_layout builds them).  Its fifth wavefront holds no
-// row loads, so its polls are not queued behind them: it polls one copy of
-// the flag (eight or so workgroups per copy) until it reads a tag, then
-// reads its tile's first rows (and the first workgroup the ends) through
-// the caches, reading a word again at device scope while its tag differs
-// from the flag's.
-// The counting workgroups have the lowest indices and never wait, and the
-// finisher waits only for them, so the hand-off completes whatever number
-// of workgroups is resident at once.  Every wait is bounded: past
-// h.wait_polls polls a workgroup sets the sticky gave-up flag, marks its
-// tokens' choices skipped in the slot map (the combine then reads nothing
-// for them), clears ends[] if it is the first, stores no row and exits.
-// Every workgroup counts itself finished once it no longer reads the
-// counters or flags (a scatter workgroup right after its hand-off, while
-// its stores proceed), in one of several group counters; the last one
-// advances the launch counter and clears the counters and the flags, and
-// stream order shows the next launch the new values.  Choices that are not
-// live mark a spare word of their own lane, in the counting histogram as
-// in the rank masks, so idle lanes past a tile's tokens never contend for
-// one LDS address.
+// kMaxExpertsOneLaunch experts.  One workgroup of five wavefronts per TB
+// slots of the tiled token space, as k_scatter has (at least
+// kLayoutMaxTiles + 1), so the grid fits the GPU as the split path's
+// scatter does.  Before its own slots, workgroup b < kLayoutMaxTiles counts
+// the live choices of layout tile b per expert and publishes them as
+// tagged words (tag << 9 | count; a tile holds at most 256 tokens) with
+// device-scope stores, tile-major; a workgroup past the round's last tile
+// publishes zeros, so every launch rewrites every word and a stale word
+// always carries another launch's tag.  Workgroup kLayoutMaxTiles, the
+// finisher, polls those words at device scope until every tile of the
+// round carries the launch's tag, computes every tile's first row per
+// expert (the aligned start of the expert plus its counts in earlier
+// tiles) and the ends, publishes them as tagged 64-bit words, and right
+// behind them sets all copies of a ready flag to the launch's tag.
+// Every workgroup then scatters its slots as k_scatter does with its first
+// four wavefronts, which rank their tokens' choices inside their tile
+// themselves (lane masks over the tile's tokens up to their own, as
+// k_layout builds them).  Its fifth wavefront holds no row loads, so its
+// polls are not queued behind them: it polls one copy of the flag (eight
+// or so workgroups per copy) until it reads a tag, then reads its tile's
+// first rows (and the first workgroup the ends) through the caches,
+// reading a word again at device scope while its tag differs from the
+// flag's.
+// The counting duties never wait and the finisher waits only for them;
+// all of them belong to the lowest block indices, so the hand-off completes
+// whatever number of workgroups is resident at once.  Every wait is
+// bounded: past h.wait_polls polls a workgroup sets the sticky gave-up
+// flag, marks its tokens' choices skipped in the slot map (the combine then
+// reads nothing for them), clears ends[] if it is the first, stores no row
+// and exits.  Every workgroup counts itself finished once it no longer
+// reads the counters or flags (right after its hand-off, while its stores
+// proceed), in one of several group counters; the last one advances the
+// launch counter and clears the counters and the flags, and stream order
+// shows the next launch the new values.  Choices that are not live mark a
+// spare word of their own lane, in the counting histogram as in the rank
+// masks, so idle lanes past a tile's tokens never contend for one LDS
+// address.
 
 constexpr int kTagShift = 9;
 constexpr uint32_t kTagMask = 0x7FFFFFu;
@@ -1215,14 +1217,18 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
     extern __shared__ __align__(16) unsigned char lds[];
     const int E = h.E, K = h.K, nblk = h.nblk;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+    constexpr int W = VMAX >= 4 ? 1 : 4 / VMAX;
+    constexpr int TB = 4 * W;
+    // LDS: the scatter's arrays first, then the counting or finishing duty's
+    const int duty_lds = 4 * (E + kWave) * 8 + 4 * E * 4 + TB * K * 4 + 2 * E * 4;
 
     if (blockIdx.x < kLayoutMaxTiles) {
-        // ---- counting workgroup of tile b: route check, count, publish
+        // ---- counting duty of tile b: route check, count, publish
         const uint32_t tag =
             launch_tag(__hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         // a count per expert, then one spare per lane for choices that are
         // not live (so they never contend for one address)
-        int *hist = reinterpret_cast<int *>(lds);          // [E + 64]
+        int *hist = reinterpret_cast<int *>(lds + duty_lds);   // [E + 64]
         const int b = blockIdx.x;
         for (int i = tid; i < E + kWave; i += kD1Threads) hist[i] = 0;
         const int n_tile = b < nblk ? int(tr.w & 0xFFFFu) : 0;
@@ -1246,11 +1252,9 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
         for (int e = tid; e < E; e += kD1Threads)
             __hip_atomic_store(&h.tcount[b * tcount_pitch(E) + e], (tag << kTagShift) | uint32_t(hist[e]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // counted finished right away: its stores land before the launch
-        // ends, and the finisher reads every word until it carries this
-        // launch's tag
-        if (wave == 0 && lane == 0) onepass_done(h);
-        return;
+        // then on to this workgroup's own slots: the count stores land
+        // before the launch ends, and the finisher reads every word until
+        // it carries this launch's tag
     }
 
     if (blockIdx.x == kLayoutMaxTiles) {
@@ -1264,7 +1268,7 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
         const uint32_t tag =
             launch_tag(__hip_atomic_load(&h.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         __shared__ int s_bad;
-        int *A = reinterpret_cast<int *>(lds);    // [E] aligned counts, then their exclusive prefix
+        int *A = reinterpret_cast<int *>(lds + duty_lds);   // [E] aligned counts, then their exclusive prefix
         if (tid == 0) s_bad = 0;
         lds_barrier();
         const int pitch = tcount_pitch(E);
@@ -1316,19 +1320,22 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
             for (int c = lane; c < kReadyCopies; c += kWave)
                 __hip_atomic_store(&h.ready[c * kReadyStride], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        // counted finished once its flag stores are acknowledged: the last
-        // finished workgroup clears the flags for the next launch, and a flag
-        // store still in flight must not land after that
+        // the flag stores acknowledged before this workgroup can be counted
+        // finished (the last finished workgroup clears the flags for the
+        // next launch, and a flag store in flight must not land after that),
+        // then on to its own slots
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        lds_barrier();
+    }
+
+    // ---- scatter: wavefronts 0-3 hold W tokens each, TB in all; wavefront
+    // 4 makes the hand-off.  A workgroup past the last slot (the grid has at
+    // least kLayoutMaxTiles + 1 workgroups) only counts itself finished.
+    constexpr int HW = kD1Waves - 1;             // the hand-off wavefront
+    if (int(blockIdx.x) * TB >= h.nblk * h.tile) {
         if (wave == 0 && lane == 0) onepass_done(h);
         return;
     }
-
-    // ---- scatter workgroup: wavefronts 0-3 hold W tokens each, TB in all;
-    // wavefront 4 makes the hand-off
-    constexpr int W = VMAX >= 4 ? 1 : 4 / VMAX;
-    constexpr int TB = 4 * W;
-    constexpr int HW = kD1Waves - 1;             // the hand-off wavefront
     __shared__ uint64_t s_prow[kMaxParts], s_pw[kMaxParts], s_ps[kMaxParts];
     __shared__ int s_gaveup;
     const int MS = E + kWave;                    // lane masks per expert, then a spare per lane
@@ -1338,7 +1345,7 @@ __global__ __launch_bounds__(kD1Threads) void k_dispatch1(DispatchArgs a)
     int *base = pkl + TB * K;                                                 // [E] this tile's first row per expert
     int *Cs = base + E;                                                       // [E] ends (first workgroup)
     const int nvec = h.nvec;
-    const int jb = blockIdx.x - kLayoutMaxTiles - 1;
+    const int jb = blockIdx.x;
     const int v_first = jb * TB;                 // first slot of the tiled token space
     const int tile = v_first / h.tile;
     const SourceRec src = load_source(a, source_of_tiled(a, h.N, v_first));
@@ -2338,16 +2345,18 @@ int launch_fused_v(const DispatchArgs &a, bool k32, dim3 grid, size_t lds, hipSt
     return launched_ok();
 }
 
-// One-launch dispatch: kLayoutMaxTiles counting workgroups, the finisher,
-// then one scatter workgroup per TB slots of the tiled token space.
+// One-launch dispatch: one workgroup per TB slots of the tiled token space
+// (at least kLayoutMaxTiles + 1 workgroups: the first kLayoutMaxTiles also
+// count a tile each, the next one also finishes the counts).
 template <int VMAX>
 int launch_onepass_v(const DispatchArgs &a, bool k32, int nslots, int E, int K, hipStream_t st)
 {
     constexpr int TB = 4 * (VMAX >= 4 ? 1 : 4 / VMAX);
     const size_t scatter_lds = size_t(4) * (E + kWave) * 8 + size_t(4) * E * 4 + size_t(TB) * K * 4 + size_t(2) * E * 4;
-    const size_t count_lds = size_t(2 * E + kWave) * 4;   // counts and lane spares, then the aligned scan
-    const size_t lds = scatter_lds > count_lds ? scatter_lds : count_lds;
-    const dim3 grid(kLayoutMaxTiles + 1 + nslots / TB);
+    const size_t duty_lds = size_t(E + kWave) * 4;   // counts and lane spares, or the finisher's aligned scan
+    const size_t lds = scatter_lds + duty_lds;
+    const int nscatter = nslots / TB;
+    const dim3 grid(nscatter > kLayoutMaxTiles + 1 ? nscatter : kLayoutMaxTiles + 1);
     if (k32) hipLaunchKernelGGL((k_dispatch1<32, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     else hipLaunchKernelGGL((k_dispatch1<8, VMAX>), grid, dim3(kD1Threads), lds, st, a);
     return launched_ok();
