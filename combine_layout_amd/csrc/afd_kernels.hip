@@ -1759,19 +1759,25 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 // trip before the row loads is the slots' (the two-way select is the
 // cheaper one, which shows at decode).  With more partitions (NB = 0) the
 // bases are looked up in the kernel arguments by partition number, all
-// eight requested before one wait.  The token offsets are read only for the
-// output address.  The wavefront then issues every live row's loads before
-// it accumulates, in ascending k, with a float32 multiply and a separate
-// add.
+// eight requested before one wait.  The wavefront then issues every live
+// row's loads before it accumulates, in ascending k, with a float32 multiply
+// and a separate add.  The output rows of the first two sources and the
+// first source's token count are preloaded arguments too (out1 is null when
+// there are more than two sources): a token of source 0 or 1 finds its
+// output row with no memory request, so the wavefront's last step is the
+// store rather than a chain of argument loads (the number of sources, the
+// offsets, the source's output base), which would add their latency once
+// per kernel.  Tokens past the first source of a round with more sources
+// still search the offsets in the argument block.
 template <int VPL, int NB>
-__global__ __launch_bounds__(256) void k_combine(const int32_t *slot, int ntok, int K, int H, int nseg, uint64_t rb0,
-                                                 uint64_t rb1, CombineArgs a)
+__global__ __launch_bounds__(256) void k_combine(const int32_t *slot, uint64_t rb0, uint64_t rb1, uint64_t out0,
+                                                 uint64_t out1, int ntok, int K, int H, int t1, CombineArgs a)
 {
 #pragma clang fp contract(off)
     static_assert(offsetof(CombineArgs, reply4) == 32 && offsetof(CombineArgs, tok_off) == 64,
                   "scalars and four bases in the first 64 bytes, offsets at byte 64");
     const u32x16 hv = *reinterpret_cast<const u32x16 *>(&a);
-    const int N = int(hv[2]), nvec = H >> 3;
+    const int nvec = H >> 3, nseg = (nvec + kWave * VPL - 1) / (kWave * VPL);
     auto base4 = [&](uint32_t q) { return (uint64_t(hv[9 + 2 * q]) << 32) | uint64_t(hv[8 + 2 * q]); };
     const uint64_t rb2 = base4(2), rb3 = base4(3);
     const int lane = threadIdx.x & (kWave - 1);
@@ -1845,10 +1851,20 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t *slot, int ntok, 
             }
         }
     }
-    // the token's source and place in it, needed only for the output address
-    int t0;
-    const int s = source_of(load_offsets(a.tok_off), N, g, t0);
-    const gptr<u32x4> o = (gptr<u32x4>)(a.out[s] + int64_t(g - t0) * H);
+    // the token's output row: sources 0 and 1 from the preloaded bases, any
+    // later one through the offsets (wave-uniform branch)
+    uint64_t ob = out0;
+    int t0 = 0;
+    if (g >= t1) {
+        if (out1 != 0) {
+            ob = out1;
+            t0 = t1;
+        } else {
+            const int s = source_of(load_offsets(a.tok_off), a.N, g, t0);
+            ob = reinterpret_cast<uint64_t>(a.out[s]);
+        }
+    }
+    const gptr<u32x4> o = (gptr<u32x4>)(ob + uint64_t(g - t0) * rowb);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int c = c0 + i * kWave;
@@ -2531,7 +2547,13 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     const int64_t waves = int64_t(p.ntok) * a.nseg;
     dim3 grid(unsigned((waves + 3) / 4));
     const uint64_t rb0 = reinterpret_cast<uint64_t>(a.reply4[0]), rb1 = reinterpret_cast<uint64_t>(a.reply4[1]);
-#define AFD_COMBINE(NB) hipLaunchKernelGGL((k_combine<1, NB>), grid, dim3(256), 0, st, a.slot, a.ntok, a.K, a.H, a.nseg, rb0, rb1, a)
+    // output rows of sources 0 and 1; with more sources out1 is null and
+    // tokens from t1 on look their source up in the offsets
+    const uint64_t out0 = reinterpret_cast<uint64_t>(a.out[0]);
+    const uint64_t out1 = p.N == 2 ? reinterpret_cast<uint64_t>(a.out[1]) : 0;
+    const int t1 = p.N > 1 ? p.tok_off[1] : p.ntok;
+#define AFD_COMBINE(NB) \
+    hipLaunchKernelGGL((k_combine<1, NB>), grid, dim3(256), 0, st, a.slot, rb0, rb1, out0, out1, a.ntok, a.K, a.H, t1, a)
     if (p.F <= 2) AFD_COMBINE(2);
     else if (p.F <= 4) AFD_COMBINE(4);
     else AFD_COMBINE(0);
