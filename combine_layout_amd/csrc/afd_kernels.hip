@@ -1768,8 +1768,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 // store rather than a chain of argument loads (the number of sources, the
 // offsets, the source's output base), which would add their latency once
 // per kernel.  Tokens past the first source of a round with more sources
-// still search the offsets in the argument block.
-template <int VPL, int NB>
+// still search the offsets in the argument block.  NT: streaming stores for
+// the output, chosen for small rounds (see be_launch_combine).
+template <int VPL, int NB, bool NT>
 __global__ __launch_bounds__(256) void k_combine(const int32_t *slot, uint64_t rb0, uint64_t rb1, uint64_t out0,
                                                  uint64_t out1, int ntok, int K, int H, int t1, CombineArgs a)
 {
@@ -1874,7 +1875,10 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t *slot, uint64_t r
             r.y = bf16_rne_bits(acc[i][2]) | (bf16_rne_bits(acc[i][3]) << 16);
             r.z = bf16_rne_bits(acc[i][4]) | (bf16_rne_bits(acc[i][5]) << 16);
             r.w = bf16_rne_bits(acc[i][6]) | (bf16_rne_bits(acc[i][7]) << 16);
-            o[c] = r;
+            if constexpr (NT)
+                __builtin_nontemporal_store(r, &o[c]);
+            else
+                o[c] = r;
         }
     }
 }
@@ -2552,11 +2556,24 @@ int be_launch_combine(const RoundPlan &p, void *stream)
     const uint64_t out0 = reinterpret_cast<uint64_t>(a.out[0]);
     const uint64_t out1 = p.N == 2 ? reinterpret_cast<uint64_t>(a.out[1]) : 0;
     const int t1 = p.N > 1 ? p.tok_off[1] : p.ntok;
-#define AFD_COMBINE(NB) \
-    hipLaunchKernelGGL((k_combine<1, NB>), grid, dim3(256), 0, st, a.slot, rb0, rb1, out0, out1, a.ntok, a.K, a.H, t1, a)
-    if (p.F <= 2) AFD_COMBINE(2);
-    else if (p.F <= 4) AFD_COMBINE(4);
-    else AFD_COMBINE(0);
+    // Streaming output stores when the output is small (decode-sized):
+    // 0.13 us faster per 1 MiB decode round, presumably as fewer dirty lines
+    // are left in L2 for the kernel's end to write back.  With 8 and 24 MiB
+    // outputs they measured slower (by up to 1 us a round), with 16 MiB
+    // within noise, so larger outputs keep the default policy.
+    const bool nt = int64_t(p.ntok) * p.H * 2 <= kCombineStreamOutBytes;
+#define AFD_COMBINE(NB, NT) \
+    hipLaunchKernelGGL((k_combine<1, NB, NT>), grid, dim3(256), 0, st, a.slot, rb0, rb1, out0, out1, a.ntok, a.K, a.H, t1, a)
+    if (p.F <= 2) {
+        if (nt) AFD_COMBINE(2, true);
+        else AFD_COMBINE(2, false);
+    } else if (p.F <= 4) {
+        if (nt) AFD_COMBINE(4, true);
+        else AFD_COMBINE(4, false);
+    } else {
+        if (nt) AFD_COMBINE(0, true);
+        else AFD_COMBINE(0, false);
+    }
 #undef AFD_COMBINE
     return launched_ok();
 }

@@ -57,6 +57,10 @@ constexpr int kDoneGroups = 16;
 // Experts of a round the one-launch dispatch takes (its hand-off reads four
 // experts' words per lane of one wavefront).
 constexpr int kMaxExpertsOneLaunch = 256;
+
+// Largest combine output (bytes) written with streaming stores.
+constexpr int64_t kCombineStreamOutBytes = int64_t(4) << 20;
+
 // Words between consecutive tiles' runs of the one-launch dispatch's tile
 // counts (tile-major, each run on whole 128-byte lines).
 #ifdef __HIPCC__
