@@ -172,3 +172,25 @@ def test_parity_fused_wide_topk(K):
     g = h.run_round(inst)
     ref = _oracle_ref(inst, g.receive_rows)
     assert check_round(inst, g, ref) == 0
+
+
+# (seed, tokens per source, H): the combine finds a token's output row from
+# preloaded bases for sources 0 and 1 and from the offsets for later ones,
+# and streams its stores when the output is at most 4 MiB.  Empty first or
+# second sources, every token in a later source, and outputs at and just
+# past the 4 MiB line.
+SOURCES = [(0, [0, 300], 512), (1, [300, 0], 512), (2, [0, 1100], 2048), (3, [0, 0, 200], 512),
+           (4, [100, 0, 0], 512), (5, [0, 0, 700, 5], 256), (6, [1024, 1024], 1024), (7, [1025, 1024], 1024),
+           (8, [70, 0, 90], 768)]
+
+
+@pytest.mark.parametrize("case", SOURCES, ids=lambda c: f"s{c[0]}")
+def test_parity_combine_output_rows_of_every_source(case):
+    h = _gpu()
+    i, T, H = case
+    inst = gen.random_small(900 + i, N=len(T), F=2, E=32, K=8, alpha=8, T=T, H=H, p_skip=0.1,
+                            bucket=max(T))
+    print(f"[parity sources] s{i} T={T} H={H} out={sum(T) * H * 2} B", flush=True)
+    g = h.run_round(inst)
+    ref = _oracle_ref(inst, g.receive_rows)
+    assert check_round(inst, g, ref) == 0
