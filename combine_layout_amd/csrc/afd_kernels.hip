@@ -1762,8 +1762,9 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 // eight requested before one wait.  The wavefront then issues every live
 // row's loads before it accumulates, in ascending k, with a float32 multiply
 // and a separate add.  The output rows of the first two sources and the
-// first source's token count are preloaded arguments too (out1 is null when
-// there are more than two sources): a token of source 0 or 1 finds its
+// first source's token count are preloaded arguments too (out1 is null
+// unless there are exactly two sources; with one, t1 = ntok and no token
+// reaches it): a token of source 0 or 1 finds its
 // output row with no memory request, so the wavefront's last step is the
 // store rather than a chain of argument loads (the number of sources, the
 // offsets, the source's output base), which would add their latency once
